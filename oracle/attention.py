@@ -1,0 +1,147 @@
+"""Oracle of the attention step on quantized operands.
+
+TEST INFRASTRUCTURE.  Part of the CPU oracle; see ``oracle/__init__.py``.
+
+Method, from the pages: QK^T is taken on the low-bit Q and K codes (integer
+matrix units), then softmax, then P.V in 16-bit or FP8 (jefxiong.cn "AIGC
+weekend special 5.10", section 1.2 item (1); GVCLab research log 2026-09-02,
+section 5.5 table, SageAttention2 row).  The tiling with a running max and a
+running sum is the FlashAttention lineage the same digest names as the
+baseline (section 1.1 and the paper timeline).
+
+Readings where the pages are silent:
+  * logits s_rj = D_rj * sQ[r // bq] * sK[j // bk] * scale with D the exact
+    integer dot product of the codes; the softmax scale is applied here, not
+    folded into Q before quantization; attention is non-causal over all N keys.
+  * 16-bit P.V: exact two-pass softmax in float64 with V the exact bf16 values
+    (the kernel's bf16 rounding of P is not mirrored; it sits far inside the
+    output tolerance).
+  * FP8 P.V: the kernel's online schedule is mirrored.  Keys are taken in tiles
+    of ``kv_tile`` in ascending order with running max m_t; P~_j =
+    exp(s_j - m_t(j)) in (0, 1]; the FP8 operand is E4M3(448 * P~_j); the row
+    sum accumulates the unrounded P~; V enters as s_v * decode(code_v).
+    Elements whose 448*P~ lies within ``eps_rel`` of an E4M3 rounding midpoint
+    may legitimately round either way in the kernel's binary32 arithmetic; the
+    possible effect of each is summed into a per-element envelope E.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fp
+
+__all__ = ["int_scores", "logits", "softmax_pv", "attention_fp64", "attend_bf16",
+           "attend_fp8", "e4m3_round_f64"]
+
+
+def int_scores(q_codes: np.ndarray, k_codes: np.ndarray) -> np.ndarray:
+    """D = q_codes @ k_codes^T as exact integers held in float64.
+
+    |D| <= d * 127^2 < 2^53, and every partial sum is an integer of smaller
+    magnitude, so float64 BLAS returns the exact value in any summation order."""
+    return np.asarray(q_codes, np.float64) @ np.asarray(k_codes, np.float64).T
+
+
+def logits(D: np.ndarray, sq_rows: np.ndarray, sk_keys: np.ndarray, scale: float) -> np.ndarray:
+    """s = D * sQ(row) * sK(key) * scale, float64."""
+    return (D * np.asarray(sq_rows, np.float64)[:, None]
+            * np.asarray(sk_keys, np.float64)[None, :] * float(scale))
+
+
+def softmax_pv(S: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Two-pass softmax and product: O = sum_j e^(s_j - m) v_j / sum_j e^(s_j - m)."""
+    m = S.max(axis=1, keepdims=True)
+    P = np.exp(S - m)
+    return (P @ np.asarray(V, np.float64)) / P.sum(axis=1, keepdims=True)
+
+
+def attention_fp64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Unquantized attention softmax(Q K^T * scale) V in float64 (the textbook
+    operation the quantized path approximates)."""
+    S = (np.asarray(Q, np.float64) @ np.asarray(K, np.float64).T) * float(scale)
+    return softmax_pv(S, V)
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_block, scale,
+                chunk: int = 256) -> np.ndarray:
+    """Output rows O[rows] (float64 [R, d]) of the 16-bit P.V path for one head."""
+    rows = np.asarray(rows, np.int64)
+    N = k_codes.shape[0]
+    sk = np.repeat(np.asarray(k_scale, np.float64), k_block)[:N]
+    V = _bf16_to_f64(v_bits)
+    out = np.empty((rows.size, V.shape[1]), np.float64)
+    for i in range(0, rows.size, chunk):
+        r = rows[i:i + chunk]
+        D = int_scores(q_codes[r], k_codes)
+        S = logits(D, np.asarray(q_scale, np.float64)[r // q_block], sk, scale)
+        out[i:i + chunk] = softmax_pv(S, V)
+    return out
+
+
+def e4m3_round_f64(y: np.ndarray):
+    """Nearest-even E4M3FN rounding of non-negative float64 values.
+
+    Returns (rounded value, quantum, position of y in units of the quantum);
+    saturates at 448."""
+    y = np.asarray(y, np.float64)
+    _, ex = np.frexp(y)                     # y = f * 2^ex, f in [0.5, 1)
+    k = ex - 1                              # binade: 2^k <= y < 2^(k+1)
+    qe = np.maximum(k - 3, -9)
+    quantum = np.ldexp(1.0, qe)
+    c = y / quantum                         # exact: division by a power of two
+    r = np.rint(c) * quantum                # rint: round half to even
+    r = np.where(y == 0, 0.0, r)
+    return np.minimum(r, fp.E4M3_MAX), quantum, c
+
+
+def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_block, k_block,
+               scale, v_block: int = 64, kv_tile: int = 64, eps_rel: float = 2.0 ** -16,
+               round_p=None, chunk: int = 128):
+    """FP8 P.V path for one head; returns (O [R, d], E [R, d], hits).
+
+    ``round_p`` maps 448*P~ to the FP8 operand value (default: E4M3 rounding;
+    the identity turns the mirror into the exact softmax, a self-check)."""
+    rows = np.asarray(rows, np.int64)
+    N = k_codes.shape[0]
+    sk = np.repeat(np.asarray(k_scale, np.float64), k_block)[:N]
+    sv = np.repeat(np.asarray(v_scale, np.float64), v_block)[:N]
+    Vh = fp.e4m3_decode(v_codes) * sv[:, None]           # dequantized V
+    absV = np.abs(Vh)
+    nt = -(-N // kv_tile)
+    pad = nt * kv_tile - N
+    O = np.empty((rows.size, Vh.shape[1]), np.float64)
+    E = np.zeros_like(O)
+    hits = 0
+    for i in range(0, rows.size, chunk):
+        r = rows[i:i + chunk]
+        S = logits(int_scores(q_codes[r], k_codes), np.asarray(q_scale, np.float64)[r // q_block],
+                   sk, scale)
+        Sp = np.pad(S, ((0, 0), (0, pad)), constant_values=-np.inf)
+        tile_max = Sp.reshape(r.size, nt, kv_tile).max(axis=2)
+        m_run = np.maximum.accumulate(tile_max, axis=1)          # m_t
+        m_key = np.repeat(m_run, kv_tile, axis=1)[:, :N]         # m_t(j)
+        m_T = m_run[:, -1:]
+        Pt = np.exp(S - m_key)                                   # P~ in (0, 1]
+        y = 448.0 * Pt
+        if round_p is None:
+            yr, quantum, c = e4m3_round_f64(y)
+        else:
+            yr = round_p(y)
+        w = np.exp(m_key - m_T)                                  # e^(m_t(j) - m_T)
+        l = (w * Pt).sum(axis=1, keepdims=True)
+        num = (w * yr / 448.0) @ Vh
+        O[i:i + chunk] = num / l
+        if round_p is None:
+            frac = c - np.floor(c)
+            amb = (np.abs(frac - 0.5) * quantum <= eps_rel * y) & (y > 0)
+            if amb.any():
+                lo = np.floor(c) * quantum
+                hi = np.minimum((np.floor(c) + 1.0) * quantum, fp.E4M3_MAX)
+                dP = np.where(amb, (hi - lo) / 448.0 * w, 0.0)
+                E[i:i + chunk] = (dP @ absV) / l
+                hits += int(amb.sum())
+    return O, E, hits
