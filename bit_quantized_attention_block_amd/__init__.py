@@ -1,0 +1,241 @@
+"""Python binding of libsqattn (low-bit quantized attention on MI355X / gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels behind
+the C-ABI declared in ``include/sqattn.h``.  PyTorch provides device memory and
+the current stream.  If ``libsqattn.so`` is missing the binding raises; there
+is no other implementation to fall back on.
+
+    import bit_quantized_attention_block_amd as sq
+    out = sq.forward(q, k, v)                  # bf16 [B,H,N,d] cuda tensors -> fp32
+    qi, qs, ki, ks, mu = sq.quantize_qk(q, k)  # INT8 codes, scales, K mean
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "forward",
+           "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
+           "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS"]
+
+PV_BF16 = 0
+PV_FP8 = 1
+_PV = {"bf16": PV_BF16, "fp8": PV_FP8, PV_BF16: PV_BF16, PV_FP8: PV_FP8}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libsqattn.so")
+
+_c = ctypes
+_vp, _i, _f, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
+
+# name -> (restype, argtypes); mirrors include/sqattn.h
+EXPORTS = {
+    "sqattn_version": (_i, []),
+    "sqattn_status_string": (_c.c_char_p, [_i]),
+    "sqattn_last_error": (_c.c_char_p, []),
+    "sqattn_quantize_qk_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "sqattn_quantize_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sqattn_quantize_v_fp8": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "sqattn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _vp]),
+    "sqattn_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]),
+    "sqattn_forward_ex": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp, _vp]),
+    "sqattn_packed_v_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "sqattn_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "sqattn_attend_quantized": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                     _vp]),
+}
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("reserved", _i)]
+
+
+class SqattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sqattn status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsqattn (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               "`python -m bit_quantized_attention_block_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().sqattn_version()
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise SqattnError(status, f"{L.sqattn_status_string(status).decode()}: "
+                                  f"{L.sqattn_last_error().decode()}")
+
+
+# --------------------------------------------------------------------------- torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _ws(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        return workspace, workspace.numel()
+    if nbytes == 0:
+        return None, 0
+    w = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return w, nbytes
+
+
+# --------------------------------------------------------------------------- API
+
+def quantize_qk_workspace_bytes(B, H, N, d) -> int:
+    return int(lib().sqattn_quantize_qk_workspace_bytes(B, H, N, d))
+
+
+def quantize_qk(q, k, q_block: int = 128, k_block: int = 64, workspace=None):
+    """Q, K bf16 [B,H,N,d] -> (q_i8, q_scale, k_i8, k_scale, k_mean)."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if tuple(k.shape) != (B, H, N, d):
+        raise ValueError("q and k shapes differ")
+    dev = q.device
+    qi = torch.empty((B, H, N, d), dtype=torch.int8, device=dev)
+    ki = torch.empty_like(qi)
+    qs = torch.empty((B, H, -(-N // q_block)), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, H, -(-N // k_block)), dtype=torch.float32, device=dev)
+    mu = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    w, wb = _ws(quantize_qk_workspace_bytes(B, H, N, d), dev, workspace)
+    _check(lib().sqattn_quantize_qk(_ptr(q), _ptr(k), B, H, N, d, q_block, k_block, _ptr(qi), _ptr(qs),
+                                    _ptr(ki), _ptr(ks), _ptr(mu), _ptr(w), wb, _stream(q)))
+    return qi, qs, ki, ks, mu
+
+
+def quantize_v_fp8(v, v_block: int = 64):
+    """V bf16 [B,H,N,d] -> (E4M3 codes uint8 [B,H,N,d], scales [B,H,ceil(N/64)])."""
+    torch = _torch()
+    _dev(v, "v", torch.bfloat16)
+    B, H, N, d = _shape(v)
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=v.device)
+    sc = torch.empty((B, H, -(-N // v_block)), dtype=torch.float32, device=v.device)
+    _check(lib().sqattn_quantize_v_fp8(_ptr(v), B, H, N, d, v_block, _ptr(codes), _ptr(sc), _stream(v)))
+    return codes, sc
+
+
+def _opts(q_block):
+    return Opts(q_block=int(q_block), k_block=64, v_block=64, reserved=0)
+
+
+def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
+    o = _opts(q_block)
+    return int(lib().sqattn_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
+
+
+def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
+            workspace=None):
+    """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> fp32 out [B,H,N,d]."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v shapes differ")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
+    o = _opts(q_block)
+    _check(lib().sqattn_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
+                                   _ptr(w), wb, _stream(q), ctypes.byref(o)))
+    return out
+
+
+def packed_v_bytes(B, H, N, d, pv="bf16") -> int:
+    return int(lib().sqattn_packed_v_bytes(B, H, N, d, _PV[pv]))
+
+
+def pack_v(v, pv="bf16"):
+    """bf16 V (pv="bf16") or E4M3 V codes (pv="fp8") [B,H,N,d] -> the attention
+    kernel's tile layout (a flat uint8 tensor)."""
+    torch = _torch()
+    _dev(v, "v", torch.bfloat16 if _PV[pv] == PV_BF16 else torch.uint8)
+    B, H, N, d = _shape(v)
+    packed = torch.empty(packed_v_bytes(B, H, N, d, pv), dtype=torch.uint8, device=v.device)
+    _check(lib().sqattn_pack_v(_ptr(v), B, H, N, d, _PV[pv], _ptr(packed), _stream(v)))
+    return packed
+
+
+def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
+                     pv="bf16", q_block: int = 128, out=None):
+    """The attention kernel alone, on quantized Q/K and packed V (see pack_v)."""
+    torch = _torch()
+    _dev(q_i8, "q_i8", torch.int8)
+    _dev(k_i8, "k_i8", torch.int8)
+    _dev(q_scale, "q_scale", torch.float32)
+    _dev(k_scale, "k_scale", torch.float32)
+    _dev(v_packed, "v_packed", torch.uint8)
+    B, H, N, d = _shape(q_i8)
+    if v_packed.numel() < packed_v_bytes(B, H, N, d, pv):
+        raise ValueError("v_packed is too small")
+    if _PV[pv] == PV_FP8:
+        _dev(v_scale, "v_scale", torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q_i8.device)
+    _dev(out, "out", torch.float32)
+    o = _opts(q_block)
+    _check(lib().sqattn_attend_quantized(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_packed),
+                                         _ptr(v_scale), B, H, N, d, float(scale), _PV[pv], ctypes.byref(o),
+                                         _ptr(out), _stream(q_i8)))
+    return out

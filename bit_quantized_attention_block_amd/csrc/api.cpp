@@ -1,0 +1,356 @@
+// C-ABI of the sqattn library: argument validation, workspace layout and the
+// launch sequence of each entry point.  See include/sqattn.h for the contract.
+#include "../../include/sqattn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Sizes {
+  long long BH, N, d, nq, nk, nt, S;
+};
+
+// Common shape checks.  Returns SQATTN_OK or an error (message set).
+int check_shape(int B, int H, int N, int d, Sizes* sz) {
+  if (B < 1 || H < 1 || N < 1) return fail(SQATTN_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d != 64 && d != 128) return fail(SQATTN_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if (N >= (1 << 24)) return fail(SQATTN_ERR_RANGE, "N must be below 2^24");
+  long long BH = (long long)B * H;
+  if (BH > 65535) return fail(SQATTN_ERR_RANGE, "B*H must be at most 65535");
+  if (BH * (long long)N * d >= (1LL << 40)) return fail(SQATTN_ERR_RANGE, "B*H*N*d must be below 2^40");
+  sz->BH = BH;
+  sz->N = N;
+  sz->d = d;
+  sz->nt = (N + sqattn::KT - 1) / sqattn::KT;
+  sz->S = sqattn::kmean_chunks((int)BH, N);
+  return SQATTN_OK;
+}
+
+int check_block(int b, const char* name) {
+  if (b < 16 || (b % 16) != 0 || b > (1 << 24))
+    return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " must be a positive multiple of 16");
+  return SQATTN_OK;
+}
+
+int check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return SQATTN_OK;
+}
+
+struct Opts {
+  int q_block, k_block, v_block;
+};
+
+int resolve_opts(const sqattn_opts* o, Opts* r) {
+  r->q_block = 128;
+  r->k_block = 64;
+  r->v_block = 64;
+  if (!o) return SQATTN_OK;
+  if (o->reserved != 0) return fail(SQATTN_ERR_INVALID_ARG, "opts.reserved must be 0");
+  if (o->q_block) r->q_block = o->q_block;
+  if (o->k_block) r->k_block = o->k_block;
+  if (o->v_block) r->v_block = o->v_block;
+  int s;
+  if ((s = check_block(r->q_block, "q_block"))) return s;
+  if (r->k_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "k_block must be 64 (the attention tile)");
+  if (r->v_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "v_block must be 64");
+  return SQATTN_OK;
+}
+
+// Workspace carving.  Each region is 256-byte aligned.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+struct FwdLayout {
+  size_t q_i8, k_i8, q_scale, k_scale, k_mean, partial, vt, v_scale, total;
+};
+
+FwdLayout forward_layout(const Sizes& z, int pv, int q_block) {
+  FwdLayout L;
+  Carve c;
+  const long long nq = (z.N + q_block - 1) / q_block;
+  L.q_i8 = c.take((size_t)(z.BH * z.N * z.d));
+  L.k_i8 = c.take((size_t)(z.BH * z.N * z.d));
+  L.q_scale = c.take((size_t)(z.BH * nq) * 4);
+  L.k_scale = c.take((size_t)(z.BH * z.nt) * 4);
+  L.k_mean = c.take((size_t)(z.BH * z.d) * 4);
+  L.partial = c.take((size_t)(z.BH * z.S * z.d) * 32);
+  L.vt = c.take((size_t)(z.BH * z.nt * z.d * sqattn::KT) * (pv == SQATTN_PV_BF16 ? 2 : 1));
+  L.v_scale = c.take(pv == SQATTN_PV_BF16 ? 0 : (size_t)(z.BH * z.nt) * 4);
+  L.total = c.off;
+  return L;
+}
+
+int hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SQATTN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return SQATTN_OK;
+}
+
+// Provides workspace: the caller's, or a stream-ordered allocation freed by
+// the destructor (also stream-ordered).
+struct Workspace {
+  void* ptr = nullptr;
+  bool owned = false;
+  hipStream_t st = nullptr;
+  int acquire(void* user, size_t user_bytes, size_t need, hipStream_t stream) {
+    st = stream;
+    if (user) {
+      if (user_bytes < need)
+        return fail(SQATTN_ERR_WORKSPACE, "workspace has " + std::to_string(user_bytes) + " bytes, " +
+                                              std::to_string(need) + " needed");
+      if (!aligned(user, kAlign)) return fail(SQATTN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+      ptr = user;
+      return SQATTN_OK;
+    }
+    if (need == 0) return SQATTN_OK;
+    hipError_t e = hipMallocAsync(&ptr, need, stream);
+    if (e != hipSuccess) return fail(SQATTN_ERR_HIP, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    owned = true;
+    return SQATTN_OK;
+  }
+  ~Workspace() {
+    if (owned && ptr) (void)hipFreeAsync(ptr, st);
+  }
+  template <class T>
+  T* at(size_t off) const {
+    return (T*)((char*)ptr + off);
+  }
+};
+
+const float kLog2e = 1.4426950408889634f;
+
+int validate_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                     int pv, const float* out, const sqattn_opts* opts, Sizes* z, Opts* o) {
+  int s;
+  if ((s = check_ptr(q, "q", 16)) || (s = check_ptr(k, "k", 16)) || (s = check_ptr(v, "v", 16)) ||
+      (s = check_ptr(out, "out", 16)))
+    return s;
+  if ((s = check_shape(B, H, N, d, z))) return s;
+  if (pv != SQATTN_PV_BF16 && pv != SQATTN_PV_FP8_E4M3) return fail(SQATTN_ERR_INVALID_ARG, "unknown pv_dtype");
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(SQATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((s = resolve_opts(opts, o))) return s;
+  z->nq = (N + o->q_block - 1) / o->q_block;
+  z->nk = z->nt;
+  return SQATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sqattn_version(void) { return SQATTN_VERSION; }
+
+const char* sqattn_status_string(int s) {
+  switch (s) {
+    case SQATTN_OK: return "ok";
+    case SQATTN_ERR_INVALID_ARG: return "invalid argument";
+    case SQATTN_ERR_UNSUPPORTED: return "unsupported";
+    case SQATTN_ERR_WORKSPACE: return "workspace too small";
+    case SQATTN_ERR_HIP: return "HIP runtime error";
+    case SQATTN_ERR_RANGE: return "size out of range";
+    default: return "unknown status";
+  }
+}
+
+const char* sqattn_last_error(void) { return g_err.c_str(); }
+
+size_t sqattn_quantize_qk_workspace_bytes(int B, int H, int N, int d) {
+  Sizes z;
+  std::string keep = g_err;
+  if (check_shape(B, H, N, d, &z)) {
+    g_err = keep;
+    return 0;
+  }
+  return align_up((size_t)(z.BH * z.S * z.d) * 32);
+}
+
+int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int q_block, int k_block,
+                       int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  if ((s = check_ptr(q, "q", 16)) || (s = check_ptr(k, "k", 16)) || (s = check_ptr(q_i8, "q_i8", 16)) ||
+      (s = check_ptr(k_i8, "k_i8", 16)) || (s = check_ptr(q_scale, "q_scale", 4)) ||
+      (s = check_ptr(k_scale, "k_scale", 4)) || (s = check_ptr(k_mean, "k_mean", 4)))
+    return s;
+  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if ((s = check_block(q_block, "q_block")) || (s = check_block(k_block, "k_block"))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  const size_t need = align_up((size_t)(z.BH * z.S * z.d) * 32);
+  if ((s = ws.acquire(workspace, workspace_bytes, need, st))) return s;
+  sqattn::launch_quant_i8((const uint16_t*)q, (int)z.BH, N, d, q_block, nullptr, q_i8, q_scale, st);
+  sqattn::launch_kmean((const uint16_t*)k, (int)z.BH, N, d, ws.at<uint64_t>(0), k_mean, st);
+  sqattn::launch_quant_i8((const uint16_t*)k, (int)z.BH, N, d, k_block, k_mean, k_i8, k_scale, st);
+  return hip_check("sqattn_quantize_qk launch");
+}
+
+int sqattn_quantize_v_fp8(const void* v, int B, int H, int N, int d, int v_block, uint8_t* v_fp8,
+                          float* v_scale, void* stream) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  if ((s = check_ptr(v, "v", 16)) || (s = check_ptr(v_fp8, "v_fp8", 16)) || (s = check_ptr(v_scale, "v_scale", 4)))
+    return s;
+  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if (v_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "v_block must be 64");
+  hipStream_t st = (hipStream_t)stream;
+  sqattn::launch_quant_v_fp8((const uint16_t*)v, (int)z.BH, N, d, v_fp8, nullptr, v_scale, st);
+  return hip_check("sqattn_quantize_v_fp8 launch");
+}
+
+size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sqattn_opts* opts) {
+  std::string keep = g_err;
+  Sizes z;
+  Opts o;
+  if (check_shape(B, H, N, d, &z) || (pv_dtype != 0 && pv_dtype != 1) || resolve_opts(opts, &o)) {
+    g_err = keep;
+    return 0;
+  }
+  return forward_layout(z, pv_dtype, o.q_block).total;
+}
+
+int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                      int pv_dtype, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                      const sqattn_opts* opts) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  Opts o;
+  if ((s = validate_forward(q, k, v, B, H, N, d, scale, pv_dtype, out, opts, &z, &o))) return s;
+  const FwdLayout L = forward_layout(z, pv_dtype, o.q_block);
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  if ((s = ws.acquire(workspace, workspace_bytes, L.total, st))) return s;
+  const int BH = (int)z.BH;
+  int8_t* qi = ws.at<int8_t>(L.q_i8);
+  int8_t* ki = ws.at<int8_t>(L.k_i8);
+  float* qs = ws.at<float>(L.q_scale);
+  float* ks = ws.at<float>(L.k_scale);
+  float* km = ws.at<float>(L.k_mean);
+  sqattn::launch_quant_i8((const uint16_t*)q, BH, N, d, o.q_block, nullptr, qi, qs, st);
+  sqattn::launch_kmean((const uint16_t*)k, BH, N, d, ws.at<uint64_t>(L.partial), km, st);
+  sqattn::launch_quant_i8((const uint16_t*)k, BH, N, d, o.k_block, km, ki, ks, st);
+  float* vs = nullptr;
+  if (pv_dtype == SQATTN_PV_BF16) {
+    sqattn::launch_v_tiles_bf16((const uint16_t*)v, BH, N, d, ws.at<uint16_t>(L.vt), st);
+  } else {
+    vs = ws.at<float>(L.v_scale);
+    sqattn::launch_quant_v_fp8((const uint16_t*)v, BH, N, d, nullptr, ws.at<uint8_t>(L.vt), vs, st);
+  }
+  sqattn::AttnParams p{};
+  p.q = qi;
+  p.sq = qs;
+  p.k = ki;
+  p.sk = ks;
+  p.vt = ws.at<void>(L.vt);
+  p.sv = vs;
+  p.out = out;
+  p.N = N;
+  p.nq = (int)z.nq;
+  p.q_block = o.q_block;
+  p.nt = (int)z.nt;
+  p.BH = BH;
+  p.scale_log2e = scale * kLog2e;
+  sqattn::launch_attention(p, d, pv_dtype, st);
+  return hip_check("sqattn_forward launch");
+}
+
+int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                   int pv_dtype, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return sqattn_forward_ex(q, k, v, B, H, N, d, scale, pv_dtype, out, workspace, workspace_bytes, stream,
+                           nullptr);
+}
+
+size_t sqattn_packed_v_bytes(int B, int H, int N, int d, int pv_dtype) {
+  std::string keep = g_err;
+  Sizes z;
+  if (check_shape(B, H, N, d, &z) || (pv_dtype != 0 && pv_dtype != 1)) {
+    g_err = keep;
+    return 0;
+  }
+  return (size_t)(z.BH * z.nt * z.d * sqattn::KT) * (pv_dtype == SQATTN_PV_BF16 ? 2 : 1);
+}
+
+int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void* v_packed, void* stream) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  if ((s = check_ptr(v, "v", 16)) || (s = check_ptr(v_packed, "v_packed", 16))) return s;
+  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if (pv_dtype != SQATTN_PV_BF16 && pv_dtype != SQATTN_PV_FP8_E4M3)
+    return fail(SQATTN_ERR_INVALID_ARG, "unknown pv_dtype");
+  hipStream_t st = (hipStream_t)stream;
+  if (pv_dtype == SQATTN_PV_BF16)
+    sqattn::launch_v_tiles_bf16((const uint16_t*)v, (int)z.BH, N, d, (uint16_t*)v_packed, st);
+  else
+    sqattn::launch_v_tiles_fp8((const uint8_t*)v, (int)z.BH, N, d, (uint8_t*)v_packed, st);
+  return hip_check("sqattn_pack_v launch");
+}
+
+int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
+                            int pv_dtype, const sqattn_opts* opts, float* out, void* stream) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  Opts o;
+  if ((s = check_ptr(q_i8, "q_i8", 16)) || (s = check_ptr(k_i8, "k_i8", 16)) ||
+      (s = check_ptr(q_scale, "q_scale", 4)) || (s = check_ptr(k_scale, "k_scale", 4)) ||
+      (s = check_ptr(v_packed, "v_packed", 16)) || (s = check_ptr(out, "out", 16)))
+    return s;
+  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if (pv_dtype != SQATTN_PV_BF16 && pv_dtype != SQATTN_PV_FP8_E4M3)
+    return fail(SQATTN_ERR_INVALID_ARG, "unknown pv_dtype");
+  if (pv_dtype == SQATTN_PV_FP8_E4M3 && (s = check_ptr(v_scale, "v_scale", 4))) return s;
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(SQATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((s = resolve_opts(opts, &o))) return s;
+  sqattn::AttnParams p{};
+  p.q = q_i8;
+  p.sq = q_scale;
+  p.k = k_i8;
+  p.sk = k_scale;
+  p.vt = v_packed;
+  p.sv = v_scale;
+  p.out = out;
+  p.N = N;
+  p.nq = (int)((N + o.q_block - 1) / o.q_block);
+  p.q_block = o.q_block;
+  p.nt = (int)z.nt;
+  p.BH = (int)z.BH;
+  p.scale_log2e = scale * kLog2e;
+  sqattn::launch_attention(p, d, pv_dtype, (hipStream_t)stream);
+  return hip_check("sqattn_attend_quantized launch");
+}
+
+}  // extern "C"

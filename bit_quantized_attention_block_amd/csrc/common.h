@@ -1,0 +1,39 @@
+// Shared device-side definitions of the sqattn HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqattn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Attention tile: 64 keys.  K blocks must coincide with these tiles.
+constexpr int KT = 64;
+// Attention work-group: 4 waves, 64 query rows each.
+constexpr int ATT_WAVES = 4;
+constexpr int ATT_QW = 64;
+constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Layout of one 64-key V tile inside the kernel (both in HBM workspace and LDS):
+// transposed, [d][64 keys].  For FP8 the 64 key bytes of a row are permuted so
+// that the 32 keys one MFMA lane-half consumes are contiguous:
+//   pos(key) = g*32 + (key/16)*8 + key%8 with g = (key/8)%2.
+__host__ __device__ __forceinline__ int fp8_key_pos(int key) {
+  return (((key >> 3) & 1) << 5) | ((key >> 4) << 3) | (key & 7);
+}
+
+// Size helpers shared by host code.
+__host__ __device__ __forceinline__ long long ceil_div_ll(long long a, long long b) {
+  return (a + b - 1) / b;
+}
+
+}  // namespace sqattn

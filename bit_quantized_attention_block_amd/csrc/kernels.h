@@ -1,0 +1,33 @@
+// Host-side launchers of the sqattn kernels (all enqueue on the given stream).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqattn {
+
+int kmean_chunks(int BH, int N);
+void launch_kmean(const uint16_t* k, int BH, int N, int d, uint64_t* partial, float* mean,
+                  hipStream_t st);
+void launch_quant_i8(const uint16_t* x, int BH, int N, int d, int block, const float* mean,
+                     int8_t* codes, float* scales, hipStream_t st);
+void launch_v_tiles_bf16(const uint16_t* v, int BH, int N, int d, uint16_t* vt, hipStream_t st);
+void launch_quant_v_fp8(const uint16_t* v, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
+                        float* scales, hipStream_t st);
+void launch_v_tiles_fp8(const uint8_t* codes, int BH, int N, int d, uint8_t* vt, hipStream_t st);
+
+struct AttnParams {
+  const int8_t* q;
+  const float* sq;
+  const int8_t* k;
+  const float* sk;
+  const void* vt;
+  const float* sv;
+  float* out;
+  int N, nq, q_block, nt, BH, qtiles, per_xcd;
+  float scale_log2e;
+};
+
+void launch_attention(const AttnParams& p, int d, int pv, hipStream_t st);
+
+}  // namespace sqattn

@@ -1,0 +1,378 @@
+// Quantization kernels of the sqattn path (gfx950).
+//
+//   kmean_partial / kmean_finalize : exact per-channel K mean (192-bit fixed
+//       point, one rounding), the smoothing step named in the SageAttention2
+//       title (GVCLab Video-Generation-101 systems survey, reference [3]).
+//   quant_i8 : per-block INT8 codes of Q and of the smoothed K (jefxiong.cn
+//       "AIGC weekend special 5.10", section 1.2 item (1): Q/K to low bit so
+//       QK^T runs on integer matrix units).  s = fl32(absmax/127),
+//       code = clamp(rne(fl32(x/s)), -127, 127).
+//   v_tiles_bf16 : V into the attention kernel's tile layout ([d][64 keys]).
+//   quant_v_fp8 : per-64-row E4M3 codes of V (GVCLab research log 2026-09-02,
+//       section 5.5 table: FP8 P.V), s_v = fl32(absmax/448).
+//
+// All kernels are HBM-bound streaming passes; loads and stores are 16-byte
+// per lane along rows so that each wave touches whole 128-byte lines.
+#include "common.h"
+#include "e4m3.h"
+#include "exact.h"
+#include "kernels.h"
+
+namespace sqattn {
+
+// ---------------------------------------------------------------------------
+// exact K mean
+// ---------------------------------------------------------------------------
+
+// grid (S, B*H), 256 threads.  Chunk c of a head covers rows
+// [c*rows_per_chunk, min(N, (c+1)*rows_per_chunk)).  Thread t reads channels
+// (t % CPR)*8 .. +8 (CPR = D/8 16-byte pieces per row) of rows
+// r0 + t/CPR + j*RPP (RPP = 256/CPR rows per pass).
+template <int D>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __restrict__ k, int N,
+                                                            int rows_per_chunk,
+                                                            uint64_t* __restrict__ partial) {
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 256 / CPR;
+  const int chunk = blockIdx.x, S = gridDim.x;
+  const long long bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int cg = t % CPR, rg = t / CPR;
+  const uint16_t* kh = k + bh * (long long)N * D;
+  int r0 = chunk * rows_per_chunk;
+  int r1 = min(N, r0 + rows_per_chunk);
+
+  Acc192 acc[8];
+  int64_t win[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc192_zero(acc[j]);
+    win[j] = 0;
+  }
+  bool bad = false;
+  for (int r = r0 + rg; r < r1; r += RPP) {
+    v4i w = *(const v4i*)(kh + (long long)r * D + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t u = (uint32_t)w[j];
+      bad |= kmean_accumulate(acc[2 * j], win[2 * j], u & 0xFFFFu);
+      bad |= kmean_accumulate(acc[2 * j + 1], win[2 * j + 1], u >> 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kmean_flush_window(acc[j], win[j]);
+
+  // reduce the RPP row groups of each channel through LDS
+  __shared__ Acc192 red[RPP][D];
+  __shared__ int redbad[256];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rg][cg * 8 + j] = acc[j];
+  redbad[t] = bad ? 1 : 0;
+  __syncthreads();
+  if (t < D) {
+    Acc192 s;
+    acc192_zero(s);
+    int anybad = 0;
+    for (int g = 0; g < RPP; ++g) acc192_add(s, red[g][t]);
+    for (int i = 0; i < 256; ++i) anybad |= redbad[i];
+    uint64_t* p = partial + ((bh * S + chunk) * D + t) * 4;
+    p[0] = s.w0;
+    p[1] = s.w1;
+    p[2] = s.w2;
+    p[3] = (uint64_t)anybad;
+  }
+}
+
+// grid (B*H), D threads: sums the S partials of a channel and rounds the mean.
+template <int D>
+__global__ __launch_bounds__(D) void kmean_finalize_kernel(const uint64_t* __restrict__ partial,
+                                                           int S, int N, float* __restrict__ mean) {
+  const long long bh = blockIdx.x;
+  const int c = threadIdx.x;
+  Acc192 s;
+  acc192_zero(s);
+  uint64_t bad = 0;
+  for (int i = 0; i < S; ++i) {
+    const uint64_t* p = partial + ((bh * S + i) * D + c) * 4;
+    acc192_add(s, p[0], p[1], p[2]);
+    bad |= p[3];
+  }
+  mean[bh * D + c] = bad ? __builtin_nanf("") : acc192_mean_f32(s, (uint32_t)N);
+}
+
+// ---------------------------------------------------------------------------
+// per-block INT8 quantization
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float block_max_256(float v, float* sh) {
+  // max over the 256 threads of the work-group (all values >= 0 or NaN-free)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+// grid (nblocks, B*H), 256 threads.  One work-group per block of `block` rows.
+// mean == nullptr: plain Q.  Otherwise x = fl32(K - mean[c]) (IEEE subtract).
+template <int D>
+__global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, int N, int block,
+                                                       const float* __restrict__ mean,
+                                                       int8_t* __restrict__ codes,
+                                                       float* __restrict__ scales) {
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 256 / CPR;
+  __shared__ float sh[4];
+  const long long bh = blockIdx.y;
+  const int blk = blockIdx.x, nblk = gridDim.x;
+  const int t = threadIdx.x, cg = t % CPR, rg = t / CPR;
+  const uint16_t* xh = x + bh * (long long)N * D;
+  int8_t* ch = codes + bh * (long long)N * D;
+  const int r0 = blk * block, r1 = min(N, r0 + block);
+
+  float mu[8];
+  bool mean_nan = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    mu[j] = mean ? mean[bh * D + cg * 8 + j] : 0.0f;
+    mean_nan |= (mu[j] != mu[j]);
+  }
+
+  float amax = 0.0f;
+  for (int r = r0 + rg; r < r1; r += RPP) {
+    v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t u = (uint32_t)w[j];
+      float a = bf16_bits_to_f32(u & 0xFFFFu), b = bf16_bits_to_f32(u >> 16);
+      if (mean) {
+        a = a - mu[2 * j];
+        b = b - mu[2 * j + 1];
+      }
+      amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
+    }
+  }
+  // a NaN mean (K out of range) poisons the whole block's scale
+  float nanflag = block_max_256(mean_nan ? 1.0f : 0.0f, sh);
+  amax = block_max_256(amax, sh);
+  const float s = amax / 127.0f;  // correctly rounded binary32 division
+  if (t == 0) scales[bh * nblk + blk] = (nanflag > 0.0f) ? __builtin_nanf("") : s;
+  const bool zero = !(s > 0.0f) || (nanflag > 0.0f);
+
+  for (int r = r0 + rg; r < r1; r += RPP) {
+    v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t u = (uint32_t)w[j >> 1];
+      float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
+      if (mean) a = a - mu[j];
+      int c = 0;
+      if (!zero) {
+        float qv = rintf(a / s);  // rne of the correctly rounded quotient
+        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+        c = (int)qv;
+      }
+      packed[j >> 2] |= ((uint32_t)(c & 0xFF)) << ((j & 3) * 8);
+    }
+    *(uint2*)(ch + (long long)r * D + cg * 8) = make_uint2(packed[0], packed[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V layouts for the attention kernel
+// ---------------------------------------------------------------------------
+
+// grid (nt, B*H), 256 threads: V bf16 [N][D] -> Vt [nt][D][64] bf16 (tile t,
+// channel c, key j) with zeros for keys >= N.
+template <int D>
+__global__ __launch_bounds__(256) void v_tiles_bf16_kernel(const uint16_t* __restrict__ v, int N,
+                                                           uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[KT][D + 8];
+  const long long bh = blockIdx.y;
+  const int tt = blockIdx.x, nt = gridDim.x;
+  const int t = threadIdx.x;
+  const uint16_t* vh = v + bh * (long long)N * D;
+  constexpr int CPR = D / 8;
+  for (int i = t; i < KT * CPR; i += 256) {
+    int r = i / CPR, c8 = (i % CPR) * 8;
+    int key = tt * KT + r;
+    v4i w = (key < N) ? *(const v4i*)(vh + (long long)key * D + c8) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][c8 + 2 * j] = (uint16_t)((uint32_t)w[j] & 0xFFFFu);
+      tile[r][c8 + 2 * j + 1] = (uint16_t)((uint32_t)w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* out = vt + (bh * nt + tt) * (long long)D * KT;
+  for (int i = t; i < D * (KT / 8); i += 256) {
+    int c = i / (KT / 8), k8 = (i % (KT / 8)) * 8;
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p[j] = (uint32_t)tile[k8 + 2 * j][c] | ((uint32_t)tile[k8 + 2 * j + 1][c] << 16);
+    *(v4i*)(out + (long long)c * KT + k8) = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+  }
+}
+
+// grid (nt, B*H), 256 threads.  One 64-row block of V: s_v = fl32(absmax/448),
+// codes E4M3(fl32(V/s_v)).  Writes the [N][D] codes (if codes != nullptr)
+// and/or the attention tile layout [nt][D][64] with FP8 key positions
+// (if vt != nullptr, zero for keys >= N), and the scale.
+template <int D>
+__global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __restrict__ v, int N,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ vt,
+                                                          float* __restrict__ scales) {
+  __shared__ float sh[4];
+  __shared__ uint8_t tile[KT][D + 16];
+  const long long bh = blockIdx.y;
+  const int tt = blockIdx.x, nt = gridDim.x;
+  const int t = threadIdx.x;
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 256 / CPR;
+  const int cg = t % CPR, rg = t / CPR;
+  const uint16_t* vh = v + bh * (long long)N * D;
+  const int r0 = tt * KT, r1 = min(N, r0 + KT);
+  float amax = 0.0f;
+  for (int r = r0 + rg; r < r1; r += RPP) {
+    v4i w = *(const v4i*)(vh + (long long)r * D + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t u = (uint32_t)w[j];
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(u & 0xFFFFu)), fabsf(bf16_bits_to_f32(u >> 16))));
+    }
+  }
+  amax = block_max_256(amax, sh);
+  const float s = amax / 448.0f;
+  if (t == 0) scales[bh * nt + tt] = s;
+  const bool zero = !(s > 0.0f);
+  for (int r = r0 + rg; r < r0 + KT; r += RPP) {
+    uint32_t packed[2] = {0u, 0u};
+    if (r < r1) {
+      v4i w = *(const v4i*)(vh + (long long)r * D + cg * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t u = (uint32_t)w[j >> 1];
+        float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
+        uint32_t c = zero ? 0u : e4m3_encode_f32(a / s);
+        packed[j >> 2] |= c << ((j & 3) * 8);
+      }
+      if (codes)
+        *(uint2*)(codes + (bh * (long long)N + r) * D + cg * 8) = make_uint2(packed[0], packed[1]);
+    }
+    if (vt) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[r - r0][cg * 8 + j] = (uint8_t)(packed[j >> 2] >> ((j & 3) * 8));
+    }
+  }
+  if (!vt) return;
+  __syncthreads();
+  uint8_t* out = vt + (bh * nt + tt) * (long long)D * KT;
+  // each thread writes 16 consecutive positions of one channel row
+  for (int i = t; i < D * (KT / 16); i += 256) {
+    int c = i / (KT / 16), p0 = (i % (KT / 16)) * 16;
+    uint32_t p[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int pos = p0 + j;
+      // inverse of fp8_key_pos: pos = g*32 + q*8 + r -> key = q*16 + g*8 + r
+      int key = ((pos >> 3) & 3) * 16 + (pos >> 5) * 8 + (pos & 7);
+      p[j >> 2] |= (uint32_t)tile[key][c] << ((j & 3) * 8);
+    }
+    *(v4i*)(out + (long long)c * KT + p0) = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+  }
+}
+
+// grid (nt, B*H), 256 threads: FP8 codes [N][D] (as written by quant_v_fp8)
+// -> attention tile layout.  Used when the caller supplies quantized V.
+template <int D>
+__global__ __launch_bounds__(256) void v_tiles_fp8_kernel(const uint8_t* __restrict__ codes, int N,
+                                                          uint8_t* __restrict__ vt) {
+  __shared__ uint8_t tile[KT][D + 16];
+  const long long bh = blockIdx.y;
+  const int tt = blockIdx.x, nt = gridDim.x;
+  const int t = threadIdx.x;
+  for (int i = t; i < KT * (D / 16); i += 256) {
+    int r = i / (D / 16), c16 = (i % (D / 16)) * 16;
+    int key = tt * KT + r;
+    v4i w = (key < N) ? *(const v4i*)(codes + (bh * (long long)N + key) * D + c16) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[r][c16 + j] = (uint8_t)((uint32_t)w[j >> 2] >> ((j & 3) * 8));
+  }
+  __syncthreads();
+  uint8_t* out = vt + (bh * nt + tt) * (long long)D * KT;
+  for (int i = t; i < D * (KT / 16); i += 256) {
+    int c = i / (KT / 16), p0 = (i % (KT / 16)) * 16;
+    uint32_t p[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int pos = p0 + j;
+      int key = ((pos >> 3) & 3) * 16 + (pos >> 5) * 8 + (pos & 7);
+      p[j >> 2] |= (uint32_t)tile[key][c] << ((j & 3) * 8);
+    }
+    *(v4i*)(out + (long long)c * KT + p0) = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+#define SQ_DISPATCH_D(d, KERNEL, GRID, BLOCK, STREAM, ...)                         \
+  do {                                                                              \
+    if ((d) == 128)                                                                 \
+      hipLaunchKernelGGL(KERNEL<128>, GRID, BLOCK, 0, STREAM, __VA_ARGS__);         \
+    else                                                                            \
+      hipLaunchKernelGGL(KERNEL<64>, GRID, BLOCK, 0, STREAM, __VA_ARGS__);          \
+  } while (0)
+
+int kmean_chunks(int BH, int N) {
+  // enough work-groups to cover the chip a few times, each at least 256 rows;
+  // at most 2^18 rows per chunk so that each thread adds at most 2^14 values
+  // (< 2^48 each) into its 64-bit window accumulator
+  int s = (2048 + BH - 1) / BH;
+  int maxs = (N + 255) / 256;
+  if (s > maxs) s = maxs;
+  int mins = (N + (1 << 18) - 1) >> 18;
+  if (s < mins) s = mins;
+  if (s < 1) s = 1;
+  return s;
+}
+
+void launch_kmean(const uint16_t* k, int BH, int N, int d, uint64_t* partial, float* mean,
+                  hipStream_t st) {
+  int S = kmean_chunks(BH, N);
+  int rows = (N + S - 1) / S;
+  SQ_DISPATCH_D(d, kmean_partial_kernel, dim3(S, BH), dim3(256), st, k, N, rows, partial);
+  if (d == 128)
+    hipLaunchKernelGGL(kmean_finalize_kernel<128>, dim3(BH), dim3(128), 0, st, partial, S, N, mean);
+  else
+    hipLaunchKernelGGL(kmean_finalize_kernel<64>, dim3(BH), dim3(64), 0, st, partial, S, N, mean);
+}
+
+void launch_quant_i8(const uint16_t* x, int BH, int N, int d, int block, const float* mean,
+                     int8_t* codes, float* scales, hipStream_t st) {
+  int nb = (N + block - 1) / block;
+  SQ_DISPATCH_D(d, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, N, block, mean, codes, scales);
+}
+
+void launch_v_tiles_bf16(const uint16_t* v, int BH, int N, int d, uint16_t* vt, hipStream_t st) {
+  int nt = (N + KT - 1) / KT;
+  SQ_DISPATCH_D(d, v_tiles_bf16_kernel, dim3(nt, BH), dim3(256), st, v, N, vt);
+}
+
+void launch_quant_v_fp8(const uint16_t* v, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
+                        float* scales, hipStream_t st) {
+  int nt = (N + KT - 1) / KT;
+  SQ_DISPATCH_D(d, quant_v_fp8_kernel, dim3(nt, BH), dim3(256), st, v, N, codes, vt, scales);
+}
+
+void launch_v_tiles_fp8(const uint8_t* codes, int BH, int N, int d, uint8_t* vt, hipStream_t st) {
+  int nt = (N + KT - 1) / KT;
+  SQ_DISPATCH_D(d, v_tiles_fp8_kernel, dim3(nt, BH), dim3(256), st, codes, N, vt);
+}
+
+}  // namespace sqattn

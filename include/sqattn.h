@@ -1,0 +1,188 @@
+/*
+ * sqattn.h - low-bit quantized self-attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the quantized attention step of TurboDiffusion's video-DiT
+ * denoiser (SageAttention2++): Q and K are quantized per block to INT8 so that
+ * QK^T runs on the integer matrix units, then softmax, then P.V in 16-bit or
+ * FP8 (jefxiong.cn "AIGC weekend special 5.10", section 1.2, item (1);
+ * digipub.cc TurboDiffusion article, attention-acceleration paragraph; GVCLab
+ * research log 2026-09-02, section 5.5 table, SageAttention2 row).  K is first
+ * smoothed by removing its per-channel mean over tokens (the outlier smoothing
+ * in the SageAttention2 title, GVCLab Video-Generation-101 systems survey,
+ * reference [3]).
+ *
+ * Conventions for every entry point
+ *   - Tensors are DEVICE pointers to contiguous [B, H, N, d] row-major data
+ *     (BHND), 16-byte aligned.  bf16 data is passed as raw 16-bit patterns.
+ *   - Per-block scale arrays are contiguous [B, H, nblocks] float32 with
+ *     nblocks = ceil(N / block); block i covers rows [i*block, min(N, (i+1)*block))
+ *     and all d channels of one (b, h) head.
+ *   - The caller owns every buffer.  The library keeps no pointer after a call
+ *     returns and frees nothing it did not allocate.  Its only global state is
+ *     a thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     runs asynchronously; the call returns once it is enqueued.  Output
+ *     buffers must not alias inputs.
+ *   - Status codes are returned, never thrown.  Argument problems are reported
+ *     before anything is enqueued.  There is no fallback path: a request this
+ *     library has no kernel for returns SQATTN_ERR_UNSUPPORTED.
+ *   - Results are deterministic: identical inputs give bit-identical outputs
+ *     (fixed reduction orders, no floating-point atomics).
+ *
+ * Numerics (where the method statement is silent, these are the readings used)
+ *   - K mean: mu[c] = fl32(S_c / N), S_c the exact sum of the bf16 values over
+ *     the N tokens (192-bit fixed point, rounded once, nearest-even).  A head
+ *     holding any |K| >= 2^33 is outside that accumulator's range: its mu is
+ *     set to NaN (and the codes/scales derived from it are meaningless).
+ *   - K' = fl32(K - mu) (IEEE binary32, subnormals kept).  Q is not smoothed.
+ *   - INT8 scale s = fl32(absmax / 127), correctly rounded; s = 0 for an
+ *     all-zero block.  Code = clamp(rne(fl32(x / s)), -127, 127), i.e. the
+ *     correctly rounded binary32 quotient rounded half-to-even to an integer;
+ *     code = 0 where s = 0.  -128 never occurs.
+ *   - FP8 V: s_v = fl32(absmax / 448) per block of 64 rows; code =
+ *     E4M3FN(fl32(V / s_v)) (OCP E4M3, bias 7, max 448, nearest-even,
+ *     saturating, sign of zero kept); code = 0 where s_v = 0.
+ *   - Attention is non-causal over all N keys.  Logits are
+ *     D * sQ * sK * scale with D the exact int32 dot product of the codes.
+ *     Softmax uses a running max over 64-key tiles; P.V accumulates in fp32;
+ *     the output is fp32.  With SQATTN_PV_FP8_E4M3 the kernel rounds
+ *     448 * exp(s - m_tile) to E4M3 (m_tile the running max after each 64-key
+ *     tile) and keeps the unrounded values in the row sum.
+ */
+#ifndef SQATTN_H_
+#define SQATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SQATTN_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  SQATTN_OK = 0,
+  SQATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad option */
+  SQATTN_ERR_UNSUPPORTED = 2, /* valid request with no kernel (e.g. d not in {64,128}) */
+  SQATTN_ERR_WORKSPACE = 3,   /* supplied workspace smaller than required */
+  SQATTN_ERR_HIP = 4,         /* the HIP runtime reported an error when enqueuing */
+  SQATTN_ERR_RANGE = 5        /* sizes whose index arithmetic would overflow */
+} sqattn_status;
+
+typedef enum { SQATTN_PV_BF16 = 0, SQATTN_PV_FP8_E4M3 = 1 } sqattn_pv_dtype;
+
+/* Block sizes.  A zero field takes its default.  q_block: any multiple of 16
+ * (default 128).  k_block: 64 (the attention tile; default).  v_block: 64
+ * (FP8 only; default).  reserved must be 0. */
+typedef struct sqattn_opts {
+  int q_block;
+  int k_block;
+  int v_block;
+  int reserved;
+} sqattn_opts;
+
+/* SQATTN_VERSION of the loaded library. */
+int sqattn_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* sqattn_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none).  Valid until
+ * the next library call on the same thread. */
+const char* sqattn_last_error(void);
+
+/*
+ * Bytes of device workspace that sqattn_quantize_qk needs for these sizes
+ * (the partial sums of the exact K mean).  0 for invalid sizes.
+ */
+size_t sqattn_quantize_qk_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Quantize Q and K (smoothing K by its per-channel mean first).
+ *   q, k      : bf16 [B,H,N,d] inputs.
+ *   q_i8      : int8 [B,H,N,d] codes of Q;  q_scale : float [B,H,ceil(N/q_block)].
+ *   k_i8      : int8 [B,H,N,d] codes of K'; k_scale : float [B,H,ceil(N/k_block)].
+ *   k_mean    : float [B,H,d], the mean that was removed from K.
+ *   q_block   : multiple of 16; k_block : multiple of 16 (64 for use with
+ *               sqattn_attend_quantized).
+ *   workspace : device memory of at least sqattn_quantize_qk_workspace_bytes();
+ *               NULL makes the library allocate it stream-ordered on `stream`
+ *               (and free it after use, stream-ordered).
+ * B, H, N >= 1; d in {64, 128}; B*H*N*d < 2^40.
+ */
+int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int q_block,
+                       int k_block, int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                       float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantize V to OCP E4M3 per block of v_block (= 64) rows.
+ *   v       : bf16 [B,H,N,d];  v_fp8 : uint8 [B,H,N,d] codes;
+ *   v_scale : float [B,H,ceil(N/v_block)].
+ */
+int sqattn_quantize_v_fp8(const void* v, int B, int H, int N, int d, int v_block, uint8_t* v_fp8,
+                          float* v_scale, void* stream);
+
+/*
+ * Bytes of device workspace sqattn_forward / sqattn_forward_ex need
+ * (INT8 Q and K with their scales, the K mean, V in the kernel's tiled
+ * transposed layout, and the K mean partial sums).  opts may be NULL.
+ * 0 for invalid arguments.
+ */
+size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sqattn_opts* opts);
+
+/*
+ * Full forward: out = softmax(Q K^T * scale) V computed on quantized
+ * operands (the steps above), fp32 out [B,H,N,d].
+ *   scale     : softmax scale applied to the logits (commonly 1/sqrt(d)),
+ *               finite and >= 0.
+ *   pv_dtype  : SQATTN_PV_BF16 or SQATTN_PV_FP8_E4M3.
+ *   workspace : >= sqattn_workspace_bytes() bytes of device memory, 256-byte
+ *               aligned, or NULL for a stream-ordered allocation by the
+ *               library on `stream`.
+ * Defaults: q_block 128, k_block 64, v_block 64.
+ */
+int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                   float scale, int pv_dtype, float* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* sqattn_forward with explicit block sizes (opts may be NULL = defaults). */
+int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      float scale, int pv_dtype, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream, const sqattn_opts* opts);
+
+/*
+ * V in the attention kernel's tile layout ("packed V").  Tile t of a head
+ * holds keys [64t, 64t+64) transposed, [d][64], zero past N:
+ *   SQATTN_PV_BF16     : bf16, element (c, j) at ((bh*nt + t)*d + c)*64 + j.
+ *   SQATTN_PV_FP8_E4M3 : E4M3 codes, one byte per element; within each
+ *                        64-byte channel row key j sits at position
+ *                        32*((j/8)%2) + 8*(j/16) + j%8 (the order the FP8
+ *                        matrix instruction consumes keys in).
+ * nt = ceil(N/64).  Size: sqattn_packed_v_bytes().
+ *   v : bf16 [B,H,N,d] for SQATTN_PV_BF16; E4M3 codes [B,H,N,d] (as written
+ *       by sqattn_quantize_v_fp8) for SQATTN_PV_FP8_E4M3.
+ */
+size_t sqattn_packed_v_bytes(int B, int H, int N, int d, int pv_dtype);
+int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void* v_packed,
+                  void* stream);
+
+/*
+ * Attention on prepared operands: a single kernel launch (the hot kernel
+ * alone, for parity and kernel timing).
+ *   q_i8/q_scale/k_i8/k_scale : as written by sqattn_quantize_qk with
+ *              k_block = 64 and q_block = opts->q_block (default 128).
+ *   v_packed : from sqattn_pack_v with the same pv_dtype.
+ *   v_scale  : [B,H,ceil(N/64)] from sqattn_quantize_v_fp8 for FP8; NULL for bf16.
+ *   out      : fp32 [B,H,N,d].
+ */
+int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                            const float* k_scale, const void* v_packed, const float* v_scale,
+                            int B, int H, int N, int d, float scale, int pv_dtype,
+                            const sqattn_opts* opts, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQATTN_H_ */

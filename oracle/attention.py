@@ -22,7 +22,12 @@ Readings where the pages are silent:
     sum accumulates the unrounded P~; V enters as s_v * decode(code_v).
     Elements whose 448*P~ lies within ``eps_rel`` of an E4M3 rounding midpoint
     may legitimately round either way in the kernel's binary32 arithmetic; the
-    possible effect of each is summed into a per-element envelope E.
+    possible effect of each is summed into a per-element envelope E.  The
+    default width is per row, eps_r = 2^-20 * (1 + M_r) with M_r the row's
+    largest |logit| in log2 units: the kernel's logit factor
+    sQ*sK*scale*log2(e) carries up to four binary32 roundings (2^-22
+    relative), so x - m is off by at most 2^-21 * M_r, and exp2 adds about
+    2^-22; the default doubles that bound.
 """
 from __future__ import annotations
 
@@ -99,7 +104,7 @@ def e4m3_round_f64(y: np.ndarray):
 
 
 def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_block, k_block,
-               scale, v_block: int = 64, kv_tile: int = 64, eps_rel: float = 2.0 ** -16,
+               scale, v_block: int = 64, kv_tile: int = 64, eps_rel: float | None = None,
                round_p=None, chunk: int = 128):
     """FP8 P.V path for one head; returns (O [R, d], E [R, d], hits).
 
@@ -136,8 +141,12 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
         num = (w * yr / 448.0) @ Vh
         O[i:i + chunk] = num / l
         if round_p is None:
+            if eps_rel is None:
+                eps = 2.0 ** -20 * (1.0 + np.abs(S).max(axis=1, keepdims=True) / np.log(2.0))
+            else:
+                eps = eps_rel
             frac = c - np.floor(c)
-            amb = (np.abs(frac - 0.5) * quantum <= eps_rel * y) & (y > 0)
+            amb = (np.abs(frac - 0.5) * quantum <= eps * y) & (y > 0)
             if amb.any():
                 lo = np.floor(c) * quantum
                 hi = np.minimum((np.floor(c) + 1.0) * quantum, fp.E4M3_MAX)

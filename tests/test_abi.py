@@ -1,0 +1,156 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol that
+include/sqattn.h declares (as unmangled C symbols), and rejects bad arguments
+with the documented status before anything is enqueued (so no GPU is needed:
+every call below returns from host-side validation)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_quantized_attention_block_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "sqattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, RANGE = 0, 1, 2, 3, 4, 5
+FAKE = 0x100000          # 256-byte aligned, never dereferenced
+BIG = 1 << 40
+
+
+def declared():
+    txt = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(sqattn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = sq.lib()
+    names = declared()
+    assert len(names) == 12
+    assert set(names) == set(sq.EXPORTS), "binding and header disagree"
+    for n in names:
+        assert hasattr(L, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", sq.lib_path], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    for n in names:
+        assert n in syms, f"{n} is not an exported C symbol"
+    assert sq.version() == 10000
+
+
+def test_status_strings():
+    L = sq.lib()
+    for s in range(6):
+        assert L.sqattn_status_string(s).decode()
+    assert L.sqattn_status_string(99).decode() == "unknown status"
+
+
+def _fwd(q=FAKE, k=FAKE, v=FAKE, B=1, H=1, N=256, d=64, scale=0.125, pv=0, out=FAKE, ws=FAKE, wsb=1,
+         opts=None):
+    L = sq.lib()
+    o = ctypes.byref(opts) if opts is not None else None
+    return L.sqattn_forward_ex(q, k, v, B, H, N, d, scale, pv, out, ws, wsb, None, o)
+
+
+def _err():
+    return sq.lib().sqattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(v=None), INVALID, "v is NULL"),
+    (dict(out=FAKE + 4), INVALID, "aligned"),
+    (dict(k=FAKE + 8), INVALID, "aligned"),
+    (dict(B=0), INVALID, ">= 1"),
+    (dict(N=0), INVALID, ">= 1"),
+    (dict(H=-3), INVALID, ">= 1"),
+    (dict(d=96), UNSUPPORTED, "64 or 128"),
+    (dict(d=256), UNSUPPORTED, "64 or 128"),
+    (dict(N=1 << 24), RANGE, "2^24"),
+    (dict(B=300, H=300), RANGE, "65535"),
+    (dict(pv=2), INVALID, "pv_dtype"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(scale=-1.0), INVALID, "scale"),
+    (dict(wsb=1), WORKSPACE, "needed"),
+    (dict(ws=FAKE + 16, wsb=BIG), INVALID, "256-byte"),
+    (dict(opts=sq.Opts(128, 128, 64, 0)), UNSUPPORTED, "k_block"),
+    (dict(opts=sq.Opts(128, 64, 32, 0)), UNSUPPORTED, "v_block"),
+    (dict(opts=sq.Opts(24, 64, 64, 0)), INVALID, "q_block"),
+    (dict(opts=sq.Opts(128, 64, 64, 1)), INVALID, "reserved"),
+])
+def test_forward_validation(kw, code, needle):
+    assert _fwd(**kw) == code
+    assert needle in _err()
+
+
+def test_quantize_validation():
+    L = sq.lib()
+    args = [FAKE, FAKE, 1, 1, 256, 128, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None]
+    a = list(args)
+    a[6] = 0
+    assert L.sqattn_quantize_qk(*a) == INVALID and "q_block" in _err()
+    a = list(args)
+    a[7] = 8
+    assert L.sqattn_quantize_qk(*a) == INVALID and "k_block" in _err()
+    a = list(args)
+    a[12] = None
+    assert L.sqattn_quantize_qk(*a) == INVALID and "k_mean" in _err()
+    a = list(args)
+    a[11] = FAKE + 2
+    assert L.sqattn_quantize_qk(*a) == INVALID and "k_scale" in _err()
+    # workspace present but too small
+    assert L.sqattn_quantize_qk(*args) == WORKSPACE
+    assert L.sqattn_quantize_v_fp8(FAKE, 1, 1, 256, 128, 32, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.sqattn_quantize_v_fp8(None, 1, 1, 256, 128, 64, FAKE, FAKE, None) == INVALID
+
+
+def test_attend_and_pack_validation():
+    L = sq.lib()
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 300, 128, 0.1, 1, None, FAKE, None]
+    a = list(base)
+    a[5] = None                                           # fp8 needs v_scale
+    assert L.sqattn_attend_quantized(*a) == INVALID and "v_scale" in _err()
+    a = list(base)
+    a[11] = 7
+    assert L.sqattn_attend_quantized(*a) == INVALID
+    a = list(base)
+    a[4] = FAKE + 1
+    assert L.sqattn_attend_quantized(*a) == INVALID and "v_packed" in _err()
+    a = list(base)
+    a[9] = 32
+    assert L.sqattn_attend_quantized(*a) == UNSUPPORTED
+    assert L.sqattn_pack_v(FAKE, 1, 1, 100, 128, 3, FAKE, None) == INVALID
+    assert L.sqattn_pack_v(FAKE, 1, 1, 100, 128, 0, None, None) == INVALID
+    assert L.sqattn_pack_v(FAKE, 1, 1, 0, 128, 0, FAKE, None) == INVALID
+
+
+def test_workspace_sizes():
+    L = sq.lib()
+    B, H, N, d = 1, 40, 32760, 128
+    nt = -(-N // 64)
+    wb = L.sqattn_workspace_bytes(B, H, N, d, 0, None)
+    assert wb >= 2 * B * H * N * d + B * H * nt * d * 64 * 2
+    w8 = L.sqattn_workspace_bytes(B, H, N, d, 1, None)
+    assert w8 < wb and w8 >= 2 * B * H * N * d + B * H * nt * d * 64
+    assert L.sqattn_workspace_bytes(B, H, N, 96, 0, None) == 0
+    assert L.sqattn_workspace_bytes(B, H, N, d, 5, None) == 0
+    assert L.sqattn_packed_v_bytes(B, H, N, d, 0) == B * H * nt * d * 64 * 2
+    assert L.sqattn_packed_v_bytes(B, H, N, d, 1) == B * H * nt * d * 64
+    assert L.sqattn_quantize_qk_workspace_bytes(B, H, N, d) > 0
+    assert L.sqattn_quantize_qk_workspace_bytes(0, H, N, d) == 0
+    # the size queries do not disturb the last error message
+    _fwd(d=96)
+    msg = _err()
+    L.sqattn_workspace_bytes(0, 0, 0, 0, 0, None)
+    assert _err() == msg
+
+
+def test_binding_rejects_non_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sq.forward(q, q, q)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        sq.quantize_qk([1.0], q)

@@ -1,0 +1,118 @@
+"""CPU tests of the HIP path's exact-arithmetic helpers, built for the host.
+
+``csrc/exact.h`` (the 192-bit K-mean accumulator and its correctly rounded
+division) and ``csrc/e4m3.h`` (the E4M3 encoder of the V quantizer) compile
+for host and device.  Here they are built with g++ into a small driver and
+compared bit for bit with the oracle on adversarial inputs.  The oracle and
+these helpers share no code."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import fp, quant
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
+
+DRIVER = r"""
+#include <cstdio>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#include "exact.h"
+#include "e4m3.h"
+using namespace sqattn;
+int main(int argc, char** argv) {
+  char mode[16];
+  if (scanf("%15s", mode) != 1) return 2;
+  if (!strcmp(mode, "mean")) {
+    int cols; if (scanf("%d", &cols) != 1) return 2;
+    for (int c = 0; c < cols; ++c) {
+      int n; if (scanf("%d", &n) != 1) return 2;
+      Acc192 acc; acc192_zero(acc); int64_t win = 0; bool bad = false;
+      for (int i = 0; i < n; ++i) { unsigned b; if (scanf("%u", &b) != 1) return 2;
+        bad |= kmean_accumulate(acc, win, b);
+        if ((i & 1023) == 1023) kmean_flush_window(acc, win); }
+      kmean_flush_window(acc, win);
+      float m = acc192_mean_f32(acc, (uint32_t)n);
+      uint32_t u; memcpy(&u, &m, 4);
+      printf("%d %u\n", bad ? 1 : 0, u);
+    }
+  } else {
+    int n; if (scanf("%d", &n) != 1) return 2;
+    for (int i = 0; i < n; ++i) { unsigned u; if (scanf("%u", &u) != 1) return 2;
+      float y; memcpy(&y, &u, 4); printf("%u\n", e4m3_encode_f32(y)); }
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    d = tmp_path_factory.mktemp("exact")
+    src = d / "drv.cpp"
+    src.write_text(DRIVER)
+    exe = d / "drv"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    return str(exe)
+
+
+def _run(exe, text):
+    r = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
+    return r.stdout.split()
+
+
+def _columns():
+    rng = np.random.default_rng(17)
+    cols = []
+    # workload-like columns: N(0,1) + offset, tails, many sizes
+    for n in (1, 2, 3, 64, 129, 1000, 32760):
+        cols.append(W.f32_to_bf16_bits((rng.standard_normal(n) + rng.normal(0, 1.4)).astype(np.float32)))
+    # wide exponent spread, subnormal bf16 values, exact cancellation, zeros
+    x = rng.standard_normal(5000) * np.exp2(rng.uniform(-140, 30, 5000))
+    cols.append(W.f32_to_bf16_bits(x.astype(np.float32)))
+    cols.append(W.f32_to_bf16_bits(np.float32([2.0 ** 30, 1.0, -(2.0 ** 30), 2.0 ** -130])))
+    cols.append(np.zeros(77, np.uint16))
+    cols.append(np.uint16([0x0001, 0x8001, 0x0001]))          # bf16 subnormals only
+    half = W.f32_to_bf16_bits(rng.standard_normal(300).astype(np.float32))
+    cols.append(np.concatenate([half, half ^ np.uint16(0x8000)]))
+    cols.append(W.f32_to_bf16_bits(np.full(999, 3.0e-5, np.float32)))
+    return cols
+
+
+def test_kmean_host_build_matches_oracle(driver):
+    cols = _columns()
+    text = "mean %d\n" % len(cols) + "".join(
+        "%d %s\n" % (c.size, " ".join(str(int(v)) for v in c)) for c in cols)
+    out = _run(driver, text)
+    for i, c in enumerate(cols):
+        bad, bits = int(out[2 * i]), int(out[2 * i + 1])
+        assert bad == 0
+        ref = quant.kmean_exact(c.reshape(-1, 1))[0]
+        assert bits == int(np.float32(ref).view(np.uint32)), (i, bits, ref)
+
+
+def test_kmean_host_build_flags_out_of_range(driver):
+    cols = [W.f32_to_bf16_bits(np.float32([1.0, 2.0 ** 33])), W.f32_to_bf16_bits(np.float32([2.0 ** 32, -1.0])),
+            np.uint16([0x7F80, 0x3F80])]
+    text = "mean 3\n" + "".join("%d %s\n" % (c.size, " ".join(str(int(v)) for v in c)) for c in cols)
+    out = _run(driver, text)
+    assert [int(out[0]), int(out[2]), int(out[4])] == [1, 0, 1]
+
+
+def test_e4m3_host_build_matches_oracle(driver):
+    rng = np.random.default_rng(23)
+    y = (rng.standard_normal(200_000) * np.exp2(rng.uniform(-16, 9.5, 200_000))).astype(np.float32)
+    pos = fp.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    extra = np.float32([0.0, -0.0, 448.0, 463.99, 464.0, 500.0, 1e30, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11,
+                        1e-40, -1e-40])
+    y = np.concatenate([y, mids, -mids, pos.astype(np.float32), extra])
+    text = "e4m3 %d\n%s\n" % (y.size, " ".join(str(int(u)) for u in y.view(np.uint32)))
+    got = np.array([int(s) for s in _run(driver, text)], np.uint8)
+    assert np.array_equal(got, fp.e4m3_encode(y))
