@@ -320,18 +320,15 @@ void launch_attention(const AttnParams& p, int d, int pv, hipStream_t st) {
   q.qtiles = (p.N + ATT_QWG - 1) / ATT_QWG;
   const long long W = (long long)p.BH * q.qtiles;
   q.per_xcd = (int)((W + 7) / 8);
-  const dim3 grid(8 * q.per_xcd), block(256);
-  if (d == 128) {
-    if (pv == 0)
-      hipLaunchKernelGGL((attn_kernel<128, 0>), grid, block, 0, st, q);
-    else
-      hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, st, q);
-  } else {
-    if (pv == 0)
-      hipLaunchKernelGGL((attn_kernel<64, 0>), grid, block, 0, st, q);
-    else
-      hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, st, q);
+  if (pv == 0) {
+    launch_attention_bf16(q, d, st);
+    return;
   }
+  const dim3 grid(8 * q.per_xcd), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, st, q);
+  else
+    hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, st, q);
 }
 
 }  // namespace sqattn

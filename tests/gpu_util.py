@@ -35,8 +35,10 @@ def oracle_heads(q, k, v, rows, q_block, scale, pv, heads=None, workers=None):
 
     res = [None] * (B * H)
     with ThreadPoolExecutor(workers) as ex:
-        for i, r in zip(idx, ex.map(one, idx)):
+        for n, (i, r) in enumerate(zip(idx, ex.map(one, idx))):
             res[i] = r
+            if len(idx) >= 8 and (n + 1) % 4 == 0:
+                print(f"  oracle: {n + 1}/{len(idx)} heads", flush=True)
     return res
 
 
