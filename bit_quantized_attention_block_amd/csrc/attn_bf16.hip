@@ -1,31 +1,42 @@
-// Quantized attention kernel, 16-bit P.V path, software-pipelined (gfx950).
+// Quantized attention kernel, 16-bit P.V path (gfx950).
 //
 // Same mathematics and register layouts as the FP8 kernel in attn.hip (INT8
 // S^T = K Q^T, lane-local online softmax, O^T = V^T P^T); see that file for
-// the layout derivation.  What differs is the schedule.  The unit of the
-// pipeline is a half-tile h of 32 keys (half kb = h%2 of 64-key tile h/2):
+// the layout derivation.  What differs is the schedule.
 //
-//   iteration h:   MFMA  S(h+1) = K(h+1) Q^T           (8 x i8 32x32x32)
-//                  MFMA  O     += V(h-1)^T P(h-1)^T    (16 x bf16 32x32x16)
+// Work-group: 8 waves (two per SIMD), 32 query rows each, 256 rows per
+// work-group.  The unit of the pipeline is a half-tile h of 32 keys (half
+// kb = h%2 of 64-key tile h/2):
+//
+//   iteration h:   MFMA  S(h+1) = K(h+1) Q^T           (D/32 x i8 32x32x32)
+//                  MFMA  O     += V(h-1)^T P(h-1)^T    (D/16 x bf16 32x32x16)
 //                  VALU  P(h)   = softmax step on S(h)
-//   with the two MFMA streams interleaved with the VALU stream, so the matrix
-//   cores and the vector ALUs work at the same time inside one wave.  Each K
-//   and V operand read from LDS feeds both 32-query blocks of the wave.  S and
-//   P are double-buffered in registers; the two halves of a tile use them in
-//   swapped roles, so no copies are needed.  Tiles move global -> LDS with
-//   direct-to-LDS loads issued one tile ahead; one barrier per tile.
 //
-//   * No rescaling inside the loop: each row's reference max is the max of
-//     its first 32 keys, and P = 2^(x - ref) may grow up to 2^HEADROOM (exact
-//     in bf16/fp32; O stays finite while |V| * N < 2^(127 - HEADROOM)).  The
-//     true running max is tracked; if any row of the work-group exceeds its
-//     reference by more than HEADROOM, the work-group recomputes once with the
-//     true max as reference (then P <= 1).  So the loop body has no branch.
+// The MFMAs and the softmax of an iteration are independent; they are
+// interleaved at the finest grain: each MFMA is followed by one softmax pair
+// (two scores) in the same inline-assembly statement, and each MFMA operand is
+// read from LDS four MFMAs ahead.  The second wave on the SIMD fills what is
+// left of the gaps.
+//
+//   * LDS: a 4-slot ring of K tiles (with the tile's K scale) and of V tiles,
+//     refilled with direct-to-LDS loads three tiles ahead; one barrier per
+//     tile, waiting only for the loads issued three tiles earlier.  Rows are
+//     padded to a stride of 144 bytes (80 for 64-byte K rows): with an odd
+//     number of 16-byte units per row, the 16 rows read by 16 consecutive
+//     lanes fall in distinct banks, and every operand address is one base
+//     register plus an immediate offset.
+//   * No rescaling inside the loop: each row's reference is the max of its
+//     first 32 keys, and P = 2^(x - ref) is exact in bf16/fp32 far above 1.
+//     The row sum bounds every P of the row; if some row's sum reaches
+//     2^HEADROOM, the work-group takes the exact row max over all keys in a
+//     second sweep and recomputes with it as reference (then P <= 1).  So the
+//     loop body has no branch on data.
 //   * The row sum is taken on the bf16-rounded P with v_dot2c_f32_bf16, so the
 //     normalisation uses exactly the weights the matrix core multiplied.
-//   * Only the last, possibly ragged tile carries key masking.  Rows past N in
-//     the K tile load row N-1 (in-bounds); their logits are masked.  The packed
-//     V tiles are zero past N.
+//   * Only the last, possibly ragged tile needs key masking.  Rows past N in
+//     the K tile load row N-1 (in bounds, a real score); their P entries are
+//     zeroed and taken out of the row sum afterwards.  The packed V tiles are
+//     zero past N.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,18 +45,17 @@ namespace sqattn {
 namespace {
 
 __device__ __forceinline__ int perm_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (D == 128)
-    return ((row >> 1) ^ ((row & 1) << 1)) & 7;
-  else
-    return ((row >> 1) & 1) | ((row >> 2) & 2);
-}
-__device__ __forceinline__ int swz_v16(int c) { return (c ^ (c >> 3)) & 7; }
 
-constexpr float HEADROOM = 32.0f;  // log2 units
+constexpr float HEADROOM = 64.0f;  // log2 units
+constexpr int WAVES = 8;
+constexpr int NTHR = 64 * WAVES;
+constexpr int NSLOT = 4;           // LDS ring depth (tiles)
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 field layout:
+// vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // max and sum over lanes l and l^32 (v_permlane32_swap pairs them)
 __device__ __forceinline__ int pair_max_i(int v) {
@@ -57,168 +67,275 @@ __device__ __forceinline__ float pair_sum_f(float v) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-template <int D, int QBW>
+template <int D>
+struct Geo {
+  static constexpr int NCH = D / 32;            // QK k-steps per half-tile
+  static constexpr int NCB = D / 32;            // 32-channel blocks of O^T
+  static constexpr int KCPR = D / 16;           // 16-byte chunks of a K row
+  static constexpr int KROWC = KCPR + 1;        // ... padded (odd)
+  static constexpr int KROW = 16 * KROWC;       // padded K row stride (bytes)
+  static constexpr int KSC = KT * KROW;         // offset of the K scale in a K slot
+  static constexpr int KS = KSC + 256;          // K slot bytes (64 copies of the scale)
+  static constexpr int VROWC = 9;               // V^T row: 64 keys * 2 B = 8 chunks + pad
+  static constexpr int VROW = 16 * VROWC;
+  static constexpr int VS = D * VROW;           // V slot bytes
+  static constexpr int VBASE = NSLOT * KS;      // V ring offset in LDS
+  static constexpr int LDS_BYTES = NSLOT * (KS + VS);
+  static constexpr int KINST = (KT * KROWC + 63) / 64;   // 1 KB direct loads per K tile
+  static constexpr int VINST = (D * VROWC + 63) / 64;
+  static constexpr int KPW = (KINST + WAVES - 1) / WAVES; // per wave (every wave the same)
+  static constexpr int VPW = (VINST + WAVES - 1) / WAVES;
+  static constexpr int LPB = KPW + 1 + VPW;     // direct loads per wave per K+V tile pair
+  static constexpr int VBYTES = D * KT * 2;     // packed V tile in HBM
+};
+
+// ---------------------------------------------------------------------------
+// One MFMA followed by one softmax pair, as one inline-assembly statement.
+//
+// The pair: two scores s0, s1 of S(h) (int32) become P = 2^(s c - m),
+// rounded to a packed bf16 pair w.  Only assembly statements read the MFMA
+// results (S, O), so no compiler-generated instruction can touch a register
+// an MFMA is still writing; the compiler keeps volatile statements in order
+// and does not move memory accesses across them ("memory"), so the operand
+// reads written between them stay where they are written, with the
+// compiler's own waits.  A score of S(h) is read at least one iteration after
+// the MFMA that produced it.
+// ---------------------------------------------------------------------------
+#define SQ_PAIR                                                              \
+  "\n v_cvt_f32_i32 %[t0], %[s0]"                                            \
+  "\n v_cvt_f32_i32 %[t1], %[s1]"                                            \
+  "\n v_fma_f32 %[t0], %[t0], %[c], -%[m]"                                    \
+  "\n v_fma_f32 %[t1], %[t1], %[c], -%[m]"                                    \
+  "\n v_exp_f32 %[t0], %[t0]"                                                \
+  "\n v_exp_f32 %[t1], %[t1]"                                                \
+  "\n s_nop 0"                                                               \
+  "\n v_cvt_pk_bf16_f32 %[w], %[t0], %[t1]"
+#define SQ_PAIR_OPS(w) [w] "=&v"(w), [t0] "=&v"(t0), [t1] "=&v"(t1)
+#define SQ_PAIR_INS [s0] "v"(s0), [s1] "v"(s1), [c] "v"(c), [m] "v"(m)
+
+__device__ __forceinline__ void qk0_pair(v16i& sn, v4i a, v4i q, int s0, int s1, float c, float m, uint32_t& w) {
+  float t0, t1;
+  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], 0" SQ_PAIR
+               : [sn] "=&v"(sn), SQ_PAIR_OPS(w) : [a] "v"(a), [q] "v"(q), SQ_PAIR_INS : "memory");
+}
+__device__ __forceinline__ void qk_pair(v16i& sn, v4i a, v4i q, int s0, int s1, float c, float m, uint32_t& w) {
+  float t0, t1;
+  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], %[sn]" SQ_PAIR
+               : [sn] "+v"(sn), SQ_PAIR_OPS(w) : [a] "v"(a), [q] "v"(q), SQ_PAIR_INS : "memory");
+}
+__device__ __forceinline__ void pv_pair(v16f& o, v4i a, v4i p, int s0, int s1, float c, float m, uint32_t& w) {
+  float t0, t1;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" SQ_PAIR
+               : [o] "+v"(o), SQ_PAIR_OPS(w) : [a] "v"(a), [p] "v"(p), SQ_PAIR_INS : "memory");
+}
+__device__ __forceinline__ void pv_only(v16f& o, v4i a, v4i p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" : [o] "+v"(o) : [a] "v"(a), [p] "v"(p) : "memory");
+}
+__device__ __forceinline__ void pair_only(int s0, int s1, float c, float m, uint32_t& w) {
+  float t0, t1;
+  asm volatile(SQ_PAIR : SQ_PAIR_OPS(w) : SQ_PAIR_INS : "memory");
+}
+#undef SQ_PAIR_INS
+#undef SQ_PAIR_OPS
+#undef SQ_PAIR
+
+template <int D>
 struct Ctx {
-  static constexpr int WAVES = 8 / QBW;   // 256 query rows per work-group
-  static constexpr int NCH = D / 32;
-  static constexpr int NCB = D / 32;
-  static constexpr int KBYTES = KT * D;
-  static constexpr int VBYTES = D * KT * 2;
-  uint8_t* lk;     // LDS K tiles [2][KBYTES]
-  uint8_t* lv;     // LDS V tiles [2][VBYTES]
+  using G = Geo<D>;
+  uint8_t* lds;
   const uint8_t* kh;
   const uint8_t* vth;
   const float* skh;
-  int N, nt, tid, lane, wave, g, lr, krow0;
-  float cq[QBW];
-  v4i qreg[QBW][NCH];
-  v16f o[QBW][NCB];
-  float m[QBW], l[QBW], mrun[QBW];  // reference max, row sum, running max
+  int N, nt, lane, wave, g, lr;
+  uint32_t kbase, vbase;  // per-lane LDS operand offsets (slot 0, half 0)
+  float cq;               // sQ(row) * scale * log2(e)
+  v4i qreg[G::NCH];       // Q operands
+  v16f o[G::NCB];         // O^T accumulators
+  float m, l;             // reference max (log2 units), row sum
 
-  // ---- global -> LDS (direct), tile t of K into buffer b
-  __device__ __forceinline__ void load_k(int t, int b) {
-    constexpr int CPR = D / 16;  // 16-byte chunks per K row
-    constexpr int NINST = KBYTES / 16 / 64;  // 1 KB direct loads per tile
-    for (int u = wave; u < NINST; u += WAVES) {
-      const int j0 = u * 64;
-      const int j = j0 + lane;
-      const int row = j / CPR, pc = j % CPR;
+  // ---- global -> LDS (direct).  Every wave issues KPW+1 (VPW) instructions;
+  // instruction slots past the tile wrap around and repeat a chunk range,
+  // writing the same bytes again, so all waves count the same loads.  The
+  // extra K instruction copies the tile's K scale into the slot (each lane
+  // one copy).
+  __device__ __forceinline__ void load_k(int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < G::KPW; ++i) {
+      int u = wave + WAVES * i;
+      if (u >= G::KINST) u -= G::KINST;
+      const int q = u * 64 + lane;  // padded chunk index
+      const int row = min(q / G::KROWC, KT - 1), col = min(q % G::KROWC, G::KCPR - 1);
       const int key = min(t * KT + row, N - 1);
-      const uint8_t* src = kh + (long long)key * D + ((pc ^ swz_k<D>(row)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lk + b * KBYTES + j0 * 16), 16, 0, 0);
+      const uint8_t* src = kh + (long long)key * D + col * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + slot * G::KS + u * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(skh + t, (lds_void*)(lds + slot * G::KS + G::KSC), 4, 0, 0);
+  }
+  __device__ __forceinline__ void load_v(int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < G::VPW; ++i) {
+      int u = wave + WAVES * i;
+      if (u >= G::VINST) u -= G::VINST;
+      const int q = u * 64 + lane;
+      const int c = min(q / G::VROWC, D - 1), col = min(q % G::VROWC, 7);
+      const uint8_t* src = vth + (long long)t * G::VBYTES + c * 128 + col * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + G::VBASE + slot * G::VS + u * 1024), 16, 0, 0);
     }
   }
-  __device__ __forceinline__ void load_v(int t, int b) {
-    constexpr int NINST = VBYTES / 16 / 64;
-    for (int u = wave; u < NINST; u += WAVES) {
-      const int j0 = u * 64;
-      const int j = j0 + lane;
-      const int c = j >> 3, pc = j & 7;
-      const uint8_t* src = vth + (long long)t * VBYTES + c * 128 + ((pc ^ swz_v16(c)) << 4);
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lv + b * VBYTES + j0 * 16), 16, 0, 0);
-    }
-  }
-
-  // ---- S(h) = K half-tile Q^T for both query blocks (K tile in buffer b, half kb)
-  __device__ __forceinline__ void qk(v16i (&s)[QBW], int b, int kb) {
-    const int row = kb * 32 + krow0;
-    const uint8_t* base = lk + b * KBYTES + row * D;
-    const int sw = swz_k<D>(row);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const v4i a = *(const v4i*)(base + (((ch * 2 + g) ^ sw) << 4));
-#pragma unroll
-      for (int qb = 0; qb < QBW; ++qb) {
-        if (ch == 0) {
-          v16i z;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = 0;
-          s[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[qb][ch], z, 0, 0, 0);
-        } else {
-          s[qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[qb][ch], s[qb], 0, 0, 0);
-        }
-      }
-    }
+  __device__ __forceinline__ float k_scale(int slot) const {
+    return *(const float*)(lds + slot * G::KS + G::KSC + 4 * lane);
   }
 
-  // ---- O^T += V^T P^T over one half-tile (V tile in buffer b, half kb)
-  __device__ __forceinline__ void pv(const v4i (&pb)[QBW][2], int b, int kb) {
+  // max over the 32 keys of S (lanes l and l^32 share a query), in log2 units
+  __device__ __forceinline__ float rowmax(const v16i& s, float c) const {
+    int d = max(max(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int ks = 2 * kb + k2;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int c = cb * 32 + lr;
-        const v8bf a = *(const v8bf*)(lv + b * VBYTES + c * 128 + (((2 * ks + g) ^ swz_v16(c)) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb)
-          o[qb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, pb[qb][k2]), o[qb][cb], 0,
-                                                              0, 0);
-      }
-    }
+    for (int i = 3; i < 15; i += 2) d = max(max(d, s[i]), s[i + 1]);
+    d = max(d, s[15]);
+    return (float)pair_max_i(d) * c;  // c >= 0
   }
 
-  // ---- softmax step on S(h) (half kb of tile t): P(h) = 2^(x - ref) as
-  // packed bf16, row-sum and running-max update.  The first half-tile sets
-  // the reference.  Keys past N (last tile only) duplicate key N-1, so they
-  // never raise the max; fix_tail() removes them afterwards.
-  __device__ __forceinline__ void softmax(const v16i (&s)[QBW], v4i (&pb)[QBW][2], int t) {
-    const float skt = skh[t];
+  // ---- operand i of an iteration (see the MFMA order below); ka/va: lane
+  // offsets of the K half / V^T half
+  __device__ __forceinline__ v4i operand(int i, uint32_t ka, uint32_t va) const {
+    if (i < 2 * G::NCH && (i & 1) == 0) return *(const v4i*)(lds + ka + (i >> 1) * 32);
+    const int k2 = (i < 2 * G::NCH) ? 0 : 1;
+    const int cb = (i < 2 * G::NCH) ? (i >> 1) : (i - 2 * G::NCH);
+    return *(const v4i*)(lds + va + cb * 32 * G::VROW + k2 * 32);
+  }
+
+  // ---- one half-tile iteration h = 2t + KB.  K(h+1) is half KB^1 of tile
+  // t + KB; V(h-1) is half KB^1 of tile t - 1 + KB (for h = 0 the zeroed slot
+  // with P(-1) = 0).  c: the softmax factor of tile t.
+  //
+  // MFMA order: i < 2 NCH alternates the INT8 chain (k-step i/2) with the
+  // first P.V k-step (channel block i/2); then the second P.V k-step.  Each
+  // operand is read RD_AHEAD MFMAs ahead; softmax pair j (two scores of S(h),
+  // one packed bf16 pair of P(h)) sits between MFMA j and MFMA j+1.
+  static constexpr int NMF = G::NCH + 2 * G::NCB;
+  static constexpr int RD_AHEAD = 4;
+  template <int KB>
+  __device__ __forceinline__ void step(const v16i& scur, v16i& snext, const v4i (&pprev)[2], v4i (&pcur)[2],
+                                       int t, float c) {
+    const uint32_t ka = kbase + ((t + KB) & (NSLOT - 1)) * G::KS + (KB ^ 1) * 32 * G::KROW;
+    const uint32_t va = vbase + ((t - 1 + KB) & (NSLOT - 1)) * G::VS + (KB ^ 1) * 64;
+    v4i a[NMF];
+    uint32_t w[8];
+    float lsum = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      const float c = cq[qb] * skt;
-      int d0 = s[qb][0];
+    for (int i = 0; i < RD_AHEAD; ++i) a[i] = operand(i, ka, va);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) d0 = max(d0, s[qb][i]);
-      const float tmax = (float)pair_max_i(d0) * c;
-      mrun[qb] = __builtin_fmaxf(mrun[qb], tmax);
-      const float mref = (m[qb] == -__builtin_inff()) ? tmax : m[qb];
-      m[qb] = mref;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 8 * k2 + 2 * j;
-          v2bf pk;
-          pk[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf((float)s[qb][i], c, -mref));
-          pk[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf((float)s[qb][i + 1], c, -mref));
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, v2bf{(__bf16)1.0f, (__bf16)1.0f}, lsum, false);
-          w4[j] = __builtin_bit_cast(uint32_t, pk);
-        }
-        pb[qb][k2] = v4i{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+    for (int i = 0; i < (NMF > 8 ? NMF : 8); ++i) {
+      if (i >= NMF) {  // no MFMA left (D = 64): softmax pair only
+        pair_only(scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+      } else if (i >= 8) {  // no softmax pair left
+        pv_only(o[i - 2 * G::NCH], a[i], pprev[1]);
+      } else if (i < 2 * G::NCH && (i & 1) == 0) {
+        if (i == 0)
+          qk0_pair(snext, a[i], qreg[0], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+        else
+          qk_pair(snext, a[i], qreg[i >> 1], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+      } else {
+        const int k2 = (i < 2 * G::NCH) ? 0 : 1;
+        const int cb = (i < 2 * G::NCH) ? (i >> 1) : (i - 2 * G::NCH);
+        pv_pair(o[cb], a[i], pprev[k2], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
       }
-      l[qb] += lsum;
+      if (i + RD_AHEAD < NMF) a[i + RD_AHEAD] = operand(i + RD_AHEAD, ka, va);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[j]), v2bf{(__bf16)1.0f, (__bf16)1.0f}, lsum,
+                                             false);
+    pcur[0] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    pcur[1] = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    l += lsum;
+  }
+
+  // ---- all tiles of one pass (the loop body is generated once per order)
+  __device__ __forceinline__ void tiles(v16i& S0, v16i& S1, v4i (&P0)[2], v4i (&P1)[2], float c) {
+    for (int t = 0; t < nt - 1; ++t) {
+      step<0>(S0, S1, P1, P0, t, c);
+      // Tile boundary: every wave is done with K(t) and V(t-1); K(t+1) and
+      // V(t) (issued three boundaries ago, or in the prologue) must have
+      // landed, the two latest batches may stay in flight.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB));
+      __syncthreads();
+      const float c_next = cq * k_scale((t + 1) & (NSLOT - 1));
+      // refill the freed slots (past the end: the last tile again, unread)
+      load_k(min(t + NSLOT, nt - 1), t & (NSLOT - 1));
+      load_v(min(t + NSLOT - 1, nt - 1), (t - 1) & (NSLOT - 1));
+      step<1>(S1, S0, P0, P1, t, c);
+      c = c_next;
+    }
+    // last tile: keys past N masked
+    const int t = nt - 1;
+    step<0>(S0, S1, P1, P0, t, c);
+    fix_tail(P0, t, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    step<1>(S1, S0, P0, P1, t, c);
+    fix_tail(P1, t, 1);
+    pv_last(P1, t & (NSLOT - 1));
   }
 
   // ---- last tile, half kb: zero P of keys >= N and take them out of the row sum
-  __device__ __forceinline__ void fix_tail(v4i (&pb)[QBW][2], int t, int kb) {
+  __device__ __forceinline__ void fix_tail(v4i (&pb)[2], int t, int kb) {
     const int kvalid = N - t * KT - kb * 32;
+    float drop = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      float drop = 0.0f;
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = 16 * k2 + 8 * g + 2 * j;
+        const uint32_t w = (uint32_t)pb[k2][j];
+        const uint32_t keep = (k0 >= kvalid ? 0u : 0xFFFFu) | (k0 + 1 >= kvalid ? 0u : 0xFFFF0000u);
+        drop = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w & ~keep), v2bf{(__bf16)1.0f, (__bf16)1.0f},
+                                               drop, false);
+        pb[k2][j] = (int)(w & keep);
+      }
+    l -= drop;
+  }
+
+  // S = half kb of the K tile in slot
+  __device__ __forceinline__ void qk_half(v16i& s, int slot, int kb) const {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int k0 = 16 * k2 + 8 * g + 2 * j;
-          uint32_t w = (uint32_t)pb[qb][k2][j];
-          const uint32_t keep = (k0 >= kvalid ? 0u : 0xFFFFu) | (k0 + 1 >= kvalid ? 0u : 0xFFFF0000u);
-          const uint32_t gone = w & ~keep;
-          drop = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, gone), v2bf{(__bf16)1.0f, (__bf16)1.0f},
-                                                 drop, false);
-          pb[qb][k2][j] = (int)(w & keep);
-        }
-      l[qb] -= drop;
+    for (int ch = 0; ch < G::NCH; ++ch) {
+      const v4i a = *(const v4i*)(lds + kbase + slot * G::KS + kb * 32 * G::KROW + ch * 32);
+      if (ch == 0) {
+        v16i z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0;
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], z, 0, 0, 0);
+      } else {
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], s, 0, 0, 0);
+      }
     }
   }
-
+  __device__ __forceinline__ void pv_last(const v4i (&pb)[2], int slot) {  // half 1 of V tile in slot
+    const uint32_t va = vbase + slot * G::VS + 64;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int cb = 0; cb < G::NCB; ++cb) {
+        const v4i a = *(const v4i*)(lds + va + cb * 32 * G::VROW + k2 * 32);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                        __builtin_bit_cast(v8bf, pb[k2]), o[cb], 0, 0, 0);
+      }
+  }
 };
 
-// Interleave hint for one pipelined iteration: MFMA, VALU and LDS reads.
-// LDS reads run AHEAD reads ahead of the MFMAs that consume them.
-template <int NMFMA, int VALU_PER_MFMA, int NREAD, int AHEAD>
-__device__ __forceinline__ void interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);              // first LDS reads
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);    // VALU
-    if (i * NREAD / NMFMA + AHEAD < NREAD && (i + 1) * NREAD / NMFMA != i * NREAD / NMFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // next LDS read
-  }
+// uniform load through the scalar cache (the K scales are read-only here)
+__device__ __forceinline__ float ld_uniform(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
 }
 
 }  // namespace
 
-template <int D, int QBW>
-__global__ __launch_bounds__(64 * (8 / QBW)) void attn_bf16_kernel(AttnParams p) {
-  using Cx = Ctx<D, QBW>;
-  constexpr int NTHR = 64 * Cx::WAVES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2 * KT * D];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * D * KT * 2];
+template <int D>
+__global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
+  using Cx = Ctx<D>;
+  using G = Geo<D>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int w = blockIdx.x;
   const int item = (w & 7) * p.per_xcd + (w >> 3);
@@ -226,131 +343,115 @@ __global__ __launch_bounds__(64 * (8 / QBW)) void attn_bf16_kernel(AttnParams p)
   const int bh = item / p.qtiles, qt = item - bh * p.qtiles;
 
   Cx C;
-  C.lk = lds_k;
-  C.lv = lds_v;
-  C.tid = threadIdx.x;
-  C.lane = C.tid & 63;
-  C.wave = C.tid >> 6;
+  C.lds = smem;
+  const int tid = threadIdx.x;
+  C.lane = tid & 63;
+  C.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   C.g = C.lane >> 5;
   C.lr = C.lane & 31;
-  C.krow0 = perm_key(C.lr);
+  C.kbase = perm_key(C.lr) * G::KROW + C.g * 16;
+  C.vbase = G::VBASE + C.lr * G::VROW + C.g * 16;
   C.N = p.N;
   C.nt = p.nt;
   const long long hoff = (long long)bh * p.N * D;
   C.kh = (const uint8_t*)p.k + hoff;
-  C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * Cx::VBYTES;
+  C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
-  const int qbase = qt * ATT_QWG + C.wave * 32 * QBW;
+  const int row = qt * ATT_QWG + C.wave * 32 + C.lr;
+  const bool rok = row < p.N;
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const int row = qbase + qb * 32 + C.lr;
-    const bool ok = row < p.N;
-#pragma unroll
-    for (int ch = 0; ch < Cx::NCH; ++ch)
-      C.qreg[qb][ch] = ok ? *(const v4i*)(p.q + hoff + (long long)row * D + ch * 32 + C.g * 16) : v4i{0, 0, 0, 0};
-    C.cq[qb] = ok ? p.sq[(long long)bh * p.nq + row / p.q_block] * p.scale_log2e : 0.0f;
-    C.m[qb] = -__builtin_inff();
-    C.mrun[qb] = -__builtin_inff();
-  }
+  for (int ch = 0; ch < G::NCH; ++ch)
+    C.qreg[ch] = rok ? *(const v4i*)(p.q + hoff + (long long)row * D + ch * 32 + C.g * 16) : v4i{0, 0, 0, 0};
+  C.cq = rok ? p.sq[(long long)bh * p.nq + row / p.q_block] * p.scale_log2e : 0.0f;
 
   const int nt = p.nt;
-  const bool ragged = (p.N & (KT - 1)) != 0;
-  v16i S0[QBW], S1[QBW];
-  v4i P0[QBW][2], P1[QBW][2];
+  constexpr int LPB = G::LPB;
+  v16i S0, S1;
+  v4i P0[2], P1[2];
 
   for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      C.l[qb] = 0.0f;
-#pragma unroll
-      for (int cb = 0; cb < Cx::NCB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) C.o[qb][cb][i] = 0.0f;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) P1[qb][k2] = v4i{0, 0, 0, 0};
-    }
-
-    // prologue: K(0), K(1), V(0) -> LDS, V buffer 1 zeroed (the first
-    // iteration multiplies it by P = 0); S(0) from the first half of K(0)
-    C.load_k(0, 0);
-    C.load_k(nt > 1 ? 1 : 0, 1);
-    C.load_v(0, 0);
-    for (int i = C.tid; i < Cx::VBYTES / 16; i += NTHR)
-      *(v4i*)(lds_v + Cx::VBYTES + i * 16) = v4i{0, 0, 0, 0};
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    C.qk(S0, 0, 0);
-
-    // Half-tile iteration h = 2t + KB: S(h) in SCUR, P(h) into PCUR, S(h+1)
-    // into SNEXT, P(h-1) from PPREV.  K(h+1) is half KB^1 of tile t + KB (in
-    // the last iteration a stale tile whose S is never used); V(h-1) is half
-    // KB^1 of tile t - 1 + KB (for h = 0 the zeroed buffer, with P(-1) = 0).
-#define SQ_HALF(KB, SCUR, SNEXT, PPREV, PCUR) \
-  do {                                        \
-    C.qk(SNEXT, (t + KB) & 1, KB ^ 1);        \
-    C.pv(PPREV, (t - 1 + KB) & 1, KB ^ 1);    \
-    C.softmax(SCUR, PCUR, t);                 \
-    interleave<12 * QBW, 14 / QBW, 12, 3>();  \
-  } while (0)
-
-    for (int t = 0; t < nt; ++t) {
-      SQ_HALF(0, S0, S1, P1, P0);
-      if (ragged && t == nt - 1) C.fix_tail(P0, t, 0);
-      // loads of K(t+1), V(t) issued one tile ago have landed and every wave
-      // is done with K(t) and V(t-1): refill those buffers with K(t+2), V(t+1)
-      __builtin_amdgcn_s_waitcnt(0);
+    if (pass == 1) {
+      // Rare path: some row's sum reached 2^HEADROOM.  Take the exact row max
+      // over all keys (K tiles one at a time through slot 0) as the reference,
+      // so that every P <= 1.
+      float mx = -__builtin_inff();
+      for (int t = 0; t < nt; ++t) {
+        __syncthreads();
+        C.load_k(t, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const float c = C.cq * ld_uniform(C.skh + t);
+        C.qk_half(S0, 0, 0);
+        C.qk_half(S1, 0, 1);
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(C.rowmax(S0, c), C.rowmax(S1, c)));
+      }
+      C.m = mx;
       __syncthreads();
-      if (t + 2 < nt) C.load_k(t + 2, t & 1);
-      if (t + 1 < nt) C.load_v(t + 1, (t + 1) & 1);
-      SQ_HALF(1, S1, S0, P0, P1);
-      if (ragged && t == nt - 1) C.fix_tail(P1, t, 1);
     }
-#undef SQ_HALF
-    // the last half-tile's P.V (V(nt-1) half 1)
-    C.pv(P1, (nt - 1) & 1, 1);
-
-    // a row whose max outran its reference: redo with the true max
-    bool over = false;
+    C.l = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-      over |= C.mrun[qb] > C.m[qb] + HEADROOM;
-      C.m[qb] = C.mrun[qb];
+    for (int cb = 0; cb < G::NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) C.o[cb][i] = 0.0f;
+    P1[0] = P1[1] = v4i{0, 0, 0, 0};
+
+    // Prologue.  K(0) first, then three batches of LPB loads per wave:
+    // {K(1), V(0)}, {K(2), V(1)}, {K(3), V(2)}; every loop boundary adds one
+    // more batch, so "all but the last two batches landed" is vmcnt(2 LPB).
+    // V slot 3 is zeroed (the first iteration multiplies it by P(-1) = 0).
+    C.load_k(0, 0);
+#pragma unroll
+    for (int j = 1; j < NSLOT; ++j) {
+      C.load_k(min(j, nt - 1), j);
+      C.load_v(min(j - 1, nt - 1), j - 1);
     }
+    for (int i = tid; i < G::VS / 16; i += NTHR)
+      *(v4i*)(smem + G::VBASE + (NSLOT - 1) * G::VS + i * 16) = v4i{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPB));
+    __syncthreads();
+    float c = C.cq * C.k_scale(0);
+    C.qk_half(S0, 0, 0);
+    if (pass == 0) C.m = C.rowmax(S0, c);  // reference: max of the first 32 keys
+
+    C.tiles(S0, S1, P0, P1, c);
+    C.l = pair_sum_f(C.l);
     __syncthreads();  // all waves are done with the LDS tiles
-    if (!__syncthreads_or(over)) break;
+    // the sum bounds every P: l < 2^HEADROOM keeps P and O far from overflow
+    const bool over = !(C.l < __builtin_exp2f(HEADROOM));
+    if (pass == 1 || !__syncthreads_or(over)) break;
   }
 
   // epilogue: O = O^T / l, fp32 rows
+  const float inv = 1.0f / C.l;
+  if (rok) {
+    float* orow = p.out + hoff + (long long)row * D;
 #pragma unroll
-  for (int qb = 0; qb < QBW; ++qb) {
-    const float inv = 1.0f / pair_sum_f(C.l[qb]);
-    const int row = qbase + qb * 32 + C.lr;
-    if (row < p.N) {
-      float* orow = p.out + hoff + (long long)row * D;
+    for (int cb = 0; cb < G::NCB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < Cx::NCB; ++cb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          v4f v = {C.o[qb][cb][4 * i4] * inv, C.o[qb][cb][4 * i4 + 1] * inv, C.o[qb][cb][4 * i4 + 2] * inv,
-                   C.o[qb][cb][4 * i4 + 3] * inv};
-          *(v4f*)(orow + cb * 32 + i4 * 8 + C.g * 4) = v;
-        }
-    }
+      for (int i4 = 0; i4 < 4; ++i4) {
+        v4f v = {C.o[cb][4 * i4] * inv, C.o[cb][4 * i4 + 1] * inv, C.o[cb][4 * i4 + 2] * inv,
+                 C.o[cb][4 * i4 + 3] * inv};
+        *(v4f*)(orow + cb * 32 + i4 * 8 + C.g * 4) = v;
+      }
   }
 }
 
-// Query blocks per wave: 1 (8 waves, two per SIMD) or 2 (4 waves).
-#ifndef SQATTN_BF16_QBW
-#define SQATTN_BF16_QBW 1
-#endif
+template <int D>
+static void launch_d(const AttnParams& q, hipStream_t st) {
+  static bool configured = false;  // the attribute is per kernel, set once per process
+  if (!configured) {
+    (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Geo<D>::LDS_BYTES);
+    configured = true;
+  }
+  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(8 * q.per_xcd), dim3(NTHR), Geo<D>::LDS_BYTES, st, q);
+}
 
 void launch_attention_bf16(const AttnParams& q, int d, hipStream_t st) {
-  constexpr int QBW = SQATTN_BF16_QBW;
-  const dim3 grid(8 * q.per_xcd), block(64 * (8 / QBW));
   if (d == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, QBW>), grid, block, 0, st, q);
+    launch_d<128>(q, st);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<64, QBW>), grid, block, 0, st, q);
+    launch_d<64>(q, st);
 }
 
 }  // namespace sqattn

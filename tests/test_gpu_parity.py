@@ -113,12 +113,15 @@ def _degenerate(kind, N=333, d=128):
     elif kind == "one_hot":             # one key aligned with every query dominates
         q[:] = 1.0
         k[:, :, 100] = 6.0
+    elif kind == "far_max":             # that key's score exceeds the first keys' by far more
+        q[:] = 1.0                      # than the fp32 range: the exact-max recomputation
+        k[:, :, 100] = 20.0
     cvt = lambda x: W.f32_to_bf16_bits(x.astype(np.float32))
     rows = [np.arange(N)] * 2
     return cvt(q), cvt(k), cvt(v), rows
 
 
-@pytest.mark.parametrize("kind", ["zero_q", "constant_k", "constant_v", "zero_v_block", "one_hot"])
+@pytest.mark.parametrize("kind", ["zero_q", "constant_k", "constant_v", "zero_v_block", "one_hot", "far_max"])
 @pytest.mark.parametrize("pv", ["bf16", "fp8"])
 def test_degenerate_inputs(kind, pv):
     _run_case(W.get(1), pv=pv, q_block=128, data=_degenerate(kind))
