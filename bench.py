@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one full sqattn_forward over the workload: exact K mean, INT8
+quantization of Q and smoothed K, V packing (or E4M3 quantization), and the
+attention kernel, from bf16 Q/K/V resident in HBM to the fp32 output in HBM.
+The metric is TOPS = 4*B*H*N^2*d / time, also reported as a percentage of the
+MI355X dense INT8 matrix peak (5.0 POPS).
+
+Printed: one JSON line with the contract fields plus
+  roofline     - the attention kernel alone (its average launch duration from
+                 HIP events on the launch stream), against the INT8 MFMA peak;
+                 `traffic` comes from the rocprofv3 counter summary in
+                 profiles/ when it was taken on the current kernel source;
+  cpu_baseline - the CPU oracle timed on a bounded sample of the same workload
+                 (ten heads), scaled to the whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
+METRIC = "quantized-attention TOPS (4·B·H·N²·d/s) + % of MI355X INT8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
+# the attention kernel source of each P.V path
+ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn.hip")}
+ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_kernel"}
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(w):
+    """Per-launch HBM bytes of the attention kernel from the committed
+    counter summary, or None if absent or taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(w.name)
+    except (OSError, ValueError, AttributeError):
+        return None
+    if not t or t.get("attn_sha256") != _sha(ATTN_SRC[w.pv]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, rows, heads=10):
+    """Time the oracle on `heads` heads (full quantization of each head plus
+    its checked rows against all N keys) and scale to the whole workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    t_quant = t_attn = 0.0
+    nrows = 0
+    for i in range(heads):
+        b, h = divmod(i, w.H)
+        t0 = time.perf_counter()
+        qc, qs = oracle.quant.quantize_q(q[b, h], w.q_block)
+        kc, ks, mu = oracle.quant.quantize_k(k[b, h], w.k_block)
+        if w.pv == "fp8":
+            vc, vs = oracle.quant.quantize_v_fp8(v[b, h], 64)
+        t1 = time.perf_counter()
+        r = rows[i]
+        if w.pv == "fp8":
+            oracle.attention.attend_fp8(qc, qs, kc, ks, vc, vs, r, w.q_block, w.k_block, w.scale)
+        else:
+            oracle.attention.attend_bf16(qc, qs, kc, ks, v[b, h], r, w.q_block, w.k_block, w.scale)
+        t2 = time.perf_counter()
+        t_quant += t1 - t0
+        t_attn += t2 - t1
+        nrows += len(r)
+    BH = w.B * w.H
+    t_full = t_quant / heads * BH + t_attn / nrows * (w.N * BH)
+    return {"value": round(w.ops / t_full / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{heads} heads of {w.name}: full quantization ({t_quant:.1f} s) + {nrows} query rows "
+                      f"against all {w.N} keys ({t_attn:.1f} s); scaled to {BH} heads x {w.N} rows",
+            "sample_seconds": round(t_quant + t_attn, 2)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan14b-480p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=None)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path is per-head "
+              "independent, see the sharding notes in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_attention_block_amd as sq
+    import workloads as W
+
+    w = W.get(a.workload)
+    t0 = time.perf_counter()
+    q, k, v, rows = W.gen_inputs(w)
+    print(f"[bench] generated {w.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q, K, V = to(q), to(k), to(v)
+    out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(sq.workspace_bytes(w.B, w.H, w.N, w.d, w.pv, w.q_block), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / a.steps
+    print(f"[bench] forward {ms:.3f} ms/step (wall {t_wall / a.steps * 1e3:.3f})", file=sys.stderr, flush=True)
+
+    # ---- the attention kernel alone (one launch per call) on prepared operands
+    qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, w.q_block, 64)
+    if w.pv == "fp8":
+        vc, vs = sq.quantize_v_fp8(V)
+        vp = sq.pack_v(vc, "fp8")
+    else:
+        vs = None
+        vp = sq.pack_v(V, "bf16")
+
+    def kern():
+        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+
+    reps = a.kernel_reps or a.steps
+    for _ in range(2):
+        kern()
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(reps):
+        kern()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    k_ms = e0.elapsed_time(e1) / reps
+    # the quantization/packing stages alone, for the breakdown
+    e0.record(stream)
+    for _ in range(reps):
+        sq.quantize_qk(Q, K, w.q_block, 64)
+        if w.pv == "fp8":
+            sq.pack_v(sq.quantize_v_fp8(V)[0], "fp8")
+        else:
+            sq.pack_v(V, "bf16")
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    p_ms = e0.elapsed_time(e1) / reps
+
+    tops = w.ops / (ms * 1e-3) / 1e12
+    k_tops = w.ops / (k_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+bf16" if w.pv == "bf16" else "i8+fp8",
+        "data": "synthetic",
+        "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "q_block": w.q_block,
+                   "k_block": w.k_block, "pv": w.pv, "dist": w.dist,
+                   "stages_ms": {"attention_kernel": round(k_ms, 4), "quantize_and_pack": round(p_ms, 4)}},
+        "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": _traffic(w), "avg_launch_ms": round(k_ms, 4),
+                     "ops_per_launch": w.ops},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

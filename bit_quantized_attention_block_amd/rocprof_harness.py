@@ -1,0 +1,287 @@
+"""rocprofv3 harness for the quantized-attention path on one MI355X.
+
+Three sub-commands:
+
+    python -m bit_quantized_attention_block_amd.rocprof_harness target   --workload W [--reps R]
+    python -m bit_quantized_attention_block_amd.rocprof_harness collect  --workload W --out DIR
+    python -m bit_quantized_attention_block_amd.rocprof_harness summarize --workload W --out DIR
+
+`target` is the profiled program: seeded inputs of the workload in HBM, then
+R x (quantize Q/K, pack V, attention kernel) and, for calibration, three
+device copies of a 1 GiB buffer (a plain read + write of known size).
+
+`collect` runs `target` under rocprofv3 in separate passes: kernel trace with
+statistics, FETCH_SIZE, WRITE_SIZE, and the shader counters of MFMA
+utilisation.  Every pass is its own process under a hard time limit (a pass
+that asks for more counters than the hardware has hangs, so each pass holds
+only counters that fit one run).
+
+`summarize` turns the CSV output into
+  profiles/<kernel>_<workload>_profile.md  kernel durations (rocprofv3 --stats),
+                                           HBM bytes and MFMA busy per launch
+  profiles/attn_traffic.json               per-launch HBM bytes of the attention
+                                           kernel, keyed by workload, with the
+                                           sha256 of the kernel source it was
+                                           measured on.
+
+HBM bytes come from the TCC counters FETCH_SIZE / WRITE_SIZE (KiB per
+dispatch), each scaled by the factor that maps the same counter to the known
+byte count of the calibration copy.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shlex
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
+ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn.hip")}
+ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_kernel"}
+COPY_BYTES = 1 << 30
+COPY_REPS = 3
+
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "sq": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+           "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
+    "grbm": ["GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+}
+
+
+# ---------------------------------------------------------------------------
+# target
+# ---------------------------------------------------------------------------
+def run_target(workload: str, reps: int) -> None:
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import torch
+
+    import bit_quantized_attention_block_amd as sq
+    import workloads as W
+
+    w = W.get(workload)
+    q, k, v, _ = W.gen_inputs(w)
+    dev = torch.device("cuda:0")
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q, K, V = to(q), to(k), to(v)
+    out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        qi, qs, ki, ks, _mu = sq.quantize_qk(Q, K, w.q_block, w.k_block)
+        if w.pv == "fp8":
+            vc, vs = sq.quantize_v_fp8(V)
+            vp = sq.pack_v(vc, "fp8")
+        else:
+            vs, vp = None, sq.pack_v(V, "bf16")
+        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+        torch.cuda.synchronize()
+        print(f"[target] {w.name}: rep done", flush=True)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[target] calibration copies of {COPY_BYTES} bytes done", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# collect
+# ---------------------------------------------------------------------------
+def _target_cmd(workload: str, reps: int) -> list[str]:
+    return [sys.executable, "-m", "bit_quantized_attention_block_amd.rocprof_harness", "target",
+            "--workload", workload, "--reps", str(reps)]
+
+
+def _rocprof(args: list[str], outdir: str, name: str, workload: str, reps: int, limit: int) -> list[str]:
+    cmd = ["timeout", "-s", "KILL", str(limit), "rocprofv3", *args, "-d", os.path.join(outdir, name), "-o", name,
+           "--output-format", "csv", "--", *_target_cmd(workload, reps)]
+    return cmd
+
+
+def collect(workload: str, outdir: str, reps: int) -> int:
+    outdir = os.path.abspath(outdir)
+    os.makedirs(outdir, exist_ok=True)
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    passes = [("trace", ["--kernel-trace", "--stats"], 300)]
+    passes += [(n, ["--pmc", *c], 120) for n, c in COUNTER_PASSES.items()]
+    commands = {}
+    for name, args, limit in passes:
+        cmd = _rocprof(args, outdir, name, workload, reps, limit)
+        commands[name] = " ".join(shlex.quote(c) for c in cmd)
+        print(f"[collect] pass {name}: {commands[name]}", flush=True)
+        t0 = time.time()
+        with open(os.path.join(outdir, name + ".log"), "w") as log:
+            rc = subprocess.call(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT)
+        print(f"[collect] pass {name} rc={rc} in {time.time() - t0:.1f} s", flush=True)
+        if rc != 0:
+            return rc
+    with open(os.path.join(outdir, "commands.json"), "w") as f:
+        json.dump({"workload": workload, "reps": reps, "outdir": outdir, "commands": commands}, f, indent=1)
+    return 0
+
+
+# ---------------------------------------------------------------------------
+# summarize
+# ---------------------------------------------------------------------------
+def _rows(outdir: str, name: str, suffix: str):
+    files = glob.glob(os.path.join(outdir, name, "**", f"*{suffix}"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, value)} for one counter (values summed over
+    the counter's instances)."""
+    d = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = r["Dispatch_Id"]
+        name, val = d.get(key, (r["Kernel_Name"], 0.0))
+        d[key] = (name, val + float(r["Counter_Value"]))
+    return d
+
+
+def _mean_for(d, match):
+    vals = [v for (n, v) in d.values() if match(n)]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def summarize(workload: str, outdir: str, profiles: str) -> int:
+    sys.path.insert(0, ROOT)
+    import workloads as W
+
+    w = W.get(workload)
+    kname = ATTN_KERNEL[w.pv]
+    is_attn = lambda n: n.split("(")[0].split("<")[0].endswith(kname)
+    is_copy = lambda n: "copybuffer" in n.lower()  # the device-to-device copy of torch copy_
+    with open(os.path.join(outdir, "commands.json")) as f:
+        meta = json.load(f)
+
+    # kernel durations
+    stats = _rows(outdir, "trace", "kernel_stats.csv")
+    stat_lines = ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    attn_avg_ns = None
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        short = name.split("(")[0]
+        stat_lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                          f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                          f"{float(r['Percentage']):.1f}% |")
+        if is_attn(name):
+            attn_avg_ns = float(r["AverageNs"])
+
+    # counters
+    fetch = _per_dispatch(_rows(outdir, "fetch", "counter_collection.csv"), "FETCH_SIZE")
+    write = _per_dispatch(_rows(outdir, "write", "counter_collection.csv"), "WRITE_SIZE")
+    sqr = _rows(outdir, "sq", "counter_collection.csv")
+    grbm = _rows(outdir, "grbm", "counter_collection.csv")
+    f_attn, n_attn = _mean_for(fetch, is_attn)
+    w_attn, _ = _mean_for(write, is_attn)
+    f_copy, n_copy = _mean_for(fetch, is_copy)
+    w_copy, _ = _mean_for(write, is_copy)
+    if None in (f_attn, w_attn, f_copy, w_copy) or not f_copy or not w_copy:
+        print("[summarize] missing counter data", file=sys.stderr)
+        return 1
+    f_scale = COPY_BYTES / (f_copy * 1024.0)   # bytes per counted byte
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    read_b = f_attn * 1024.0 * f_scale
+    write_b = w_attn * 1024.0 * w_scale
+    traffic = read_b + write_b
+
+    sq_vals = {}
+    for c in COUNTER_PASSES["sq"]:
+        v, _ = _mean_for(_per_dispatch(sqr, c), is_attn)
+        sq_vals[c] = v
+    for c in COUNTER_PASSES["grbm"]:
+        v, _ = _mean_for(_per_dispatch(grbm, c), is_attn)
+        sq_vals[c] = v
+
+    ops = w.ops
+    lines = [f"# `{kname}` on {w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})", "",
+             f"Made by `python -m bit_quantized_attention_block_amd.rocprof_harness collect --workload {w.name} "
+             f"--out <out>` on one MI355X, which runs these passes from /tmp with TMPDIR=/tmp and the "
+             f"repository root on PYTHONPATH:", ""]
+    rec_out = meta.get("outdir") or shlex.split(meta["commands"]["trace"]).__getitem__(
+        shlex.split(meta["commands"]["trace"]).index("-d") + 1).rsplit("/", 1)[0]
+    for name, cmd in meta["commands"].items():
+        cmd = cmd.replace(rec_out, "<out>").replace(sys.executable, "python3")
+        cmd = " ".join("python3" if c.endswith("/python") or c.endswith("/python3") else c for c in cmd.split(" "))
+        lines += [f"- {name}: `{cmd}`"]
+    lines += ["", f"Summarized with `python -m bit_quantized_attention_block_amd.rocprof_harness summarize "
+                  f"--workload {w.name} --out <dir>`.", "",
+              "## Kernel durations (rocprofv3 --kernel-trace --stats)", ""] + stat_lines
+    if attn_avg_ns:
+        lines += ["", f"Attention kernel average: {attn_avg_ns / 1e6:.3f} ms -> "
+                      f"{ops / (attn_avg_ns * 1e-9) / 1e12:.1f} TOPS (4 B H N^2 d / t)."]
+    lines += ["", "## HBM traffic per attention launch (TCC FETCH_SIZE / WRITE_SIZE)", "",
+              f"- calibration: device copy of {COPY_BYTES} bytes, {n_copy} dispatches; FETCH_SIZE reads "
+              f"{f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per copy -> scale {f_scale:.4f} (read), "
+              f"{w_scale:.4f} (write)",
+              f"- attention ({n_attn} dispatches): FETCH_SIZE {f_attn:.0f} KiB, WRITE_SIZE {w_attn:.0f} KiB",
+              f"- scaled: read {read_b / 1e9:.3f} GB, write {write_b / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB "
+              f"per launch"]
+    if attn_avg_ns:
+        lines += [f"- at the traced average duration: {traffic / (attn_avg_ns * 1e-9) / 1e9:.0f} GB/s "
+                  f"(HBM peak 8000 GB/s)"]
+    lines += ["", "## Shader counters per attention launch (sums over the device)", ""]
+    for c, v in sq_vals.items():
+        lines += [f"- {c}: {v:.4g}" if v is not None else f"- {c}: n/a"]
+    if sq_vals.get("SQ_VALU_MFMA_BUSY_CYCLES") and sq_vals.get("SQ_BUSY_CYCLES"):
+        lines += ["", "SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD; SQ_BUSY_CYCLES per shader engine "
+                      "(32 engines, 32 SIMDs each): MFMA busy fraction = "
+                      f"{sq_vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (sq_vals['SQ_BUSY_CYCLES'] * 32):.3f}."]
+    os.makedirs(profiles, exist_ok=True)
+    stem = f"{kname}_{w.name}"
+    with open(os.path.join(profiles, stem + "_profile.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    tf = os.path.join(profiles, "attn_traffic.json")
+    try:
+        with open(tf) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[w.name] = {"kernel": kname, "attn_sha256": _sha(ATTN_SRC[w.pv]), "bytes_per_launch": round(traffic),
+                    "read_bytes": round(read_b), "write_bytes": round(write_b),
+                    "fetch_kib": f_attn, "write_kib": w_attn, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+                    "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns}
+    with open(tf, "w") as f:
+        json.dump(allt, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("cmd", choices=["target", "collect", "summarize"])
+    ap.add_argument("--workload", default="wan14b-480p")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args(argv)
+    if a.cmd == "target":
+        run_target(a.workload, a.reps)
+        return 0
+    if a.cmd == "collect":
+        return collect(a.workload, a.out, a.reps)
+    return summarize(a.workload, a.out, a.profiles)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
