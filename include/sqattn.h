@@ -44,10 +44,15 @@
  *     saturating, sign of zero kept); code = 0 where s_v = 0.
  *   - Attention is non-causal over all N keys.  Logits are
  *     D * sQ * sK * scale with D the exact int32 dot product of the codes.
- *     Softmax uses a running max over 64-key tiles; P.V accumulates in fp32;
- *     the output is fp32.  With SQATTN_PV_FP8_E4M3 the kernel rounds
- *     448 * exp(s - m_tile) to E4M3 (m_tile the running max after each 64-key
- *     tile) and keeps the unrounded values in the row sum.
+ *     P.V accumulates in fp32; the output is fp32.
+ *     With SQATTN_PV_BF16 each row is exponentiated against a reference: the
+ *     max logit of its first 32 keys, or, for every row of a 256-row block in
+ *     which some row's sum of weights reaches 2^64, the exact row max.  P is
+ *     rounded to bf16 and the row sum is taken over the rounded P.  The
+ *     normalised result is the same softmax; only roundings differ.
+ *     With SQATTN_PV_FP8_E4M3 the kernel rounds 448 * exp(s - m_tile) to E4M3
+ *     (m_tile the running max after each 64-key tile) and keeps the unrounded
+ *     values in the row sum.
  */
 #ifndef SQATTN_H_
 #define SQATTN_H_
