@@ -31,8 +31,12 @@
 //     2^HEADROOM, the work-group takes the exact row max over all keys in a
 //     second sweep and recomputes with it as reference (then P <= 1).  So the
 //     loop body has no branch on data.
-//   * The row sum is taken on the bf16-rounded P with v_dot2c_f32_bf16, so the
-//     normalisation uses exactly the weights the matrix core multiplied.
+//   * Scores come out of the INT8 MFMAs already as float bit patterns (the
+//     accumulation starts at the bits of 1.5 * 2^23), so a score costs one FMA
+//     and one v_exp_f32 before packing; the row sum adds the fp32 P.  (Vector
+//     instructions other than transcendentals overlap the matrix core only a
+//     little, and v_dot2c stalls it, so the per-score vector work is kept to
+//     FMA, exp, a share of one pack and two adds per pair.)
 //   * Only the last, possibly ragged tile needs key masking.  Rows past N in
 //     the K tile load row N-1 (in bounds, a real score); their P entries are
 //     zeroed and taken out of the row sum afterwards.  The packed V tiles are
@@ -82,48 +86,59 @@ struct Geo {
   static constexpr int VBASE = NSLOT * KS;      // V ring offset in LDS
   static constexpr int LDS_BYTES = NSLOT * (KS + VS);
   static constexpr int KINST = (KT * KROWC + 63) / 64;   // 1 KB direct loads per K tile
-  static constexpr int VINST = (D * VROWC + 63) / 64;
-  static constexpr int KPW = (KINST + WAVES - 1) / WAVES; // per wave (every wave the same)
-  static constexpr int VPW = (VINST + WAVES - 1) / WAVES;
-  static constexpr int LPB = KPW + 1 + VPW;     // direct loads per wave per K+V tile pair
+  static constexpr int VINST = (D * VROWC + 63) / 64;     // ... per V tile
+  static constexpr int PER = (KINST + VINST + WAVES - 1) / WAVES;  // K+V loads per wave
+  static constexpr int LPB = PER + 1;           // direct loads per wave per tile boundary (+ K scale)
   static constexpr int VBYTES = D * KT * 2;     // packed V tile in HBM
 };
 
 // ---------------------------------------------------------------------------
 // One MFMA followed by one softmax pair, as one inline-assembly statement.
 //
-// The pair: two scores s0, s1 of S(h) (int32) become P = 2^(s c - m),
-// rounded to a packed bf16 pair w.  Only assembly statements read the MFMA
-// results (S, O), so no compiler-generated instruction can touch a register
-// an MFMA is still writing; the compiler keeps volatile statements in order
-// and does not move memory accesses across them ("memory"), so the operand
-// reads written between them stay where they are written, with the
-// compiler's own waits.  A score of S(h) is read at least one iteration after
-// the MFMA that produced it.
+// Scores arrive as float bit patterns: the INT8 accumulation starts from the
+// bits of 1.5 * 2^23 (SQ_MAGIC) instead of 0, and since |S| < 2^22 the int32
+// result read as a float is exactly 1.5 * 2^23 + S.  The pair turns two such
+// scores into P = 2^(S c - m) = 2^(x c - k) with k = 1.5 * 2^23 c + m (one
+// FMA each, no conversion), rounds the pair to packed bf16 (w), and adds the
+// two fp32 values to the row sum (acc).
+//
+// Only assembly statements read the MFMA results (S, O), so no
+// compiler-generated instruction can touch a register an MFMA is still
+// writing; the compiler keeps volatile statements in order and does not move
+// memory accesses across them ("memory"), so the operand reads written
+// between them stay where they are written, with the compiler's own waits.  A
+// score of S(h) is read at least one iteration after the MFMA that produced
+// it.
 // ---------------------------------------------------------------------------
+constexpr int SQ_MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
+constexpr float SQ_MAGIC_F = 12582912.0f;
+
 #define SQ_PAIR                                                              \
-  "\n v_cvt_f32_i32 %[t0], %[s0]"                                            \
-  "\n v_cvt_f32_i32 %[t1], %[s1]"                                            \
-  "\n v_fma_f32 %[t0], %[t0], %[c], -%[m]"                                    \
-  "\n v_fma_f32 %[t1], %[t1], %[c], -%[m]"                                    \
+  "\n v_fma_f32 %[t0], %[s0], %[c], -%[k]"                                    \
+  "\n v_fma_f32 %[t1], %[s1], %[c], -%[k]"                                    \
   "\n v_exp_f32 %[t0], %[t0]"                                                \
   "\n v_exp_f32 %[t1], %[t1]"                                                \
   "\n s_nop 0"                                                               \
-  "\n v_cvt_pk_bf16_f32 %[w], %[t0], %[t1]"
-#define SQ_PAIR_OPS(w) [w] "=&v"(w), [t0] "=&v"(t0), [t1] "=&v"(t1)
-#define SQ_PAIR_INS [s0] "v"(s0), [s1] "v"(s1), [c] "v"(c), [m] "v"(m)
+  "\n v_cvt_pk_bf16_f32 %[w], %[t0], %[t1]"                                  \
+  "\n v_add_f32 %[acc], %[acc], %[t0]"                                       \
+  "\n v_add_f32 %[acc], %[acc], %[t1]"
+#define SQ_PAIR_OPS(w) [w] "=&v"(w), [t0] "=&v"(t0), [t1] "=&v"(t1), [acc] "+v"(acc)
+#define SQ_PAIR_INS [s0] "v"(s0), [s1] "v"(s1), [c] "v"(c), [k] "v"(k)
+#define SQ_PAIR_ARGS int s0, int s1, float c, float k, uint32_t &w, float &acc
 
-__device__ __forceinline__ void qk0_pair(v16i& sn, v4i a, v4i q, int s0, int s1, float c, float m, uint32_t& w) {
+__device__ __forceinline__ void qk0_pair(v16i& sn, v4i a, v4i q, const v16i& mg, SQ_PAIR_ARGS) {
   float t0, t1;
-  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], 0" SQ_PAIR
-               : [sn] "=&v"(sn), SQ_PAIR_OPS(w) : [a] "v"(a), [q] "v"(q), SQ_PAIR_INS : "memory");
+  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], %[mg]" SQ_PAIR
+               : [sn] "=&v"(sn), SQ_PAIR_OPS(w)
+               : [a] "v"(a), [q] "v"(q), [mg] "v"(mg), SQ_PAIR_INS
+               : "memory");
 }
-__device__ __forceinline__ void qk_pair(v16i& sn, v4i a, v4i q, int s0, int s1, float c, float m, uint32_t& w) {
+__device__ __forceinline__ void qk_pair(v16i& sn, v4i a, v4i q, SQ_PAIR_ARGS) {
   float t0, t1;
   asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], %[sn]" SQ_PAIR
                : [sn] "+v"(sn), SQ_PAIR_OPS(w) : [a] "v"(a), [q] "v"(q), SQ_PAIR_INS : "memory");
 }
-__device__ __forceinline__ void pv_pair(v16f& o, v4i a, v4i p, int s0, int s1, float c, float m, uint32_t& w) {
+__device__ __forceinline__ void pv_pair(v16f& o, v4i a, v4i p, SQ_PAIR_ARGS) {
   float t0, t1;
   asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" SQ_PAIR
                : [o] "+v"(o), SQ_PAIR_OPS(w) : [a] "v"(a), [p] "v"(p), SQ_PAIR_INS : "memory");
@@ -131,10 +146,11 @@ __device__ __forceinline__ void pv_pair(v16f& o, v4i a, v4i p, int s0, int s1, f
 __device__ __forceinline__ void pv_only(v16f& o, v4i a, v4i p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" : [o] "+v"(o) : [a] "v"(a), [p] "v"(p) : "memory");
 }
-__device__ __forceinline__ void pair_only(int s0, int s1, float c, float m, uint32_t& w) {
+__device__ __forceinline__ void pair_only(SQ_PAIR_ARGS) {
   float t0, t1;
   asm volatile(SQ_PAIR : SQ_PAIR_OPS(w) : SQ_PAIR_INS : "memory");
 }
+#undef SQ_PAIR_ARGS
 #undef SQ_PAIR_INS
 #undef SQ_PAIR_OPS
 #undef SQ_PAIR
@@ -150,36 +166,65 @@ struct Ctx {
   uint32_t kbase, vbase;  // per-lane LDS operand offsets (slot 0, half 0)
   float cq;               // sQ(row) * scale * log2(e)
   v4i qreg[G::NCH];       // Q operands
+  v16i magic;             // SQ_MAGIC in every element: start of the INT8 accumulation
   v16f o[G::NCB];         // O^T accumulators
   float m, l;             // reference max (log2 units), row sum
 
-  // ---- global -> LDS (direct).  Every wave issues KPW+1 (VPW) instructions;
-  // instruction slots past the tile wrap around and repeat a chunk range,
-  // writing the same bytes again, so all waves count the same loads.  The
-  // extra K instruction copies the tile's K scale into the slot (each lane
-  // one copy).
-  __device__ __forceinline__ void load_k(int t, int slot) {
+  // ---- global -> LDS (direct).  One boundary refills a K slot (KINST 1 KB
+  // chunks, padded rows) and a V slot (VINST chunks); the KINST + VINST chunks
+  // are spread over the waves, PER instructions each (slots past the total
+  // wrap around and load a chunk again: the same bytes, so every wave counts
+  // the same loads).  Each instruction reads 16 bytes per lane at a fixed
+  // per-lane offset (off[i]) from a wave-uniform tile base.  One more
+  // instruction per wave copies the K tile's scale into the K slot.
+  int lrow[G::PER];  // lane's row (K key row or V^T channel row) of chunk slot i
+  int lcol[G::PER];  // lane's byte offset within that row
+  int chunk[G::PER];  // wave-uniform chunk of slot i: < KINST K, else V
+
+  __device__ __forceinline__ void init_loads() {
 #pragma unroll
-    for (int i = 0; i < G::KPW; ++i) {
+    for (int i = 0; i < G::PER; ++i) {
       int u = wave + WAVES * i;
-      if (u >= G::KINST) u -= G::KINST;
-      const int q = u * 64 + lane;  // padded chunk index
-      const int row = min(q / G::KROWC, KT - 1), col = min(q % G::KROWC, G::KCPR - 1);
-      const int key = min(t * KT + row, N - 1);
-      const uint8_t* src = kh + (long long)key * D + col * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + slot * G::KS + u * 1024), 16, 0, 0);
+      if (u >= G::KINST + G::VINST) u -= G::KINST + G::VINST;
+      chunk[i] = u;
+      if (u < G::KINST) {
+        const int q = u * 64 + lane;  // padded chunk index
+        lrow[i] = min(q / G::KROWC, KT - 1);
+        lcol[i] = min(q % G::KROWC, G::KCPR - 1) * 16;
+      } else {
+        const int q = (u - G::KINST) * 64 + lane;
+        lrow[i] = min(q / G::VROWC, D - 1);
+        lcol[i] = min(q % G::VROWC, 7) * 16;
+      }
     }
-    __builtin_amdgcn_global_load_lds(skh + t, (lds_void*)(lds + slot * G::KS + G::KSC), 4, 0, 0);
   }
-  __device__ __forceinline__ void load_v(int t, int slot) {
+  // K tile tk into K slot ks and V tile tv into V slot vs.  K rows past N
+  // (last tile) read row N-1 instead.
+  __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
+    const uint8_t* kt = kh + (long long)tk * KT * D;
+    const uint8_t* vt = vth + (long long)tv * G::VBYTES;
+    const int kmax = N - 1 - tk * KT;
 #pragma unroll
-    for (int i = 0; i < G::VPW; ++i) {
-      int u = wave + WAVES * i;
-      if (u >= G::VINST) u -= G::VINST;
+    for (int i = 0; i < G::PER; ++i) {
+      const int u = chunk[i];
+      const bool isk = u < G::KINST;  // wave-uniform
+      const uint8_t* base = isk ? kt : vt;
+      const int lim = isk ? kmax : D;
+      const int stride = isk ? D : 128;
+      const uint32_t o = (uint32_t)(min(lrow[i], lim) * stride + lcol[i]);
+      const int dst = isk ? ks * G::KS + u * 1024 : G::VBASE + vs * G::VS + (u - G::KINST) * 1024;
+      __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(skh + tk, (lds_void*)(lds + ks * G::KS + G::KSC), 4, 0, 0);
+  }
+  // K tile only, into slot 0 (the exact-max sweep; not on the hot path)
+  __device__ __forceinline__ void load_k(int t) {
+    const int kmax = N - 1 - t * KT;
+    for (int u = wave; u < G::KINST; u += WAVES) {
       const int q = u * 64 + lane;
-      const int c = min(q / G::VROWC, D - 1), col = min(q % G::VROWC, 7);
-      const uint8_t* src = vth + (long long)t * G::VBYTES + c * 128 + col * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + G::VBASE + slot * G::VS + u * 1024), 16, 0, 0);
+      const int row = min(min(q / G::KROWC, KT - 1), kmax);
+      const uint8_t* src = kh + ((long long)t * KT + row) * D + min(q % G::KROWC, G::KCPR - 1) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + u * 1024), 16, 0, 0);
     }
   }
   __device__ __forceinline__ float k_scale(int slot) const {
@@ -187,12 +232,12 @@ struct Ctx {
   }
 
   // max over the 32 keys of S (lanes l and l^32 share a query), in log2 units
-  __device__ __forceinline__ float rowmax(const v16i& s, float c) const {
+  __device__ __forceinline__ float rowmax(const v16i& s, float c, int bias) const {
     int d = max(max(s[0], s[1]), s[2]);
 #pragma unroll
     for (int i = 3; i < 15; i += 2) d = max(max(d, s[i]), s[i + 1]);
     d = max(d, s[15]);
-    return (float)pair_max_i(d) * c;  // c >= 0
+    return (float)(pair_max_i(d) - bias) * c;  // c >= 0
   }
 
   // ---- operand i of an iteration (see the MFMA order below); ka/va: lane
@@ -216,96 +261,92 @@ struct Ctx {
   static constexpr int RD_AHEAD = 4;
   template <int KB>
   __device__ __forceinline__ void step(const v16i& scur, v16i& snext, const v4i (&pprev)[2], v4i (&pcur)[2],
-                                       int t, float c) {
+                                       int t, float c, float k, float& acc) {
     const uint32_t ka = kbase + ((t + KB) & (NSLOT - 1)) * G::KS + (KB ^ 1) * 32 * G::KROW;
     const uint32_t va = vbase + ((t - 1 + KB) & (NSLOT - 1)) * G::VS + (KB ^ 1) * 64;
     v4i a[NMF];
     uint32_t w[8];
-    float lsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RD_AHEAD; ++i) a[i] = operand(i, ka, va);
+    for (int i = 0; i < RD_AHEAD; ++i) {
+      a[i] = operand(i, ka, va);
+      asm volatile("" ::: "memory");  // keep the reads in MFMA order
+    }
 #pragma unroll
     for (int i = 0; i < (NMF > 8 ? NMF : 8); ++i) {
       if (i >= NMF) {  // no MFMA left (D = 64): softmax pair only
-        pair_only(scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+        pair_only(scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
       } else if (i >= 8) {  // no softmax pair left
         pv_only(o[i - 2 * G::NCH], a[i], pprev[1]);
       } else if (i < 2 * G::NCH && (i & 1) == 0) {
         if (i == 0)
-          qk0_pair(snext, a[i], qreg[0], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+          qk0_pair(snext, a[i], qreg[0], magic, scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
         else
-          qk_pair(snext, a[i], qreg[i >> 1], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+          qk_pair(snext, a[i], qreg[i >> 1], scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
       } else {
         const int k2 = (i < 2 * G::NCH) ? 0 : 1;
         const int cb = (i < 2 * G::NCH) ? (i >> 1) : (i - 2 * G::NCH);
-        pv_pair(o[cb], a[i], pprev[k2], scur[2 * i], scur[2 * i + 1], c, m, w[i]);
+        pv_pair(o[cb], a[i], pprev[k2], scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
       }
       if (i + RD_AHEAD < NMF) a[i + RD_AHEAD] = operand(i + RD_AHEAD, ka, va);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[j]), v2bf{(__bf16)1.0f, (__bf16)1.0f}, lsum,
-                                             false);
     pcur[0] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     pcur[1] = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    l += lsum;
   }
 
   // ---- all tiles of one pass (the loop body is generated once per order)
   __device__ __forceinline__ void tiles(v16i& S0, v16i& S1, v4i (&P0)[2], v4i (&P1)[2], float c) {
+    float k = __builtin_fmaf(SQ_MAGIC_F, c, m);
     for (int t = 0; t < nt - 1; ++t) {
-      step<0>(S0, S1, P1, P0, t, c);
+      step<0>(S0, S1, P1, P0, t, c, k, l);
       // Tile boundary: every wave is done with K(t) and V(t-1); K(t+1) and
       // V(t) (issued three boundaries ago, or in the prologue) must have
       // landed, the two latest batches may stay in flight.
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB));
       __syncthreads();
-      const float c_next = cq * k_scale((t + 1) & (NSLOT - 1));
       // refill the freed slots (past the end: the last tile again, unread)
-      load_k(min(t + NSLOT, nt - 1), t & (NSLOT - 1));
-      load_v(min(t + NSLOT - 1, nt - 1), (t - 1) & (NSLOT - 1));
-      step<1>(S1, S0, P0, P1, t, c);
+      load_kv(min(t + NSLOT, nt - 1), t & (NSLOT - 1), min(t + NSLOT - 1, nt - 1), (t - 1) & (NSLOT - 1));
+      const float c_next = cq * k_scale((t + 1) & (NSLOT - 1));
+      step<1>(S1, S0, P0, P1, t, c, k, l);
       c = c_next;
+      k = __builtin_fmaf(SQ_MAGIC_F, c, m);
     }
-    // last tile: keys past N masked
+    // last tile: keys past N masked; its row-sum terms are taken from the
+    // masked bf16 P instead of the pairs' fp32 sums
     const int t = nt - 1;
-    step<0>(S0, S1, P1, P0, t, c);
-    fix_tail(P0, t, 0);
+    float unused = 0.0f;
+    step<0>(S0, S1, P1, P0, t, c, k, unused);
+    l += tail_sum(P0, t, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    step<1>(S1, S0, P0, P1, t, c);
-    fix_tail(P1, t, 1);
+    step<1>(S1, S0, P0, P1, t, c, k, unused);
+    l += tail_sum(P1, t, 1);
     pv_last(P1, t & (NSLOT - 1));
   }
 
-  // ---- last tile, half kb: zero P of keys >= N and take them out of the row sum
-  __device__ __forceinline__ void fix_tail(v4i (&pb)[2], int t, int kb) {
+  // ---- last tile, half kb: zero P of keys >= N; returns the sum of the kept P
+  __device__ __forceinline__ float tail_sum(v4i (&pb)[2], int t, int kb) {
     const int kvalid = N - t * KT - kb * 32;
-    float drop = 0.0f;
+    float kept = 0.0f;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k0 = 16 * k2 + 8 * g + 2 * j;
-        const uint32_t w = (uint32_t)pb[k2][j];
         const uint32_t keep = (k0 >= kvalid ? 0u : 0xFFFFu) | (k0 + 1 >= kvalid ? 0u : 0xFFFF0000u);
-        drop = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w & ~keep), v2bf{(__bf16)1.0f, (__bf16)1.0f},
-                                               drop, false);
-        pb[k2][j] = (int)(w & keep);
+        const uint32_t w = (uint32_t)pb[k2][j] & keep;
+        kept += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+        pb[k2][j] = (int)w;
       }
-    l -= drop;
+    return kept;
   }
 
-  // S = half kb of the K tile in slot
-  __device__ __forceinline__ void qk_half(v16i& s, int slot, int kb) const {
+  // S = half kb of the K tile in slot, accumulated from `init`
+  __device__ __forceinline__ void qk_half(v16i& s, int slot, int kb, const v16i& init) const {
 #pragma unroll
     for (int ch = 0; ch < G::NCH; ++ch) {
       const v4i a = *(const v4i*)(lds + kbase + slot * G::KS + kb * 32 * G::KROW + ch * 32);
       if (ch == 0) {
-        v16i z;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = 0;
-        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], z, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], init, 0, 0, 0);
       } else {
         s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], s, 0, 0, 0);
       }
@@ -357,6 +398,12 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   C.kh = (const uint8_t*)p.k + hoff;
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
+  C.init_loads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) C.magic[r] = SQ_MAGIC;
+  v16i zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero[r] = 0;
   const int row = qt * ATT_QWG + C.wave * 32 + C.lr;
   const bool rok = row < p.N;
 #pragma unroll
@@ -365,7 +412,6 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   C.cq = rok ? p.sq[(long long)bh * p.nq + row / p.q_block] * p.scale_log2e : 0.0f;
 
   const int nt = p.nt;
-  constexpr int LPB = G::LPB;
   v16i S0, S1;
   v4i P0[2], P1[2];
 
@@ -377,13 +423,13 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
       float mx = -__builtin_inff();
       for (int t = 0; t < nt; ++t) {
         __syncthreads();
-        C.load_k(t, 0);
+        C.load_k(t);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const float c = C.cq * ld_uniform(C.skh + t);
-        C.qk_half(S0, 0, 0);
-        C.qk_half(S1, 0, 1);
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(C.rowmax(S0, c), C.rowmax(S1, c)));
+        C.qk_half(S0, 0, 0, zero);
+        C.qk_half(S1, 0, 1, zero);
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(C.rowmax(S0, c, 0), C.rowmax(S1, c, 0)));
       }
       C.m = mx;
       __syncthreads();
@@ -395,23 +441,18 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
       for (int i = 0; i < 16; ++i) C.o[cb][i] = 0.0f;
     P1[0] = P1[1] = v4i{0, 0, 0, 0};
 
-    // Prologue.  K(0) first, then three batches of LPB loads per wave:
-    // {K(1), V(0)}, {K(2), V(1)}, {K(3), V(2)}; every loop boundary adds one
-    // more batch, so "all but the last two batches landed" is vmcnt(2 LPB).
-    // V slot 3 is zeroed (the first iteration multiplies it by P(-1) = 0).
-    C.load_k(0, 0);
+    // Prologue: K(0..3) and V(0..3) into slots 0..3, all landed before the
+    // loop.  The first iteration multiplies V slot 3 by P(-1) = 0 (a finite
+    // tile, so the product is 0).  In the loop, boundary t waits for the loads
+    // of boundary t-3 and lets those of t-2 and t-1 (LPB per wave each) stay
+    // in flight.
 #pragma unroll
-    for (int j = 1; j < NSLOT; ++j) {
-      C.load_k(min(j, nt - 1), j);
-      C.load_v(min(j - 1, nt - 1), j - 1);
-    }
-    for (int i = tid; i < G::VS / 16; i += NTHR)
-      *(v4i*)(smem + G::VBASE + (NSLOT - 1) * G::VS + i * 16) = v4i{0, 0, 0, 0};
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPB));
+    for (int j = 0; j < NSLOT; ++j) C.load_kv(min(j, nt - 1), j, min(j, nt - 1), j);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     float c = C.cq * C.k_scale(0);
-    C.qk_half(S0, 0, 0);
-    if (pass == 0) C.m = C.rowmax(S0, c);  // reference: max of the first 32 keys
+    C.qk_half(S0, 0, 0, C.magic);
+    if (pass == 0) C.m = C.rowmax(S0, c, SQ_MAGIC);  // reference: max of the first 32 keys
 
     C.tiles(S0, S1, P0, P1, c);
     C.l = pair_sum_f(C.l);

@@ -48,8 +48,9 @@
  *     With SQATTN_PV_BF16 each row is exponentiated against a reference: the
  *     max logit of its first 32 keys, or, for every row of a 256-row block in
  *     which some row's sum of weights reaches 2^64, the exact row max.  P is
- *     rounded to bf16 and the row sum is taken over the rounded P.  The
- *     normalised result is the same softmax; only roundings differ.
+ *     rounded to bf16 for P.V; the row sum adds the fp32 values of P (for the
+ *     last, masked tile the bf16 values).  The normalised result is the same
+ *     softmax; only roundings differ.
  *     With SQATTN_PV_FP8_E4M3 the kernel rounds 448 * exp(s - m_tile) to E4M3
  *     (m_tile the running max after each 64-key tile) and keeps the unrounded
  *     values in the row sum.
