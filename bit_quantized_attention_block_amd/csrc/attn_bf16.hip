@@ -199,23 +199,34 @@ struct Ctx {
     }
   }
   // K tile tk into K slot ks and V tile tv into V slot vs.  K rows past N
-  // (last tile) read row N-1 instead.
-  __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
-    const uint8_t* kt = kh + (long long)tk * KT * D;
-    const uint8_t* vt = vth + (long long)tv * G::VBYTES;
-    const int kmax = N - 1 - tk * KT;
-#pragma unroll
-    for (int i = 0; i < G::PER; ++i) {
-      const int u = chunk[i];
-      const bool isk = u < G::KINST;  // wave-uniform
-      const uint8_t* base = isk ? kt : vt;
-      const int lim = isk ? kmax : D;
-      const int stride = isk ? D : 128;
-      const uint32_t o = (uint32_t)(min(lrow[i], lim) * stride + lcol[i]);
-      const int dst = isk ? ks * G::KS + u * 1024 : G::VBASE + vs * G::VS + (u - G::KINST) * 1024;
-      __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
+  // (last tile) read row N-1 instead.  Instruction i < PER is one chunk; i ==
+  // PER copies the K scale.
+  struct Refill {
+    const uint8_t* kt;
+    const uint8_t* vt;
+    int tk, ks, vs, kmax;
+  };
+  __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) const {
+    return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, ks, vs, N - 1 - tk * KT};
+  }
+  __device__ __forceinline__ void load_part(const Refill& r, int i) {
+    if (i == G::PER) {
+      __builtin_amdgcn_global_load_lds(skh + r.tk, (lds_void*)(lds + r.ks * G::KS + G::KSC), 4, 0, 0);
+      return;
     }
-    __builtin_amdgcn_global_load_lds(skh + tk, (lds_void*)(lds + ks * G::KS + G::KSC), 4, 0, 0);
+    const int u = chunk[i];
+    const bool isk = u < G::KINST;  // wave-uniform
+    const uint8_t* base = isk ? r.kt : r.vt;
+    const int lim = isk ? r.kmax : D;
+    const int stride = isk ? D : 128;
+    const uint32_t o = (uint32_t)(min(lrow[i], lim) * stride + lcol[i]);
+    const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
+    __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
+  }
+  __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
+    const Refill r = refill(tk, ks, tv, vs);
+#pragma unroll
+    for (int i = 0; i <= G::PER; ++i) load_part(r, i);
   }
   // K tile only, into slot 0 (the exact-max sweep; not on the hot path)
   __device__ __forceinline__ void load_k(int t) {
@@ -259,9 +270,9 @@ struct Ctx {
   // one packed bf16 pair of P(h)) sits between MFMA j and MFMA j+1.
   static constexpr int NMF = G::NCH + 2 * G::NCB;
   static constexpr int RD_AHEAD = 4;
-  template <int KB>
+  template <int KB, bool REFILL = false>
   __device__ __forceinline__ void step(const v16i& scur, v16i& snext, const v4i (&pprev)[2], v4i (&pcur)[2],
-                                       int t, float c, float k, float& acc) {
+                                       int t, float c, float k, float& acc, const Refill* rf = nullptr) {
     const uint32_t ka = kbase + ((t + KB) & (NSLOT - 1)) * G::KS + (KB ^ 1) * 32 * G::KROW;
     const uint32_t va = vbase + ((t - 1 + KB) & (NSLOT - 1)) * G::VS + (KB ^ 1) * 64;
     v4i a[NMF];
@@ -288,6 +299,14 @@ struct Ctx {
         pv_pair(o[cb], a[i], pprev[k2], scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
       }
       if (i + RD_AHEAD < NMF) a[i + RD_AHEAD] = operand(i + RD_AHEAD, ka, va);
+      // the tile refill, one load after every other MFMA
+      if constexpr (REFILL) {
+        if ((i & 1) == 1 && (i >> 1) <= G::PER) load_part(*rf, i >> 1);
+      }
+    }
+    if constexpr (REFILL) {  // fewer MFMAs than loads (D = 64)
+#pragma unroll
+      for (int j = ((NMF > 8 ? NMF : 8) + 1) / 2; j <= G::PER; ++j) load_part(*rf, j);
     }
     pcur[0] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     pcur[1] = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
@@ -303,10 +322,11 @@ struct Ctx {
       // landed, the two latest batches may stay in flight.
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB));
       __syncthreads();
-      // refill the freed slots (past the end: the last tile again, unread)
-      load_kv(min(t + NSLOT, nt - 1), t & (NSLOT - 1), min(t + NSLOT - 1, nt - 1), (t - 1) & (NSLOT - 1));
+      // refill the freed slots (past the end: the last tile again, unread),
+      // spread over the next iteration's MFMAs
+      const Refill rf = refill(min(t + NSLOT, nt - 1), t & (NSLOT - 1), min(t + NSLOT - 1, nt - 1), (t - 1) & (NSLOT - 1));
       const float c_next = cq * k_scale((t + 1) & (NSLOT - 1));
-      step<1>(S1, S0, P0, P1, t, c, k, l);
+      step<1, true>(S1, S0, P0, P1, t, c, k, l, &rf);
       c = c_next;
       k = __builtin_fmaf(SQ_MAGIC_F, c, m);
     }
