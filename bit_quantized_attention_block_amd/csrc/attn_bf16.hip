@@ -113,47 +113,59 @@ struct Geo {
 constexpr int SQ_MAGIC = 0x4B400000;   // bits of 1.5 * 2^23
 constexpr float SQ_MAGIC_F = 12582912.0f;
 
-#define SQ_PAIR                                                              \
-  "\n v_fma_f32 %[t0], %[s0], %[c], -%[k]"                                    \
-  "\n v_fma_f32 %[t1], %[s1], %[c], -%[k]"                                    \
-  "\n v_exp_f32 %[t0], %[t0]"                                                \
-  "\n v_exp_f32 %[t1], %[t1]"                                                \
-  "\n s_nop 0"                                                               \
-  "\n v_cvt_pk_bf16_f32 %[w], %[t0], %[t1]"                                  \
-  "\n v_add_f32 %[acc], %[acc], %[t0]"                                       \
-  "\n v_add_f32 %[acc], %[acc], %[t1]"
-#define SQ_PAIR_OPS(w) [w] "=&v"(w), [t0] "=&v"(t0), [t1] "=&v"(t1), [acc] "+v"(acc)
-#define SQ_PAIR_INS [s0] "v"(s0), [s1] "v"(s1), [c] "v"(c), [k] "v"(k)
-#define SQ_PAIR_ARGS int s0, int s1, float c, float k, uint32_t &w, float &acc
+// One MFMA and up to two softmax-pair stages as one inline-assembly
+// statement.  Stage 1 turns two scores into P = 2^(x c - k) in fp32 (u0, u1);
+// stage 2, four MFMAs later, packs such a pair to bf16 (w) and adds it to the
+// row sum (acc).  Exponentials overlap the matrix core well, other vector
+// instructions much less, so the stages are spread over the iteration's
+// MFMAs.  Being one statement, no stage output can share a register with the
+// MFMA's sources (early-clobber outputs), which a separate statement could
+// reuse while the MFMA has yet to read them.
+//   MF: 0 none, 1 first INT8 k-step (accumulator from mg), 2 INT8, 3 bf16 P.V
+#define SQ_ST1                                      \
+  "\n v_fma_f32 %[u0], %[s0], %[c], -%[k]"          \
+  "\n v_fma_f32 %[u1], %[s1], %[c], -%[k]"          \
+  "\n v_exp_f32 %[u0], %[u0]"                      \
+  "\n v_exp_f32 %[u1], %[u1]"
+#define SQ_ST2                                      \
+  "\n s_nop 0"                                     \
+  "\n v_cvt_pk_bf16_f32 %[w], %[v0], %[v1]"        \
+  "\n v_add_f32 %[acc], %[acc], %[v0]"             \
+  "\n v_add_f32 %[acc], %[acc], %[v1]"
+#define SQ_OUTS [acc] "+v"(acc), [u0] "=&v"(u0), [u1] "=&v"(u1), [w] "=&v"(w)
+#define SQ_INS [a] "v"(a), [b] "v"(b), [s0] "v"(s0), [s1] "v"(s1), [c] "v"(c), [k] "v"(k), [v0] "v"(v0), [v1] "v"(v1)
+// the statement for MFMA text mf, with the stages this slot holds
+#define SQ_SLOT(mf, outs, ins)                                          \
+  if constexpr (S1 && S2)                                               \
+    asm volatile(mf SQ_ST1 SQ_ST2 : outs : ins : "memory");             \
+  else if constexpr (S1)                                                \
+    asm volatile(mf SQ_ST1 : outs : ins : "memory");                    \
+  else if constexpr (S2)                                                \
+    asm volatile(mf SQ_ST2 : outs : ins : "memory");                    \
+  else                                                                  \
+    asm volatile(mf : outs : ins : "memory");
+#define SQ_COMMA ,
 
-__device__ __forceinline__ void qk0_pair(v16i& sn, v4i a, v4i q, const v16i& mg, SQ_PAIR_ARGS) {
-  float t0, t1;
-  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], %[mg]" SQ_PAIR
-               : [sn] "=&v"(sn), SQ_PAIR_OPS(w)
-               : [a] "v"(a), [q] "v"(q), [mg] "v"(mg), SQ_PAIR_INS
-               : "memory");
+template <int MF, bool S1, bool S2>
+__device__ __forceinline__ void slot(v16i& sn, v16f& o, v4i a, v4i b, const v16i& mg, int s0, int s1, float c,
+                                     float k, float& u0, float& u1, float v0, float v1, uint32_t& w, float& acc) {
+  if constexpr (MF == 1) {
+    SQ_SLOT("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[b], %[mg]", [sn] "=&v"(sn) SQ_COMMA SQ_OUTS,
+            SQ_INS SQ_COMMA [mg] "v"(mg))
+  } else if constexpr (MF == 2) {
+    SQ_SLOT("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[b], %[sn]", [sn] "+v"(sn) SQ_COMMA SQ_OUTS, SQ_INS)
+  } else if constexpr (MF == 3) {
+    SQ_SLOT("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[b], %[o]", [o] "+v"(o) SQ_COMMA SQ_OUTS, SQ_INS)
+  } else {
+    SQ_SLOT("", SQ_OUTS, SQ_INS)
+  }
 }
-__device__ __forceinline__ void qk_pair(v16i& sn, v4i a, v4i q, SQ_PAIR_ARGS) {
-  float t0, t1;
-  asm volatile("v_mfma_i32_32x32x32_i8 %[sn], %[a], %[q], %[sn]" SQ_PAIR
-               : [sn] "+v"(sn), SQ_PAIR_OPS(w) : [a] "v"(a), [q] "v"(q), SQ_PAIR_INS : "memory");
-}
-__device__ __forceinline__ void pv_pair(v16f& o, v4i a, v4i p, SQ_PAIR_ARGS) {
-  float t0, t1;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" SQ_PAIR
-               : [o] "+v"(o), SQ_PAIR_OPS(w) : [a] "v"(a), [p] "v"(p), SQ_PAIR_INS : "memory");
-}
-__device__ __forceinline__ void pv_only(v16f& o, v4i a, v4i p) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %[o], %[a], %[p], %[o]" : [o] "+v"(o) : [a] "v"(a), [p] "v"(p) : "memory");
-}
-__device__ __forceinline__ void pair_only(SQ_PAIR_ARGS) {
-  float t0, t1;
-  asm volatile(SQ_PAIR : SQ_PAIR_OPS(w) : SQ_PAIR_INS : "memory");
-}
-#undef SQ_PAIR_ARGS
-#undef SQ_PAIR_INS
-#undef SQ_PAIR_OPS
-#undef SQ_PAIR
+#undef SQ_COMMA
+#undef SQ_SLOT
+#undef SQ_INS
+#undef SQ_OUTS
+#undef SQ_ST2
+#undef SQ_ST1
 
 template <int D>
 struct Ctx {
@@ -260,6 +272,38 @@ struct Ctx {
     return *(const v4i*)(lds + va + cb * 32 * G::VROW + k2 * 32);
   }
 
+  static constexpr int NMF = G::NCH + 2 * G::NCB;  // MFMAs per half-tile iteration
+  static constexpr int RD_AHEAD = 4;                // operand reads ahead of their MFMA
+
+  // ---- slot i of an iteration: MFMA i (if any), stage 1 of pair i (i < 8),
+  // stage 2 of pair i - 4 (4 <= i < 12)
+  template <int I>
+  __device__ __forceinline__ void slot_i(const v16i& scur, v16i& snext, const v4i (&pprev)[2], const v4i (&a)[NMF],
+                                         float (&u)[8][2], uint32_t (&w)[8], float c, float k, float& acc) {
+    constexpr bool S1 = I < 8, S2 = I >= 4 && I < 12;
+    constexpr int MF = I >= NMF ? 0 : (I < 2 * G::NCH && (I & 1) == 0) ? (I == 0 ? 1 : 2) : 3;
+    constexpr int K2 = (I < 2 * G::NCH) ? 0 : 1;
+    constexpr int CB = I >= NMF ? 0 : (I < 2 * G::NCH) ? (I >> 1) : (I - 2 * G::NCH);
+    const v4i av = a[I < NMF ? I : 0];
+    const v4i bv = MF == 3 ? pprev[K2] : qreg[MF == 0 ? 0 : ((I >> 1) < G::NCH ? (I >> 1) : 0)];
+    float d0, d1;
+    uint32_t dw;
+    float& u0 = S1 ? u[I < 8 ? I : 0][0] : d0;
+    float& u1 = S1 ? u[I < 8 ? I : 0][1] : d1;
+    const float v0 = S2 ? u[S2 ? I - 4 : 0][0] : 0.0f;
+    const float v1 = S2 ? u[S2 ? I - 4 : 0][1] : 0.0f;
+    uint32_t& wr = S2 ? w[S2 ? I - 4 : 0] : dw;
+    const int s0 = S1 ? scur[S1 ? 2 * I : 0] : 0, s1 = S1 ? scur[S1 ? 2 * I + 1 : 0] : 0;
+    slot<MF, S1, S2>(snext, o[CB], av, bv, magic, s0, s1, c, k, u0, u1, v0, v1, wr, acc);
+  }
+  template <int I = 0>
+  __device__ __forceinline__ void issue_slot(int i, const v16i& scur, v16i& snext, const v4i (&pprev)[2],
+                                             const v4i (&a)[NMF], float (&u)[8][2], uint32_t (&w)[8], float c,
+                                             float k, float& acc) {
+    if (i == I) slot_i<I>(scur, snext, pprev, a, u, w, c, k, acc);
+    if constexpr (I + 1 < (NMF > 12 ? NMF : 12)) issue_slot<I + 1>(i, scur, snext, pprev, a, u, w, c, k, acc);
+  }
+
   // ---- one half-tile iteration h = 2t + KB.  K(h+1) is half KB^1 of tile
   // t + KB; V(h-1) is half KB^1 of tile t - 1 + KB (for h = 0 the zeroed slot
   // with P(-1) = 0).  c: the softmax factor of tile t.
@@ -268,8 +312,6 @@ struct Ctx {
   // first P.V k-step (channel block i/2); then the second P.V k-step.  Each
   // operand is read RD_AHEAD MFMAs ahead; softmax pair j (two scores of S(h),
   // one packed bf16 pair of P(h)) sits between MFMA j and MFMA j+1.
-  static constexpr int NMF = G::NCH + 2 * G::NCB;
-  static constexpr int RD_AHEAD = 4;
   template <int KB, bool REFILL = false>
   __device__ __forceinline__ void step(const v16i& scur, v16i& snext, const v4i (&pprev)[2], v4i (&pcur)[2],
                                        int t, float c, float k, float& acc, const Refill* rf = nullptr) {
@@ -282,31 +324,23 @@ struct Ctx {
       a[i] = operand(i, ka, va);
       asm volatile("" ::: "memory");  // keep the reads in MFMA order
     }
+    float u[8][2];
 #pragma unroll
-    for (int i = 0; i < (NMF > 8 ? NMF : 8); ++i) {
-      if (i >= NMF) {  // no MFMA left (D = 64): softmax pair only
-        pair_only(scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
-      } else if (i >= 8) {  // no softmax pair left
-        pv_only(o[i - 2 * G::NCH], a[i], pprev[1]);
-      } else if (i < 2 * G::NCH && (i & 1) == 0) {
-        if (i == 0)
-          qk0_pair(snext, a[i], qreg[0], magic, scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
-        else
-          qk_pair(snext, a[i], qreg[i >> 1], scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
-      } else {
-        const int k2 = (i < 2 * G::NCH) ? 0 : 1;
-        const int cb = (i < 2 * G::NCH) ? (i >> 1) : (i - 2 * G::NCH);
-        pv_pair(o[cb], a[i], pprev[k2], scur[2 * i], scur[2 * i + 1], c, k, w[i], acc);
-      }
+    for (int i = 0; i < (NMF > 12 ? NMF : 12); ++i) {
+      issue_slot(i, scur, snext, pprev, a, u, w, c, k, acc);  // MFMA i, pair i stage 1, pair i-4 stage 2
       if (i + RD_AHEAD < NMF) a[i + RD_AHEAD] = operand(i + RD_AHEAD, ka, va);
       // the tile refill, one load after every other MFMA
       if constexpr (REFILL) {
         if ((i & 1) == 1 && (i >> 1) <= G::PER) load_part(*rf, i >> 1);
       }
     }
-    if constexpr (REFILL) {  // fewer MFMAs than loads (D = 64)
+    // The first INT8 MFMA reads `magic` as its accumulator a few cycles after
+    // issue; keep that register block live to the end of the iteration so the
+    // compiler cannot hand it to a later statement's outputs meanwhile.
+    asm volatile("" ::"v"(magic));
+    if constexpr (REFILL) {  // more loads than iterations
 #pragma unroll
-      for (int j = ((NMF > 8 ? NMF : 8) + 1) / 2; j <= G::PER; ++j) load_part(*rf, j);
+      for (int j = ((NMF > 12 ? NMF : 12) + 1) / 2; j <= G::PER; ++j) load_part(*rf, j);
     }
     pcur[0] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     pcur[1] = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
