@@ -34,8 +34,8 @@ METRIC = "quantized-attention TOPS (4·B·H·N²·d/s) + % of MI355X INT8 MFMA p
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
 # the attention kernel source of each P.V path
-ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn.hip")}
-ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_kernel"}
+ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn_fp8.hip")}
+ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel"}
 
 
 def _sha(path):

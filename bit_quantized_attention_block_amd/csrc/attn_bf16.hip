@@ -1,8 +1,7 @@
 // Quantized attention kernel, 16-bit P.V path (gfx950).
 //
-// Same mathematics and register layouts as the FP8 kernel in attn.hip (INT8
-// S^T = K Q^T, lane-local online softmax, O^T = V^T P^T); see that file for
-// the layout derivation.  What differs is the schedule.
+// INT8 S^T = K Q^T, lane-local softmax, O^T = V^T P^T in the register
+// layouts described in attn.hip.
 //
 // Work-group: 8 waves (two per SIMD), 32 query rows each, 256 rows per
 // work-group.  The unit of the pipeline is a half-tile h of 32 keys (half
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   v16i zero;
 #pragma unroll
   for (int r = 0; r < 16; ++r) zero[r] = 0;
-  const int row = qt * ATT_QWG + C.wave * 32 + C.lr;
+  const int row = qt * ATT_QWG + C.wave * ATT_QW + C.lr;
   const bool rok = row < p.N;
 #pragma unroll
   for (int ch = 0; ch < G::NCH; ++ch)

@@ -16,9 +16,9 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Attention tile: 64 keys.  K blocks must coincide with these tiles.
 constexpr int KT = 64;
-// Attention work-group: 4 waves, 64 query rows each.
-constexpr int ATT_WAVES = 4;
-constexpr int ATT_QW = 64;
+// Attention work-group: 8 waves, 32 query rows each.
+constexpr int ATT_WAVES = 8;
+constexpr int ATT_QW = 32;
 constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

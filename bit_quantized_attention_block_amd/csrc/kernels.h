@@ -31,5 +31,7 @@ struct AttnParams {
 void launch_attention(const AttnParams& p, int d, int pv, hipStream_t st);
 // 16-bit P.V kernel (software-pipelined); p.qtiles and p.per_xcd must be set.
 void launch_attention_bf16(const AttnParams& p, int d, hipStream_t st);
+// FP8 P.V kernel (software-pipelined, running max per tile); same requirements.
+void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 
 }  // namespace sqattn

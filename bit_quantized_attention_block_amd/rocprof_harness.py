@@ -43,8 +43,8 @@ import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
-ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn.hip")}
-ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_kernel"}
+ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn_fp8.hip")}
+ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel"}
 COPY_BYTES = 1 << 30
 COPY_REPS = 3
 
