@@ -364,7 +364,6 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 8; ++r) P1[r] = 0;
-  float svp = 0.0f;
 
   // Boundary after iteration t: K(t+2) and V(t) (issued three boundaries ago
   // or in the prologue) must have landed; refill K slot (t+1)%4 with K(t+5)
@@ -374,8 +373,10 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   // boundaries that wait for it), so every iteration issues the same loads.
   typename Cx::Refill rf = C.refill(min(4, nt - 1), 0, min(2, nt - 1), 2);
   auto step = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
+    // K(t+1) and V(t-1) have landed (boundary t-1); their slots are refilled
+    // only after this iteration
     const float c_next = C.cq * C.k_scale((t + 1) & (NSLOT - 1));
-    const float sv_cur = C.v_scale(t & (NSLOT - 1));
+    const float svp = C.v_scale((t - 1) & (NSLOT - 1));
     C.template iter<true, false>(sc, sn, pprev, pcur, t, c, svp, rf);
     // Wait for our own loads of three boundaries ago and all LDS reads, then
     // a plain barrier (the "memory" clobber keeps every memory access on its
@@ -385,12 +386,15 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     asm volatile("s_barrier" ::: "memory");
     rf = C.refill(min(t + 5, nt - 1), (t + 1) & (NSLOT - 1), min(t + 3, nt - 1), (t - 1) & (NSLOT - 1));
     c = c_next;
-    svp = sv_cur;
   };
   auto last = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
-    const float sv_last = C.v_scale(t & (NSLOT - 1));
+    const float svp = C.v_scale((t - 1) & (NSLOT - 1));
     C.template iter<false, true>(sc, sn, pprev, pcur, t, c, svp, rf);
-    C.pv_last(pcur, t & (NSLOT - 1), sv_last);
+    // V(t) may still be in flight (issued up to two boundaries ago, by any
+    // wave): wait for every load, then a barrier
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    C.pv_last(pcur, t & (NSLOT - 1), C.v_scale(t & (NSLOT - 1)));
   };
   // tiles in pairs, so that the score and P registers alternate without copies
   int t = 0;
@@ -404,7 +408,6 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   } else {
     last(S0, S1, P1, P0, t);
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may outlive the work-group
 
   // epilogue: O = O^T / l, fp32 rows
   const float inv = 1.0f / pair_sum_f(C.l);
