@@ -48,7 +48,7 @@ EXPORTS = {
 
 
 class Opts(ctypes.Structure):
-    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("reserved", _i)]
+    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("out_dtype", _i)]
 
 
 class SqattnError(RuntimeError):
@@ -170,8 +170,28 @@ def quantize_v_fp8(v, v_block: int = 64):
     return codes, sc
 
 
-def _opts(q_block):
-    return Opts(q_block=int(q_block), k_block=64, v_block=64, reserved=0)
+OUT_FP32, OUT_BF16 = 0, 1
+
+
+def _opts(q_block, out_dtype=OUT_FP32):
+    return Opts(q_block=int(q_block), k_block=64, v_block=64, out_dtype=out_dtype)
+
+
+def _out(out, shape, dev, out_dtype):
+    """The output tensor (allocated when None) and its sqattn_out_dtype code:
+    fp32 by default, bf16 (the fp32 result rounded to nearest even) when
+    out_dtype is torch.bfloat16 or a bf16 `out` is given."""
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"out_dtype must be torch.float32 or torch.bfloat16, got {out_dtype}")
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    _dev(out, "out", out_dtype)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out, (OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32)
 
 
 def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
@@ -180,8 +200,9 @@ def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
 
 
 def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
-            workspace=None):
-    """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> fp32 out [B,H,N,d]."""
+            workspace=None, out_dtype=None):
+    """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> out [B,H,N,d],
+    fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, torch.bfloat16)
@@ -190,11 +211,9 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
         raise ValueError("q, k, v shapes differ")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    _dev(out, "out", torch.float32)
+    out, od = _out(out, (B, H, N, d), q.device, out_dtype)
     w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
-    o = _opts(q_block)
+    o = _opts(q_block, od)
     _check(lib().sqattn_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                    _ptr(w), wb, _stream(q), ctypes.byref(o)))
     return out
@@ -216,7 +235,7 @@ def pack_v(v, pv="bf16"):
 
 
 def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
-                     pv="bf16", q_block: int = 128, out=None):
+                     pv="bf16", q_block: int = 128, out=None, out_dtype=None):
     """The attention kernel alone, on quantized Q/K and packed V (see pack_v)."""
     torch = _torch()
     _dev(q_i8, "q_i8", torch.int8)
@@ -231,10 +250,8 @@ def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale
         _dev(v_scale, "v_scale", torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q_i8.device)
-    _dev(out, "out", torch.float32)
-    o = _opts(q_block)
+    out, od = _out(out, (B, H, N, d), q_i8.device, out_dtype)
+    o = _opts(q_block, od)
     _check(lib().sqattn_attend_quantized(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_packed),
                                          _ptr(v_scale), B, H, N, d, float(scale), _PV[pv], ctypes.byref(o),
                                          _ptr(out), _stream(q_i8)))

@@ -60,15 +60,18 @@ int check_ptr(const void* p, const char* name, size_t align) {
 }
 
 struct Opts {
-  int q_block, k_block, v_block;
+  int q_block, k_block, v_block, out_bf16;
 };
 
 int resolve_opts(const sqattn_opts* o, Opts* r) {
   r->q_block = 128;
   r->k_block = 64;
   r->v_block = 64;
+  r->out_bf16 = 0;
   if (!o) return SQATTN_OK;
-  if (o->reserved != 0) return fail(SQATTN_ERR_INVALID_ARG, "opts.reserved must be 0");
+  if (o->out_dtype != SQATTN_OUT_FP32 && o->out_dtype != SQATTN_OUT_BF16)
+    return fail(SQATTN_ERR_INVALID_ARG, "opts.out_dtype must be SQATTN_OUT_FP32 or SQATTN_OUT_BF16");
+  r->out_bf16 = o->out_dtype == SQATTN_OUT_BF16;
   if (o->q_block) r->q_block = o->q_block;
   if (o->k_block) r->k_block = o->k_block;
   if (o->v_block) r->v_block = o->v_block;
@@ -149,7 +152,7 @@ struct Workspace {
 const float kLog2e = 1.4426950408889634f;
 
 int validate_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
-                     int pv, const float* out, const sqattn_opts* opts, Sizes* z, Opts* o) {
+                     int pv, const void* out, const sqattn_opts* opts, Sizes* z, Opts* o) {
   int s;
   if ((s = check_ptr(q, "q", 16)) || (s = check_ptr(k, "k", 16)) || (s = check_ptr(v, "v", 16)) ||
       (s = check_ptr(out, "out", 16)))
@@ -241,7 +244,7 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
 }
 
 int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
-                      int pv_dtype, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                      int pv_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
                       const sqattn_opts* opts) {
   g_err.clear();
   int s;
@@ -276,6 +279,7 @@ int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H,
   p.vt = ws.at<void>(L.vt);
   p.sv = vs;
   p.out = out;
+  p.out_bf16 = o.out_bf16;
   p.N = N;
   p.nq = (int)z.nq;
   p.q_block = o.q_block;
@@ -287,7 +291,7 @@ int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H,
 }
 
 int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
-                   int pv_dtype, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                   int pv_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return sqattn_forward_ex(q, k, v, B, H, N, d, scale, pv_dtype, out, workspace, workspace_bytes, stream,
                            nullptr);
 }
@@ -320,7 +324,7 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
 
 int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                             const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
-                            int pv_dtype, const sqattn_opts* opts, float* out, void* stream) {
+                            int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
   g_err.clear();
   int s;
   Sizes z;
@@ -343,6 +347,7 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
   p.vt = v_packed;
   p.sv = v_scale;
   p.out = out;
+  p.out_bf16 = o.out_bf16;
   p.N = N;
   p.nq = (int)((N + o.q_block - 1) / o.q_block);
   p.q_block = o.q_block;

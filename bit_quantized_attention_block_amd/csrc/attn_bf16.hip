@@ -515,19 +515,9 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     if (pass == 1 || !__syncthreads_or(over)) break;
   }
 
-  // epilogue: O = O^T / l, fp32 rows
+  // epilogue: O = O^T / l, fp32 or bf16 rows
   const float inv = 1.0f / C.l;
-  if (rok) {
-    float* orow = p.out + hoff + (long long)row * D;
-#pragma unroll
-    for (int cb = 0; cb < G::NCB; ++cb)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        v4f v = {C.o[cb][4 * i4] * inv, C.o[cb][4 * i4 + 1] * inv, C.o[cb][4 * i4 + 2] * inv,
-                 C.o[cb][4 * i4 + 3] * inv};
-        *(v4f*)(orow + cb * 32 + i4 * 8 + C.g * 4) = v;
-      }
-  }
+  if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, inv, C.g);
 }
 
 template <int D>

@@ -23,6 +23,43 @@ constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats to packed bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  v2bf v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Epilogue of the attention kernels: one query row of O = scale * O^T.  Lane
+// half g holds channels 32 cb + 8 i4 + 4 g + j in o[cb][4 i4 + j]; the row
+// goes out as fp32 or, with bf16, rounded to bf16.
+template <int NCB>
+__device__ __forceinline__ void store_out_row(void* out, bool bf16, long long base, const v16f (&o)[NCB],
+                                              float scale, int g) {
+  if (bf16) {
+    uint16_t* orow = (uint16_t*)out + base;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const uint2 w = make_uint2(pack_bf16x2(o[cb][4 * i4] * scale, o[cb][4 * i4 + 1] * scale),
+                                   pack_bf16x2(o[cb][4 * i4 + 2] * scale, o[cb][4 * i4 + 3] * scale));
+        *(uint2*)(orow + cb * 32 + i4 * 8 + g * 4) = w;
+      }
+  } else {
+    float* orow = (float*)out + base;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v4f v = {o[cb][4 * i4] * scale, o[cb][4 * i4 + 1] * scale, o[cb][4 * i4 + 2] * scale,
+                       o[cb][4 * i4 + 3] * scale};
+        *(v4f*)(orow + cb * 32 + i4 * 8 + g * 4) = v;
+      }
+  }
+}
+
 // Layout of one 64-key V tile inside the kernel (both in HBM workspace and LDS):
 // transposed, [d][64 keys].  For FP8 the 64 key bytes of a row are permuted so
 // that the 32 keys one MFMA lane-half consumes are contiguous:

@@ -23,7 +23,8 @@ struct AttnParams {
   const float* sk;
   const void* vt;
   const float* sv;
-  float* out;
+  void* out;      // fp32, or bf16 (round to nearest even) when out_bf16
+  int out_bf16;
   int N, nq, q_block, nt, BH, qtiles, per_xcd;
   float scale_log2e;
 };

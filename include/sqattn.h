@@ -78,14 +78,18 @@ typedef enum {
 
 typedef enum { SQATTN_PV_BF16 = 0, SQATTN_PV_FP8_E4M3 = 1 } sqattn_pv_dtype;
 
-/* Block sizes.  A zero field takes its default.  q_block: any multiple of 16
- * (default 128).  k_block: 64 (the attention tile; default).  v_block: 64
- * (FP8 only; default).  reserved must be 0. */
+/* Output element type (sqattn_opts.out_dtype). */
+typedef enum { SQATTN_OUT_FP32 = 0, SQATTN_OUT_BF16 = 1 } sqattn_out_dtype;
+
+/* Block sizes and output type.  A zero field takes its default.  q_block:
+ * any multiple of 16 (default 128).  k_block: 64 (the attention tile;
+ * default).  v_block: 64 (FP8 only; default).  out_dtype: SQATTN_OUT_FP32
+ * (default) or SQATTN_OUT_BF16, the fp32 result rounded to nearest even. */
 typedef struct sqattn_opts {
   int q_block;
   int k_block;
   int v_block;
-  int reserved;
+  int out_dtype;
 } sqattn_opts;
 
 /* SQATTN_VERSION of the loaded library. */
@@ -139,7 +143,8 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
 
 /*
  * Full forward: out = softmax(Q K^T * scale) V computed on quantized
- * operands (the steps above), fp32 out [B,H,N,d].
+ * operands (the steps above), out [B,H,N,d] fp32 (bf16 with
+ * opts->out_dtype = SQATTN_OUT_BF16 in sqattn_forward_ex).
  *   scale     : softmax scale applied to the logits (commonly 1/sqrt(d)),
  *               finite and >= 0.
  *   pv_dtype  : SQATTN_PV_BF16 or SQATTN_PV_FP8_E4M3.
@@ -149,12 +154,12 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
  * Defaults: q_block 128, k_block 64, v_block 64.
  */
 int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d,
-                   float scale, int pv_dtype, float* out, void* workspace, size_t workspace_bytes,
+                   float scale, int pv_dtype, void* out, void* workspace, size_t workspace_bytes,
                    void* stream);
 
 /* sqattn_forward with explicit block sizes (opts may be NULL = defaults). */
 int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d,
-                      float scale, int pv_dtype, float* out, void* workspace,
+                      float scale, int pv_dtype, void* out, void* workspace,
                       size_t workspace_bytes, void* stream, const sqattn_opts* opts);
 
 /*
@@ -180,12 +185,12 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
  *              k_block = 64 and q_block = opts->q_block (default 128).
  *   v_packed : from sqattn_pack_v with the same pv_dtype.
  *   v_scale  : [B,H,ceil(N/64)] from sqattn_quantize_v_fp8 for FP8; NULL for bf16.
- *   out      : fp32 [B,H,N,d].
+ *   out      : [B,H,N,d], fp32 or bf16 as opts->out_dtype says.
  */
 int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                             const float* k_scale, const void* v_packed, const float* v_scale,
                             int B, int H, int N, int d, float scale, int pv_dtype,
-                            const sqattn_opts* opts, float* out, void* stream);
+                            const sqattn_opts* opts, void* out, void* stream);
 
 #ifdef __cplusplus
 }

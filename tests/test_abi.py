@@ -78,7 +78,8 @@ def _err():
     (dict(opts=sq.Opts(128, 128, 64, 0)), UNSUPPORTED, "k_block"),
     (dict(opts=sq.Opts(128, 64, 32, 0)), UNSUPPORTED, "v_block"),
     (dict(opts=sq.Opts(24, 64, 64, 0)), INVALID, "q_block"),
-    (dict(opts=sq.Opts(128, 64, 64, 1)), INVALID, "reserved"),
+    (dict(opts=sq.Opts(128, 64, 64, 2)), INVALID, "out_dtype"),
+    (dict(opts=sq.Opts(128, 64, 64, -1)), INVALID, "out_dtype"),
 ])
 def test_forward_validation(kw, code, needle):
     assert _fwd(**kw) == code

@@ -181,6 +181,38 @@ def test_deterministic_full_grid(pv):
     assert bool(torch.isfinite(outs[0]).all())
 
 
+@pytest.mark.parametrize("pv", ["bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_output(pv, d):
+    """opts.out_dtype = bf16: the fp32 result rounded to nearest even, bit for
+    bit, from both entry points; and within the parity bound plus one bf16
+    ulp of the oracle."""
+    w = W.get(1)
+    q, k, v, rows = W.gen_inputs(w, N=700, d=d, B=1, H=2)
+    Q, K, V = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o32 = sq.forward(Q, K, V, scale=w.scale, pv=pv)
+    o16 = sq.forward(Q, K, V, scale=w.scale, pv=pv, out_dtype=torch.bfloat16)
+    qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, w.q_block, 64)
+    if pv == "fp8":
+        vc, vs = sq.quantize_v_fp8(V)
+        a16 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(vc, pv), vs, scale=w.scale, pv=pv,
+                                  out=torch.empty_like(o16))
+    else:
+        a16 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(V, pv), scale=w.scale, pv=pv,
+                                  out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16 and a16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(a16, o16)
+    ref = oracle_heads(q, k, v, rows, w.q_block, w.scale, pv)
+    got = host(o16.float())
+    for i in range(2):
+        r = ref[i]["out"]
+        e = ref[i]["envelope"] if pv == "fp8" else 0.0
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+        assert (np.abs(got[0, i][rows[i]] - r) <= MAX_ABS + e + ulp).all()
+
+
 def test_workspace_too_small_raises():
     Q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
