@@ -188,9 +188,8 @@ struct Ctx {
   // the same loads).  Each instruction reads 16 bytes per lane at a fixed
   // per-lane offset (off[i]) from a wave-uniform tile base.  One more
   // instruction per wave copies the K tile's scale into the K slot.
-  int lrow[G::PER];  // lane's row (K key row or V^T channel row) of chunk slot i
-  int lcol[G::PER];  // lane's byte offset within that row
-  int chunk[G::PER];  // wave-uniform chunk of slot i: < KINST K, else V
+  uint32_t off[G::PER];  // lane's byte offset of chunk slot i within its tile
+  int chunk[G::PER];     // wave-uniform chunk of slot i: < KINST K, else V
 
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
@@ -199,26 +198,35 @@ struct Ctx {
       if (u >= G::KINST + G::VINST) u -= G::KINST + G::VINST;
       chunk[i] = u;
       if (u < G::KINST) {
-        const int q = u * 64 + lane;  // padded chunk index
-        lrow[i] = min(q / G::KROWC, KT - 1);
-        lcol[i] = min(q % G::KROWC, G::KCPR - 1) * 16;
+        const int q = u * 64 + lane;
+        off[i] = (uint32_t)(min(q / G::KROWC, KT - 1) * D + min(q % G::KROWC, G::KCPR - 1) * 16);
       } else {
         const int q = (u - G::KINST) * 64 + lane;
-        lrow[i] = min(q / G::VROWC, D - 1);
-        lcol[i] = min(q % G::VROWC, 7) * 16;
+        off[i] = (uint32_t)(min(q / G::VROWC, D - 1) * 128 + min(q % G::VROWC, 7) * 16);
       }
     }
   }
-  // K tile tk into K slot ks and V tile tv into V slot vs.  K rows past N
-  // (last tile) read row N-1 instead.  Instruction i < PER is one chunk; i ==
-  // PER copies the K scale.
+  // K rows past N in the last K tile read row N-1 instead.  Refills only move
+  // forward and end on the last tile, so from its first refill on the K
+  // offsets stay clamped (init_loads restores them).
+  __device__ __forceinline__ void clamp_last_k() {
+    const uint32_t lim = (uint32_t)((N - 1 - (nt - 1) * KT) * D);
+#pragma unroll
+    for (int i = 0; i < G::PER; ++i)
+      if (chunk[i] < G::KINST) off[i] = min(off[i], lim + (off[i] & (D - 1)));
+  }
+
+
+  // K tile tk into K slot ks and V tile tv into V slot vs.  Instruction i <
+  // PER is one chunk; i == PER copies the K scale.
   struct Refill {
     const uint8_t* kt;
     const uint8_t* vt;
-    int tk, ks, vs, kmax;
+    int tk, ks, vs;
   };
-  __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) const {
-    return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, ks, vs, N - 1 - tk * KT};
+  __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) {
+    if (tk == nt - 1) clamp_last_k();
+    return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, ks, vs};
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (i == G::PER) {
@@ -228,9 +236,7 @@ struct Ctx {
     const int u = chunk[i];
     const bool isk = u < G::KINST;  // wave-uniform
     const uint8_t* base = isk ? r.kt : r.vt;
-    const int lim = isk ? r.kmax : D;
-    const int stride = isk ? D : 128;
-    const uint32_t o = (uint32_t)(min(lrow[i], lim) * stride + lcol[i]);
+    const uint32_t o = off[i];
     const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
     __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
   }
@@ -451,7 +457,6 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   C.kh = (const uint8_t*)p.k + hoff;
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
-  C.init_loads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) C.magic[r] = SQ_MAGIC;
   v16i zero;
@@ -469,6 +474,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   v4i P0[2], P1[2];
 
   for (int pass = 0; pass < 2; ++pass) {
+    C.init_loads();  // the refills of a pass clamp the K offsets at its end
     if (pass == 1) {
       // Rare path: some row's sum reached 2^HEADROOM.  Take the exact row max
       // over all keys (K tiles one at a time through slot 0) as the reference,

@@ -112,9 +112,8 @@ struct Ctx {
   // ---- global -> LDS (direct); see the 16-bit kernel for the scheme.  Chunk
   // slot i < PER of a wave is one 1 KB chunk of the K or V slot; PER and
   // PER + 1 copy the K and V scales.
-  int lrow[G::PER];
-  int lcol[G::PER];
-  int chunk[G::PER];
+  uint32_t off[G::PER];  // lane's byte offset of chunk slot i within its tile
+  int chunk[G::PER];     // wave-uniform chunk of slot i: < KINST K, else V
 
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
@@ -124,22 +123,24 @@ struct Ctx {
       chunk[i] = u;
       if (u < G::KINST) {
         const int q = u * 64 + lane;
-        lrow[i] = min(q / G::KROWC, KT - 1);
-        lcol[i] = min(q % G::KROWC, G::KCPR - 1) * 16;
+        off[i] = (uint32_t)(min(q / G::KROWC, KT - 1) * D + min(q % G::KROWC, G::KCPR - 1) * 16);
       } else {
         const int q = (u - G::KINST) * 64 + lane;
-        lrow[i] = min(q / G::VROWC, D - 1);
-        lcol[i] = min(q % G::VROWC, 3) * 16;
+        off[i] = (uint32_t)(min(q / G::VROWC, D - 1) * KT + min(q % G::VROWC, 3) * 16);
       }
     }
   }
+  // K rows past N (last tile) read row N-1 instead: klim is the byte offset
+  // of the last row to read (past every offset when the tile is full).
   struct Refill {
     const uint8_t* kt;
     const uint8_t* vt;
-    int tk, tv, ks, vs, kmax;
+    int tk, tv, ks, vs;
+    uint32_t klim;
   };
   __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) const {
-    return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, tv, ks, vs, N - 1 - tk * KT};
+    return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, tv, ks, vs,
+                  (uint32_t)(min(N - 1 - tk * KT, KT) * D)};
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (i == G::PER) {
@@ -153,9 +154,7 @@ struct Ctx {
     const int u = chunk[i];
     const bool isk = u < G::KINST;  // wave-uniform
     const uint8_t* base = isk ? r.kt : r.vt;
-    const int lim = isk ? r.kmax : D;
-    const int stride = isk ? D : KT;
-    const uint32_t o = (uint32_t)(min(lrow[i], lim) * stride + lcol[i]);
+    const uint32_t o = isk ? min(off[i], r.klim + (off[i] & (D - 1))) : off[i];
     const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
     __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
   }
