@@ -14,13 +14,14 @@
 //
 //   iteration t:   MFMA  T    = V(t-1)^T P(t-1)^T     (D/32 x fp8 32x32x64)
 //                  MFMA  S(t+1) = K(t+1) Q^T          (2 D/32 x i8 32x32x32)
-//                  VALU  tile max of S(t) -> m(t), alpha = 2^(m(t-1) - m(t))
-//                        O = alpha (O + sV(t-1) T)
+//                  VALU  tile max of S(t) -> m(t)
+//                        O += sV(t-1) 2^(m(t-1) - mr) T
 //                        P(t) = E4M3(448 * 2^(S(t) c(t) - m(t))), row sum
 //
-// * Tile t's P is relative to m(t), the max over tiles 0..t; O and the row
-//   sum are kept relative to the latest max (one exp per row and tile, and a
-//   vector rescale of O only when some row of the wave saw a larger max).
+// * Tile t's P is relative to m(t), the exact max over tiles 0..t.  O and
+//   the row sum are kept relative to a reference mr <= m that moves up only
+//   when some row's max outgrew it by 2^16 (one exp per row and tile, and a
+//   vector rescale of O rarely after the first tile).
 // * The per-block V scale is applied as O += sV * T with T from an MFMA that
 //   starts at zero, so O is held in absolute units (no ratio of scales that
 //   could overflow when neighbouring V blocks differ by many orders of
@@ -51,6 +52,7 @@ constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
 constexpr int NSLOT = 4;                          // LDS ring depth (tiles)
 constexpr float LOG2_448 = 8.80735492205760410f;  // log2(448)
+constexpr float REBASE = 16.0f;                   // lazy reference of O: at most 2^16 below the max
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -107,7 +109,10 @@ struct Ctx {
   float cq;               // sQ(row) * scale * log2(e)
   v4i qreg[G::NCH];       // Q operands
   v16f o[G::NCB];         // O^T accumulators (absolute units, relative to m)
-  float m, l;             // running max (log2 units), running sum of 448 P~
+  float m;               // running max (log2 units): P of tile t is relative to m(t)
+  float mr;              // reference of O and l (mr <= m, lazily moved up)
+  float ep;              // 2^(m - mr) of the latest tile
+  float l;               // running sum of 448 P~, relative to mr
 
   // ---- global -> LDS (direct); see the 16-bit kernel for the scheme.  Chunk
   // slot i < PER of a wave is one 1 KB chunk of the K or V slot; PER and
@@ -213,21 +218,10 @@ struct Ctx {
     const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
 
     // running max of tile t
-    const float tmax = (float)tile_max(sc) * c;  // c >= 0
-    const bool grow = tmax > m;
-    const float mn = grow ? tmax : m;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;  // m = -inf: 0
-    m = mn;
-    const float mp = mn - LOG2_448;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int cb = 0; cb < G::NCB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-    }
-    const float w = svp * alpha;
+    const float mn = __builtin_fmaxf(m, (float)tile_max(sc) * c);  // c >= 0
+    const float w = svp * ep;  // tile t-1 relative to mr
 
-    // P.V of the previous tile from a zero accumulator, O = alpha (O + sV T)
+    // P.V of the previous tile from a zero accumulator, O += w T
 #pragma unroll
     for (int cb = 0; cb < G::NCB; ++cb) {
       const v4i a0 = *(const v4i*)(lds + va + cb * 32 * G::VROW);
@@ -261,6 +255,21 @@ struct Ctx {
 #pragma unroll
     for (int i = G::NCB; i < G::LPB; ++i) load_part(rf, i);
 
+    // move the reference of O and l up once some row's max outgrew it by
+    // 2^REBASE (always on the first tile, where mr = -inf)
+    if (__builtin_amdgcn_ballot_w64(mn - mr > REBASE)) {
+      const float f = __builtin_amdgcn_exp2f(mr - mn);  // mr = -inf: 0
+#pragma unroll
+      for (int cb = 0; cb < G::NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= f;
+      l *= f;
+      mr = mn;
+    }
+    m = mn;
+    const float mp = mn - LOG2_448;
+    ep = __builtin_amdgcn_exp2f(mn - mr);  // tile t relative to mr, <= 2^REBASE
+
     // P(t) = E4M3(y), y = 448 P~; byte 16 kb + i of the operand is key
     // 32 kb + 16 (i / 8) + 8 g + i % 8, the lane's S(t)[kb][i]
     const int kvalid = N - t * KT;
@@ -284,11 +293,12 @@ struct Ctx {
       word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
       pcur[r] = word;
     }
-    l = __builtin_fmaf(l, alpha, (part[0] + part[1]) + (part[2] + part[3]));
+    l = __builtin_fmaf(ep, (part[0] + part[1]) + (part[2] + part[3]), l);
   }
 
-  // ---- O += sV(last) V(last)^T P(last)^T
+  // ---- O += sV(last) 2^(m - mr) V(last)^T P(last)^T
   __device__ __forceinline__ void pv_last(const v8i& p, int slot, float sv) {
+    sv *= ep;
     const uint32_t va = vbase + slot * G::VS;
 #pragma unroll
     for (int cb = 0; cb < G::NCB; ++cb) {
@@ -342,6 +352,8 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     C.qreg[ch] = rok ? *(const v4i*)(p.q + hoff + (long long)row * D + ch * 32 + C.g * 16) : v4i{0, 0, 0, 0};
   C.cq = rok ? p.sq[(long long)bh * p.nq + row / p.q_block] * p.scale_log2e : 0.0f;
   C.m = -__builtin_inff();
+  C.mr = -__builtin_inff();
+  C.ep = 0.0f;
   C.l = 0.0f;
 #pragma unroll
   for (int cb = 0; cb < G::NCB; ++cb)
