@@ -221,6 +221,34 @@ def test_workspace_too_small_raises():
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("pv", ["bf16", "fp8"])
+def test_long_sequence(pv):
+    """One head of 2^19 + 37 tokens (d = 64): 8193 key tiles with a ragged
+    last Q block and K tile.  Checked rows: the whole last Q block plus 200
+    seeded ones."""
+    w = W.get(3 if pv == "fp8" else 2)
+    N = (1 << 19) + 37
+    q, k, v, _ = W.gen_inputs(w, N=N, d=64, B=1, H=1)
+    rng = np.random.default_rng(20)
+    tail = np.arange(N - N % w.q_block, N)
+    rows = [np.concatenate([np.sort(rng.choice(N - len(tail), 200, replace=False)), tail])]
+    _run_case(w, pv=pv, data=(q, k, v, rows))
+
+
+@pytest.mark.timeout(900)
+def test_offsets_past_2gib():
+    """140 heads of 32760 x 128: the fp32 output spans 2.35e9 bytes, so the
+    last head's rows sit past 2^31 bytes (and its Q/K/V past 2^30); that head
+    is checked against the oracle on 256 seeded rows (with its ragged tail)."""
+    w = W.get(2)
+    H = 140
+    q, k, v, rows = W.gen_inputs(w, H=H)
+    assert q.size * 4 > (1 << 31)
+    rows = [r[-256:] for r in rows]
+    _run_case(w, data=(q, k, v, rows), heads=[H - 1])
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("index", [1, 2, 3, 4])
 def test_full_size_workload(index):
     """The Wan-shaped workloads at full size: quantization bit-exact on every
