@@ -128,19 +128,28 @@ def main(argv=None):
     def step():
         sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws)
 
+    def timed(fn, n):
+        """Average, median and minimum ms of n calls of fn, from HIP events on
+        the launch stream (one event after every call), and the wall time of
+        the n calls (launch to completion)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - wall
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        return ev[0].elapsed_time(ev[n]) / n, float(np.median(per)), min(per), wall
+
     for _ in range(a.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(a.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / a.steps
-    print(f"[bench] forward {ms:.3f} ms/step (wall {t_wall / a.steps * 1e3:.3f})", file=sys.stderr, flush=True)
+    ms, ms_med, ms_min, t_wall = timed(step, a.steps)
+    print(f"[bench] forward {ms:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f}; wall "
+          f"{t_wall / a.steps * 1e3:.3f}); torch {torch.__version__}, HIP {torch.version.hip}",
+          file=sys.stderr, flush=True)
 
     # ---- the attention kernel alone (one launch per call) on prepared operands
     qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, w.q_block, 64)
@@ -157,24 +166,17 @@ def main(argv=None):
     reps = a.kernel_reps or a.steps
     for _ in range(2):
         kern()
-    torch.cuda.synchronize(dev)
-    e0.record(stream)
-    for _ in range(reps):
-        kern()
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    k_ms = e0.elapsed_time(e1) / reps
+    k_ms, k_med, k_min, _ = timed(kern, reps)
+
     # the quantization/packing stages alone, for the breakdown
-    e0.record(stream)
-    for _ in range(reps):
+    def prep():
         sq.quantize_qk(Q, K, w.q_block, 64)
         if w.pv == "fp8":
             sq.pack_v(sq.quantize_v_fp8(V)[0], "fp8")
         else:
             sq.pack_v(V, "bf16")
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    p_ms = e0.elapsed_time(e1) / reps
+
+    p_ms = timed(prep, reps)[0]
 
     tops = w.ops / (ms * 1e-3) / 1e12
     k_tops = w.ops / (k_ms * 1e-3) / 1e12
@@ -194,7 +196,9 @@ def main(argv=None):
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "q_block": w.q_block,
                    "k_block": w.k_block, "pv": w.pv, "dist": w.dist,
-                   "stages_ms": {"attention_kernel": round(k_ms, 4), "quantize_and_pack": round(p_ms, 4)}},
+                   "stages_ms": {"forward_median": round(ms_med, 4), "forward_min": round(ms_min, 4),
+                                 "attention_kernel": round(k_ms, 4), "attention_kernel_median": round(k_med, 4),
+                                 "attention_kernel_min": round(k_min, 4), "quantize_and_pack": round(p_ms, 4)}},
         "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
                      "traffic": _traffic(w), "avg_launch_ms": round(k_ms, 4),
