@@ -54,7 +54,6 @@ constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
 constexpr int NSLOT = 4;           // LDS ring depth (tiles)
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 field layout:
 // vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
@@ -230,7 +229,7 @@ struct Ctx {
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (i == G::PER) {
-      __builtin_amdgcn_global_load_lds(skh + r.tk, (lds_void*)(lds + r.ks * G::KS + G::KSC), 4, 0, 0);
+      lds_dma4(skh + r.tk, 0u, lds_addr(lds + r.ks * G::KS + G::KSC));
       return;
     }
     const int u = chunk[i];
@@ -238,7 +237,7 @@ struct Ctx {
     const uint8_t* base = isk ? r.kt : r.vt;
     const uint32_t o = off[i];
     const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
-    __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
+    lds_dma16(base, o, lds_addr(lds + dst));
   }
   __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
     const Refill r = refill(tk, ks, tv, vs);
@@ -251,8 +250,8 @@ struct Ctx {
     for (int u = wave; u < G::KINST; u += WAVES) {
       const int q = u * 64 + lane;
       const int row = min(min(q / G::KROWC, KT - 1), kmax);
-      const uint8_t* src = kh + ((long long)t * KT + row) * D + min(q % G::KROWC, G::KCPR - 1) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + u * 1024), 16, 0, 0);
+      lds_dma16(kh + (long long)t * KT * D, (uint32_t)(row * D + min(q % G::KROWC, G::KCPR - 1) * 16),
+                lds_addr(lds + u * 1024));
     }
   }
   __device__ __forceinline__ float k_scale(int slot) const {

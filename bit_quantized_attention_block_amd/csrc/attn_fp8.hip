@@ -54,7 +54,6 @@ constexpr int NSLOT = 4;                          // LDS ring depth (tiles)
 constexpr float LOG2_448 = 8.80735492205760410f;  // log2(448)
 constexpr float REBASE = 16.0f;                   // lazy reference of O: at most 2^16 below the max
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 field layout:
 // vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
@@ -149,11 +148,11 @@ struct Ctx {
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (i == G::PER) {
-      __builtin_amdgcn_global_load_lds(skh + r.tk, (lds_void*)(lds + r.ks * G::KS + G::KSC), 4, 0, 0);
+      lds_dma4(skh + r.tk, 0u, lds_addr(lds + r.ks * G::KS + G::KSC));
       return;
     }
     if (i == G::PER + 1) {
-      __builtin_amdgcn_global_load_lds(svh + r.tv, (lds_void*)(lds + G::VBASE + r.vs * G::VS + G::VSC), 4, 0, 0);
+      lds_dma4(svh + r.tv, 0u, lds_addr(lds + G::VBASE + r.vs * G::VS + G::VSC));
       return;
     }
     const int u = chunk[i];
@@ -161,7 +160,7 @@ struct Ctx {
     const uint8_t* base = isk ? r.kt : r.vt;
     const uint32_t o = isk ? min(off[i], r.klim + (off[i] & (D - 1))) : off[i];
     const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
-    __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(lds + dst), 16, 0, 0);
+    lds_dma16(base, o, lds_addr(lds + dst));
   }
   __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
     const Refill r = refill(tk, ks, tv, vs);

@@ -31,6 +31,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Direct global -> LDS loads (global_load_lds), each lane's bytes at
+// sbase + voff to the LDS address lds_addr + 16 * lane (4 * lane for the
+// dword form); lds_addr and sbase are wave-uniform.  Issued from inline
+// assembly so that the compiler's LDS-wait bookkeeping is not disturbed: it
+// models the compiler-generated form as touching both wait counters and
+// then waits for every LDS read in flight at the next use of one.  These
+// loads have no register result; their completion is waited for explicitly
+// (vmcnt) by the kernels.  M0 carries the LDS address, so the kernels leave
+// M0 to these statements alone.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n s_nop 0\n global_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n s_nop 0\n global_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory");
+}
+// 32-bit LDS address of a pointer into the kernel's dynamic LDS
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 // Epilogue of the attention kernels: one query row of O = scale * O^T.  Lane
 // half g holds channels 32 cb + 8 i4 + 4 g + j in o[cb][4 i4 + j]; the row
 // goes out as fp32 or, with bf16, rounded to bf16.
