@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
     win[j] = 0;
   }
   bool bad = false;
+#pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(kh + (long long)r * D + cg * 8);
 #pragma unroll
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   }
 
   float amax = 0.0f;
+#pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
 #pragma unroll
@@ -160,6 +162,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   if (t == 0) scales[bh * nblk + blk] = (nanflag > 0.0f) ? __builtin_nanf("") : s;
   const bool zero = !(s > 0.0f) || (nanflag > 0.0f);
 
+#pragma unroll 2
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
     uint32_t packed[2] = {0u, 0u};
