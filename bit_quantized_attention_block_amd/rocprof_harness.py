@@ -1,10 +1,15 @@
 """rocprofv3 harness for the quantized-attention path on one MI355X.
 
-Three sub-commands:
+Sub-commands:
 
     python -m bit_quantized_attention_block_amd.rocprof_harness target   --workload W [--reps R]
     python -m bit_quantized_attention_block_amd.rocprof_harness collect  --workload W --out DIR
     python -m bit_quantized_attention_block_amd.rocprof_harness summarize --workload W --out DIR
+    python -m bit_quantized_attention_block_amd.rocprof_harness bench-trace --workload W --out DIR
+
+`bench-trace` runs rocprofv3 --kernel-trace --stats around bench.py itself and
+writes profiles/<kernel>_<workload>_bench_trace.md: the per-kernel durations of
+that run next to the HIP-event figures of its bench line.
 
 `target` is the profiled program: seeded inputs of the workload in HBM, then
 R x (quantize Q/K, pack V, attention kernel) and, for calibration, three
@@ -267,9 +272,71 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     return 0
 
 
+# ---------------------------------------------------------------------------
+# bench-trace: the kernel trace of bench.py itself
+# ---------------------------------------------------------------------------
+def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: int) -> int:
+    """rocprofv3 --kernel-trace --stats around `python3 bench.py` (the same
+    command that produces the bench line, without the CPU baseline), then
+    profiles/<kernel>_<workload>_bench_trace.md with the per-kernel durations
+    next to the bench line's own HIP-event figures from that run."""
+    sys.path.insert(0, ROOT)
+    import workloads as W
+
+    w = W.get(workload)
+    kname = ATTN_KERNEL[w.pv]
+    outdir = os.path.abspath(outdir)
+    os.makedirs(outdir, exist_ok=True)
+    env = dict(os.environ, TMPDIR="/tmp")
+    bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", w.name, "--steps", str(steps),
+             "--warmup", str(warmup), "--no-cpu-baseline"]
+    cmd = ["timeout", "-s", "KILL", "600", "rocprofv3", "--kernel-trace", "--stats", "-d",
+           os.path.join(outdir, "bench_trace"), "-o", "bench_trace", "--output-format", "csv", "--", *bench]
+    print(f"[bench-trace] {' '.join(shlex.quote(c) for c in cmd)}", flush=True)
+    with open(os.path.join(outdir, "bench_trace.json"), "w") as out, \
+            open(os.path.join(outdir, "bench_trace.log"), "w") as log:
+        rc = subprocess.call(cmd, cwd="/tmp", env=env, stdout=out, stderr=log)
+    print(f"[bench-trace] rc={rc}", flush=True)
+    if rc != 0:
+        return rc
+    with open(os.path.join(outdir, "bench_trace.json")) as f:
+        line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
+    res = json.loads(line)
+    stats = _rows(outdir, "bench_trace", "kernel_stats.csv")
+    is_attn = lambda n: n.split("(")[0].split("<")[0].endswith(kname)
+    rows = ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    attn = None
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        rows.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                    f"{float(r['Percentage']):.1f}% |")
+        if is_attn(r["Name"]):
+            attn = float(r["AverageNs"]) / 1e6
+    shown = " ".join(c if not c.startswith(ROOT) else c.replace(ROOT, ".") for c in bench)
+    lines = [f"# `{kname}` on {w.name}: kernel trace of the bench command", "",
+             f"Command (from /tmp with TMPDIR=/tmp): `rocprofv3 --kernel-trace --stats -d <out>/bench_trace "
+             f"-o bench_trace --output-format csv -- {shown}`, run by `python -m "
+             f"bit_quantized_attention_block_amd.rocprof_harness bench-trace --workload {w.name}`.", "",
+             "## Kernel durations (rocprofv3 --kernel-trace --stats)", ""] + rows + [""]
+    k_ev = res["roofline"]["avg_launch_ms"]
+    lines += [f"- attention kernel, rocprofv3 average over all its launches in the run: {attn:.4f} ms",
+              f"- attention kernel, the bench line's HIP-event average (same run): {k_ev:.4f} ms "
+              f"({100.0 * (attn - k_ev) / k_ev:+.2f}%)",
+              f"- forward (the bench line's `ms_per_step`): {res['ms_per_step']:.4f} ms, "
+              f"value {res['value']} {res['unit']}", "",
+              "Bench line of the traced run:", "", "```", line, "```"]
+    os.makedirs(profiles, exist_ok=True)
+    with open(os.path.join(profiles, f"{kname}_{w.name}_bench_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("cmd", choices=["target", "collect", "summarize"])
+    ap.add_argument("cmd", choices=["target", "collect", "summarize", "bench-trace"])
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-480p")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
@@ -280,6 +347,8 @@ def main(argv=None) -> int:
         return 0
     if a.cmd == "collect":
         return collect(a.workload, a.out, a.reps)
+    if a.cmd == "bench-trace":
+        return bench_trace(a.workload, a.out, a.profiles, a.steps, a.warmup)
     return summarize(a.workload, a.out, a.profiles)
 
 
