@@ -104,8 +104,8 @@ def main(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=None)
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path is per-head "
-              "independent, see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every head is "
+              "independent: heads would be split over GPUs with no communication)", file=sys.stderr)
         return 2
 
     import numpy as np
