@@ -20,6 +20,13 @@ paragraph; GVCLab research log 2026-09-02, section 5.5 table):
   attention.attend_fp8   the same with the kernel's online FP8 P rounding
                          mirrored, plus an ambiguity envelope
 
+and, for the W8A8 linear layers on either side of attention (jefxiong.cn
+"AIGC weekend special 5.10", section 1.2 item (4); digipub.cc TurboDiffusion
+article, linear-layer quantization paragraph):
+
+  w8a8.quantize_blocks   INT8 codes + one scale per 128x128 block
+  w8a8.linear            y = x W^T (+ b) from the block codes and scales
+
 Pins (what ties these functions to something other than themselves) live in
 ``tests/test_oracle_*.py``.  The end-to-end output against the pages is
 "parity unpinned": the pages print no numerical example of the attention
@@ -27,9 +34,9 @@ step; the quantized-vs-exact gap is reported as a diagnostic only.
 """
 from __future__ import annotations
 
-from . import attention, fp, quant  # noqa: F401
+from . import attention, fp, quant, w8a8  # noqa: F401
 
-__all__ = ["attention", "fp", "quant", "forward_head"]
+__all__ = ["attention", "fp", "quant", "w8a8", "forward_head"]
 
 
 def forward_head(q_bits, k_bits, v_bits, rows, q_block, k_block, scale, pv="bf16",
