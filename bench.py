@@ -3,6 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+With a W8A8 workload (--workload w8a8-qkv-wan14b-480p and the other w8a8-*
+names) it measures the block-wise INT8 linear layer instead; see bench_w8a8.
+
 One step is one full sqattn_forward over the workload: exact K mean, INT8
 quantization of Q and smoothed K, V packing (or E4M3 quantization), and the
 attention kernel, from bf16 Q/K/V resident in HBM to the fp32 output in HBM.
@@ -31,11 +34,14 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
 METRIC = "quantized-attention TOPS (4·B·H·N²·d/s) + % of MI355X INT8 MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+W8A8_METRIC = "W8A8 linear INT8 TOPS (2·M·N·K/s) + % of MI355X INT8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic.json")
 CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
 # the attention kernel source of each P.V path
 ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn_fp8.hip")}
 ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel"}
+W8A8_SRC = os.path.join(CSRC, "w8a8.hip")
+W8A8_KERNEL = "w8a8_gemm_kernel"
 
 
 def _sha(path):
@@ -43,17 +49,144 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _traffic(w):
-    """Per-launch HBM bytes of the attention kernel from the committed
-    counter summary, or None if absent or taken on another kernel source."""
+def _traffic(name, src):
+    """Per-launch HBM bytes of the workload's profiled kernel from the
+    committed counter summary, or None if absent or taken on another version
+    of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(w.name)
+            t = json.load(f).get(name)
     except (OSError, ValueError, AttributeError):
         return None
-    if not t or t.get("attn_sha256") != _sha(ATTN_SRC[w.pv]):
+    if not t or t.get("src_sha256") != _sha(src):
         return None
     return t.get("bytes_per_launch")
+
+
+def _timed(torch, np, dev, stream, fn, n):
+    """Average, median and minimum ms of n calls of fn, from HIP events on the
+    launch stream (one event after every call), and the wall time of the n
+    calls (launch to completion)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return ev[0].elapsed_time(ev[n]) / n, float(np.median(per)), min(per), wall
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline_w8a8(w, x, wt, b, row_blocks=64, w_rows=8192):
+    """Time the oracle on a sample of the layer: INT8 quantization of
+    `row_blocks` 128-row blocks of x and the block-scaled product of those rows
+    with the first `w_rows` rows of W (quantized by the oracle too, untimed:
+    the weights are quantized once, off the step), scaled to the whole layer."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    rows = min(w.M, 128 * row_blocks)
+    wr = min(w.N, w_rows)
+    cw, sw = oracle.w8a8.quantize_blocks(W.bf16_bits_to_f32(wt[:wr]))
+    t0 = time.perf_counter()
+    cx, sx = oracle.w8a8.quantize_blocks(W.bf16_bits_to_f32(x[:rows]))
+    t1 = time.perf_counter()
+    oracle.w8a8.linear(cx, sx, cw, sw, None if b is None else b[:wr])
+    t2 = time.perf_counter()
+    t_full = (t1 - t0) / rows * w.M + (t2 - t1) / (rows * wr) * (w.M * w.N)
+    return {"value": round(w.ops / t_full / 1e12, 6), "unit": "TOPS", "cores": int(_cores()), "kind": "oracle",
+            "sample": f"{rows} rows of x quantized ({t1 - t0:.1f} s) and multiplied with {wr} of the {w.N} rows "
+                      f"of W ({t2 - t1:.1f} s); scaled to {w.M} x {w.N} outputs",
+            "sample_seconds": round(t2 - t0, 2)}
+
+
+def bench_w8a8(a):
+    """One step = the W8A8 layer on bf16 activations in HBM: INT8 quantization
+    of x (128x128 blocks) and the block-scaled INT8 GEMM with bias, bf16
+    output; the weights are quantized once before timing, as a deployed
+    model stores them.  TOPS = 2*M*N*K / time."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_attention_block_amd as sq
+    from workloads import linear as WL
+
+    w = WL.get_linear(a.workload)
+    t0 = time.perf_counter()
+    x, wt, b = WL.gen_x(w), WL.gen_w(w), WL.gen_bias(w)
+    print(f"[bench] generated {w.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    to = lambda v: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+    X = to(x)
+    wc, ws = sq.w8a8_quantize(to(wt))
+    B = torch.from_numpy(b).to(dev) if b is not None else None
+    Y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(sq.w8a8_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sq.w8a8_linear(X, wc, ws, bias=B, out=Y, workspace=wsb)
+
+    for _ in range(a.warmup):
+        step()
+    ms, ms_med, ms_min, t_wall = _timed(torch, np, dev, stream, step, a.steps)
+    print(f"[bench] linear {ms:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f}; wall "
+          f"{t_wall / a.steps * 1e3:.3f}); torch {torch.__version__}, HIP {torch.version.hip}",
+          file=sys.stderr, flush=True)
+    xc, xs = sq.w8a8_quantize(X)
+
+    def kern():
+        sq.w8a8_gemm(xc, xs, wc, ws, bias=B, out=Y)
+
+    reps = a.kernel_reps or a.steps
+    for _ in range(2):
+        kern()
+    k_ms, k_med, k_min, _ = _timed(torch, np, dev, stream, kern, reps)
+    q_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_quantize(X), reps)[0]
+    tops = w.ops / (ms * 1e-3) / 1e12
+    k_tops = w.ops / (k_ms * 1e-3) / 1e12
+    res = {
+        "metric": W8A8_METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "block": 128, "bias": b is not None,
+                   "out": "bf16",
+                   "stages_ms": {"step_median": round(ms_med, 4), "step_min": round(ms_min, 4),
+                                 "gemm_kernel": round(k_ms, 4), "gemm_kernel_median": round(k_med, 4),
+                                 "gemm_kernel_min": round(k_min, 4), "quantize_x": round(q_ms, 4)}},
+        "roofline": {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
+                     "ops_per_launch": w.ops},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_w8a8(w, x, wt, b)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def cpu_baseline(w, q, k, v, rows, heads=10):
@@ -61,11 +194,7 @@ def cpu_baseline(w, q, k, v, rows, heads=10):
     its checked rows against all N keys) and scale to the whole workload."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores = _cores()
     t_quant = t_attn = 0.0
     nrows = 0
     for i in range(heads):
@@ -107,6 +236,8 @@ def main(argv=None):
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every head is "
               "independent: heads would be split over GPUs with no communication)", file=sys.stderr)
         return 2
+    if a.workload.startswith("w8a8-"):
+        return bench_w8a8(a)
 
     import numpy as np
     import torch
@@ -129,20 +260,7 @@ def main(argv=None):
         sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws)
 
     def timed(fn, n):
-        """Average, median and minimum ms of n calls of fn, from HIP events on
-        the launch stream (one event after every call), and the wall time of
-        the n calls (launch to completion)."""
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter()
-        ev[0].record(stream)
-        for i in range(n):
-            fn()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - wall
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
-        return ev[0].elapsed_time(ev[n]) / n, float(np.median(per)), min(per), wall
+        return _timed(torch, np, dev, stream, fn, n)
 
     for _ in range(a.warmup):
         step()
@@ -201,7 +319,7 @@ def main(argv=None):
                                  "attention_kernel_min": round(k_min, 4), "quantize_and_pack": round(p_ms, 4)}},
         "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": _traffic(w), "avg_launch_ms": round(k_ms, 4),
+                     "traffic": _traffic(w.name, ATTN_SRC[w.pv]), "avg_launch_ms": round(k_ms, 4),
                      "ops_per_launch": w.ops},
     }
     if not a.no_cpu_baseline:

@@ -17,7 +17,8 @@ import os
 
 __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "forward",
            "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
-           "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS"]
+           "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
+           "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -44,6 +45,10 @@ EXPORTS = {
     "sqattn_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_attend_quantized": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                      _vp]),
+    "sqattn_w8a8_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "sqattn_w8a8_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "sqattn_w8a8_workspace_bytes": (_sz, [_i, _i]),
+    "sqattn_w8a8_linear": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -255,4 +260,75 @@ def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale
     _check(lib().sqattn_attend_quantized(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_packed),
                                          _ptr(v_scale), B, H, N, d, float(scale), _PV[pv], ctypes.byref(o),
                                          _ptr(out), _stream(q_i8)))
+    return out
+
+
+# --------------------------------------------------------------------------- W8A8 linear
+
+def w8a8_quantize(x):
+    """bf16 [R, K] (K a multiple of 128) -> (int8 codes [R, K], float32
+    scales [ceil(R/128), K/128]), one scale per 128x128 block."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    R, C = (int(v) for v in x.shape)
+    codes = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    scales = torch.empty((-(-R // 128), C // 128 if C % 128 == 0 else 0), dtype=torch.float32, device=x.device)
+    _check(lib().sqattn_w8a8_quantize(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def _w8a8_shapes(x_shape, w_codes, w_scales, bias):
+    torch = _torch()
+    _dev(w_codes, "w_codes", torch.int8)
+    _dev(w_scales, "w_scales", torch.float32)
+    if w_codes.dim() != 2:
+        raise ValueError("w_codes must be [N, K]")
+    M, K = (int(v) for v in x_shape)
+    N, K2 = (int(v) for v in w_codes.shape)
+    if K != K2:
+        raise ValueError(f"x has K = {K}, w_codes has K = {K2}")
+    if K % 128 == 0 and tuple(w_scales.shape) != (-(-N // 128), K // 128):
+        raise ValueError("w_scales must be [ceil(N/128), K/128]")
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+        if tuple(bias.shape) != (N,):
+            raise ValueError("bias must be [N]")
+    return M, N, K
+
+
+def w8a8_gemm(x_codes, x_scales, w_codes, w_scales, bias=None, out=None, out_dtype=None):
+    """y = x W^T (+ bias) from block codes and scales (see w8a8_quantize):
+    [M, N] fp32, or bf16 (out_dtype=torch.bfloat16 or a bf16 `out`)."""
+    torch = _torch()
+    _dev(x_codes, "x_codes", torch.int8)
+    _dev(x_scales, "x_scales", torch.float32)
+    if x_codes.dim() != 2:
+        raise ValueError("x_codes must be [M, K]")
+    M, N, K = _w8a8_shapes(x_codes.shape, w_codes, w_scales, bias)
+    if K % 128 == 0 and tuple(x_scales.shape) != (-(-M // 128), K // 128):
+        raise ValueError("x_scales must be [ceil(M/128), K/128]")
+    out, od = _out(out, (M, N), x_codes.device, out_dtype)
+    _check(lib().sqattn_w8a8_gemm(_ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scales), _ptr(bias),
+                                  M, N, K, od, _ptr(out), _stream(x_codes)))
+    return out
+
+
+def w8a8_workspace_bytes(M, K) -> int:
+    return int(lib().sqattn_w8a8_workspace_bytes(M, K))
+
+
+def w8a8_linear(x, w_codes, w_scales, bias=None, out=None, out_dtype=None, workspace=None):
+    """The W8A8 layer on bf16 activations x [M, K] and pre-quantized weights
+    (w8a8_quantize of W [N, K]): quantizes x, then the block-scaled GEMM."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, N, K = _w8a8_shapes(x.shape, w_codes, w_scales, bias)
+    out, od = _out(out, (M, N), x.device, out_dtype)
+    w, wb = _ws(w8a8_workspace_bytes(M, K), x.device, workspace)
+    _check(lib().sqattn_w8a8_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(bias), M, N, K, od, _ptr(out),
+                                    _ptr(w), wb, _stream(x)))
     return out

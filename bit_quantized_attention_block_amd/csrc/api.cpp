@@ -166,6 +166,28 @@ int validate_forward(const void* q, const void* k, const void* v, int B, int H, 
   return SQATTN_OK;
 }
 
+// W8A8 sizes: K a positive multiple of 128 up to 2^20, 0 <= rows <= 65535*128.
+int check_w8a8_rows(int rows, const char* name) {
+  if (rows < 0) return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " must be >= 0");
+  if (rows > 65535 * 128) return fail(SQATTN_ERR_RANGE, std::string(name) + " must be at most 65535*128");
+  return SQATTN_OK;
+}
+
+int check_w8a8_k(int K) {
+  if (K < 128 || (K % 128) != 0)
+    return fail(SQATTN_ERR_INVALID_ARG, "K (columns) must be a positive multiple of 128");
+  if (K > (1 << 20)) return fail(SQATTN_ERR_RANGE, "K (columns) must be at most 2^20");
+  return SQATTN_OK;
+}
+
+int check_out_dtype(int out_dtype) {
+  if (out_dtype != SQATTN_OUT_FP32 && out_dtype != SQATTN_OUT_BF16)
+    return fail(SQATTN_ERR_INVALID_ARG, "out_dtype must be SQATTN_OUT_FP32 or SQATTN_OUT_BF16");
+  return SQATTN_OK;
+}
+
+size_t w8a8_scale_bytes(long long rows, long long K) { return (size_t)(((rows + 127) / 128) * (K / 128)) * 4; }
+
 }  // namespace
 
 extern "C" {
@@ -356,6 +378,67 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
   p.scale_log2e = scale * kLog2e;
   sqattn::launch_attention(p, d, pv_dtype, (hipStream_t)stream);
   return hip_check("sqattn_attend_quantized launch");
+}
+
+int sqattn_w8a8_quantize(const void* x, int rows, int cols, int8_t* codes, float* scales, void* stream) {
+  g_err.clear();
+  int s;
+  if ((s = check_w8a8_rows(rows, "rows")) || (s = check_w8a8_k(cols))) return s;
+  if (rows == 0) return SQATTN_OK;  // empty: pointers are not inspected
+  if ((s = check_ptr(x, "x", 16)) || (s = check_ptr(codes, "codes", 16)) || (s = check_ptr(scales, "scales", 4)))
+    return s;
+  sqattn::launch_w8a8_quant((const uint16_t*)x, rows, cols, codes, scales, (hipStream_t)stream);
+  return hip_check("sqattn_w8a8_quantize launch");
+}
+
+int sqattn_w8a8_gemm(const int8_t* x_codes, const float* x_scales, const int8_t* w_codes, const float* w_scales,
+                     const float* bias, int M, int N, int K, int out_dtype, void* out, void* stream) {
+  g_err.clear();
+  int s;
+  if ((s = check_w8a8_rows(M, "M")) || (s = check_w8a8_rows(N, "N")) || (s = check_w8a8_k(K)) ||
+      (s = check_out_dtype(out_dtype)))
+    return s;
+  if (M == 0 || N == 0) return SQATTN_OK;  // empty: pointers are not inspected
+  if ((s = check_ptr(x_codes, "x_codes", 16)) || (s = check_ptr(w_codes, "w_codes", 16)) ||
+      (s = check_ptr(x_scales, "x_scales", 4)) || (s = check_ptr(w_scales, "w_scales", 4)) ||
+      (s = check_ptr(out, "out", 16)))
+    return s;
+  if (bias && (s = check_ptr(bias, "bias", 4))) return s;
+  sqattn::launch_w8a8_gemm(x_codes, x_scales, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16,
+                           (hipStream_t)stream);
+  return hip_check("sqattn_w8a8_gemm launch");
+}
+
+size_t sqattn_w8a8_workspace_bytes(int M, int K) {
+  std::string keep = g_err;
+  if (check_w8a8_rows(M, "M") || check_w8a8_k(K)) {
+    g_err = keep;
+    return 0;
+  }
+  return align_up((size_t)M * K) + align_up(w8a8_scale_bytes(M, K));
+}
+
+int sqattn_w8a8_linear(const void* x, const int8_t* w_codes, const float* w_scales, const float* bias, int M, int N,
+                       int K, int out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int s;
+  if ((s = check_w8a8_rows(M, "M")) || (s = check_w8a8_rows(N, "N")) || (s = check_w8a8_k(K)) ||
+      (s = check_out_dtype(out_dtype)))
+    return s;
+  if (M == 0 || N == 0) return SQATTN_OK;  // empty: pointers are not inspected
+  if ((s = check_ptr(x, "x", 16)) || (s = check_ptr(w_codes, "w_codes", 16)) ||
+      (s = check_ptr(w_scales, "w_scales", 4)) || (s = check_ptr(out, "out", 16)))
+    return s;
+  if (bias && (s = check_ptr(bias, "bias", 4))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  const size_t codes_bytes = align_up((size_t)M * K);
+  if ((s = ws.acquire(workspace, workspace_bytes, codes_bytes + align_up(w8a8_scale_bytes(M, K)), st))) return s;
+  int8_t* xc = ws.at<int8_t>(0);
+  float* xs = ws.at<float>(codes_bytes);
+  sqattn::launch_w8a8_quant((const uint16_t*)x, M, K, xc, xs, st);
+  sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st);
+  return hip_check("sqattn_w8a8_linear launch");
 }
 
 }  // extern "C"

@@ -35,4 +35,9 @@ void launch_attention_bf16(const AttnParams& p, int d, hipStream_t st);
 // FP8 P.V kernel (software-pipelined, running max per tile); same requirements.
 void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 
+// W8A8 linear layer: 128x128 block quantizer and the block-scaled INT8 GEMM.
+void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* scales, hipStream_t st);
+void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
+                      int M, int N, int K, void* out, int out_bf16, hipStream_t st);
+
 }  // namespace sqattn

@@ -1,4 +1,5 @@
-"""rocprofv3 harness for the quantized-attention path on one MI355X.
+"""rocprofv3 harness for the sqattn kernels on one MI355X: the attention
+kernels (attention workloads) and the W8A8 GEMM (workloads named w8a8-*).
 
 Sub-commands:
 
@@ -12,8 +13,10 @@ writes profiles/<kernel>_<workload>_bench_trace.md: the per-kernel durations of
 that run next to the HIP-event figures of its bench line.
 
 `target` is the profiled program: seeded inputs of the workload in HBM, then
-R x (quantize Q/K, pack V, attention kernel) and, for calibration, three
-device copies of a 1 GiB buffer (a plain read + write of known size).
+R x (quantize Q/K, pack V, attention kernel) -- or, for a W8A8 workload, R x
+(quantize x, block-scaled GEMM) on pre-quantized weights -- and, for
+calibration, three device copies of a 1 GiB buffer (a plain read + write of
+known size).
 
 `collect` runs `target` under rocprofv3 in separate passes: kernel trace with
 statistics, FETCH_SIZE, WRITE_SIZE, and the shader counters of MFMA
@@ -24,7 +27,7 @@ only counters that fit one run).
 `summarize` turns the CSV output into
   profiles/<kernel>_<workload>_profile.md  kernel durations (rocprofv3 --stats),
                                            HBM bytes and MFMA busy per launch
-  profiles/attn_traffic.json               per-launch HBM bytes of the attention
+  profiles/kernel_traffic.json             per-launch HBM bytes of the profiled
                                            kernel, keyed by workload, with the
                                            sha256 of the kernel source it was
                                            measured on.
@@ -50,6 +53,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_quantized_attention_block_amd", "csrc")
 ATTN_SRC = {"bf16": os.path.join(CSRC, "attn_bf16.hip"), "fp8": os.path.join(CSRC, "attn_fp8.hip")}
 ATTN_KERNEL = {"bf16": "attn_bf16_kernel", "fp8": "attn_fp8_kernel"}
+W8A8_SRC = os.path.join(CSRC, "w8a8.hip")
+W8A8_KERNEL = "w8a8_gemm_kernel"
+
+
+def spec(workload: str) -> dict:
+    """The profiled kernel of a workload: name, source, operation count, title."""
+    sys.path.insert(0, ROOT)
+    if workload.startswith("w8a8-"):
+        from workloads import linear as WL
+        w = WL.get_linear(workload)
+        return {"w": w, "kind": "w8a8", "kernel": W8A8_KERNEL, "src": W8A8_SRC, "ops": w.ops,
+                "ops_text": "2 M N K", "title": f"{w.name} (M={w.M}, N={w.N}, K={w.K}, bf16 output, bias)"}
+    import workloads as W
+    w = W.get(workload)
+    return {"w": w, "kind": "attn", "kernel": ATTN_KERNEL[w.pv], "src": ATTN_SRC[w.pv], "ops": w.ops,
+            "ops_text": "4 B H N^2 d", "title": f"{w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})"}
 COPY_BYTES = 1 << 30
 COPY_REPS = 3
 
@@ -73,22 +92,36 @@ def run_target(workload: str, reps: int) -> None:
     import bit_quantized_attention_block_amd as sq
     import workloads as W
 
-    w = W.get(workload)
-    q, k, v, _ = W.gen_inputs(w)
+    sp = spec(workload)
+    w = sp["w"]
     dev = torch.device("cuda:0")
     to = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-    Q, K, V = to(q), to(k), to(v)
-    out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
-    for _ in range(reps):
-        qi, qs, ki, ks, _mu = sq.quantize_qk(Q, K, w.q_block, w.k_block)
-        if w.pv == "fp8":
-            vc, vs = sq.quantize_v_fp8(V)
-            vp = sq.pack_v(vc, "fp8")
-        else:
-            vs, vp = None, sq.pack_v(V, "bf16")
-        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
-        torch.cuda.synchronize()
-        print(f"[target] {w.name}: rep done", flush=True)
+    if sp["kind"] == "w8a8":
+        from workloads import linear as WL
+        X, Wt = to(WL.gen_x(w)), to(WL.gen_w(w))
+        bias = torch.from_numpy(WL.gen_bias(w)).to(dev)
+        wc, ws = sq.w8a8_quantize(Wt)
+        del Wt
+        y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        for _ in range(reps):
+            xc, xs = sq.w8a8_quantize(X)
+            sq.w8a8_gemm(xc, xs, wc, ws, bias=bias, out=y)
+            torch.cuda.synchronize()
+            print(f"[target] {w.name}: rep done", flush=True)
+    else:
+        q, k, v, _ = W.gen_inputs(w)
+        Q, K, V = to(q), to(k), to(v)
+        out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        for _ in range(reps):
+            qi, qs, ki, ks, _mu = sq.quantize_qk(Q, K, w.q_block, w.k_block)
+            if w.pv == "fp8":
+                vc, vs = sq.quantize_v_fp8(V)
+                vp = sq.pack_v(vc, "fp8")
+            else:
+                vs, vp = None, sq.pack_v(V, "bf16")
+            sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+            torch.cuda.synchronize()
+            print(f"[target] {w.name}: rep done", flush=True)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(COPY_REPS):
@@ -169,11 +202,9 @@ def _sha(path):
 
 
 def summarize(workload: str, outdir: str, profiles: str) -> int:
-    sys.path.insert(0, ROOT)
-    import workloads as W
-
-    w = W.get(workload)
-    kname = ATTN_KERNEL[w.pv]
+    sp = spec(workload)
+    w = sp["w"]
+    kname = sp["kernel"]
     is_attn = lambda n: n.split("(")[0].split("<")[0].endswith(kname)
     is_copy = lambda n: "copybuffer" in n.lower()  # the device-to-device copy of torch copy_
     with open(os.path.join(outdir, "commands.json")) as f:
@@ -218,8 +249,8 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
         v, _ = _mean_for(_per_dispatch(grbm, c), is_attn)
         sq_vals[c] = v
 
-    ops = w.ops
-    lines = [f"# `{kname}` on {w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})", "",
+    ops = sp["ops"]
+    lines = [f"# `{kname}` on {sp['title']}", "",
              f"Made by `python -m bit_quantized_attention_block_amd.rocprof_harness collect --workload {w.name} "
              f"--out <out>` on one MI355X, which runs these passes from /tmp with TMPDIR=/tmp and the "
              f"repository root on PYTHONPATH:", ""]
@@ -233,19 +264,19 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
                   f"--workload {w.name} --out <dir>`.", "",
               "## Kernel durations (rocprofv3 --kernel-trace --stats)", ""] + stat_lines
     if attn_avg_ns:
-        lines += ["", f"Attention kernel average: {attn_avg_ns / 1e6:.3f} ms -> "
-                      f"{ops / (attn_avg_ns * 1e-9) / 1e12:.1f} TOPS (4 B H N^2 d / t)."]
-    lines += ["", "## HBM traffic per attention launch (TCC FETCH_SIZE / WRITE_SIZE)", "",
+        lines += ["", f"`{kname}` average: {attn_avg_ns / 1e6:.3f} ms -> "
+                      f"{ops / (attn_avg_ns * 1e-9) / 1e12:.1f} TOPS ({sp['ops_text']} / t)."]
+    lines += ["", f"## HBM traffic per `{kname}` launch (TCC FETCH_SIZE / WRITE_SIZE)", "",
               f"- calibration: device copy of {COPY_BYTES} bytes, {n_copy} dispatches; FETCH_SIZE reads "
               f"{f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per copy -> scale {f_scale:.4f} (read), "
               f"{w_scale:.4f} (write)",
-              f"- attention ({n_attn} dispatches): FETCH_SIZE {f_attn:.0f} KiB, WRITE_SIZE {w_attn:.0f} KiB",
+              f"- `{kname}` ({n_attn} dispatches): FETCH_SIZE {f_attn:.0f} KiB, WRITE_SIZE {w_attn:.0f} KiB",
               f"- scaled: read {read_b / 1e9:.3f} GB, write {write_b / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB "
               f"per launch"]
     if attn_avg_ns:
         lines += [f"- at the traced average duration: {traffic / (attn_avg_ns * 1e-9) / 1e9:.0f} GB/s "
                   f"(HBM peak 8000 GB/s)"]
-    lines += ["", "## Shader counters per attention launch (sums over the device)", ""]
+    lines += ["", f"## Shader counters per `{kname}` launch (sums over the device)", ""]
     for c, v in sq_vals.items():
         lines += [f"- {c}: {v:.4g}" if v is not None else f"- {c}: n/a"]
     if sq_vals.get("SQ_VALU_MFMA_BUSY_CYCLES") and sq_vals.get("SQ_BUSY_CYCLES"):
@@ -256,13 +287,13 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     stem = f"{kname}_{w.name}"
     with open(os.path.join(profiles, stem + "_profile.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    tf = os.path.join(profiles, "attn_traffic.json")
+    tf = os.path.join(profiles, "kernel_traffic.json")
     try:
         with open(tf) as f:
             allt = json.load(f)
     except (OSError, ValueError):
         allt = {}
-    allt[w.name] = {"kernel": kname, "attn_sha256": _sha(ATTN_SRC[w.pv]), "bytes_per_launch": round(traffic),
+    allt[w.name] = {"kernel": kname, "src_sha256": _sha(sp["src"]), "bytes_per_launch": round(traffic),
                     "read_bytes": round(read_b), "write_bytes": round(write_b),
                     "fetch_kib": f_attn, "write_kib": w_attn, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
                     "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns}
@@ -280,11 +311,9 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
     command that produces the bench line, without the CPU baseline), then
     profiles/<kernel>_<workload>_bench_trace.md with the per-kernel durations
     next to the bench line's own HIP-event figures from that run."""
-    sys.path.insert(0, ROOT)
-    import workloads as W
-
-    w = W.get(workload)
-    kname = ATTN_KERNEL[w.pv]
+    sp = spec(workload)
+    w = sp["w"]
+    kname = sp["kernel"]
     outdir = os.path.abspath(outdir)
     os.makedirs(outdir, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
@@ -319,10 +348,10 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
              f"bit_quantized_attention_block_amd.rocprof_harness bench-trace --workload {w.name}`.", "",
              "## Kernel durations (rocprofv3 --kernel-trace --stats)", ""] + rows + [""]
     k_ev = res["roofline"]["avg_launch_ms"]
-    lines += [f"- attention kernel, rocprofv3 average over all its launches in the run: {attn:.4f} ms",
-              f"- attention kernel, the bench line's HIP-event average (same run): {k_ev:.4f} ms "
+    lines += [f"- `{kname}`, rocprofv3 average over all its launches in the run: {attn:.4f} ms",
+              f"- `{kname}`, the bench line's HIP-event average (same run): {k_ev:.4f} ms "
               f"({100.0 * (attn - k_ev) / k_ev:+.2f}%)",
-              f"- forward (the bench line's `ms_per_step`): {res['ms_per_step']:.4f} ms, "
+              f"- one step (the bench line's `ms_per_step`): {res['ms_per_step']:.4f} ms, "
               f"value {res['value']} {res['unit']}", "",
               "Bench line of the traced run:", "", "```", line, "```"]
     os.makedirs(profiles, exist_ok=True)

@@ -192,6 +192,58 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
                             int B, int H, int N, int d, float scale, int pv_dtype,
                             const sqattn_opts* opts, void* out, void* stream);
 
+/*
+ * W8A8 block-wise INT8 linear layer, y = x W^T (+ b): the projections on
+ * either side of attention with weights and activations both quantized to
+ * INT8 in 128x128 blocks and the products on the INT8 matrix units
+ * (jefxiong.cn "AIGC weekend special 5.10", section 1.2 item (4), W8A8;
+ * digipub.cc TurboDiffusion article, linear-layer quantization paragraph).
+ *
+ * Layout (all row-major, device pointers, 16-byte aligned):
+ *   x  : [M, K] activations (tokens x in-features), bf16 bits.
+ *   W  : [N, K] weights (out-features x in-features), the nn.Linear layout.
+ *   codes of a [R, K] matrix : int8 [R, K];  scales : float32
+ *        [ceil(R/128), K/128], scale (i, j) for rows [128i, min(R, 128i+128))
+ *        and columns [128j, 128j+128).
+ *   b  : float32 [N] or NULL;  y : [M, N], fp32 or bf16 (out_dtype).
+ * K must be a positive multiple of 128 (the block edge) and at most 2^20;
+ * M and N may be 0: then nothing is enqueued and the data pointers are not
+ * inspected (they may be NULL); M, N <= 65535 * 128.
+ * Inputs must be finite (the result for Inf or NaN inputs is unspecified).
+ *
+ * Numerics: scale s = fl32(absmax / 127) per block (0 for an all-zero block),
+ * code = clamp(rne(fl32(v / s)), -127, 127), as for the attention's Q/K
+ * blocks.  For each 128-wide slice j of K the exact int32 partial
+ * D_j[m, n] = sum over the slice of cx[m, k] * cw[n, k] is scaled by
+ * fl32(sx[m/128, j] * sw[n/128, j]) and added to an fp32 accumulator with
+ * one fused multiply-add per slice, in increasing j; then b[n] is added and
+ * the sum is stored as fp32 or rounded to nearest-even bf16.
+ */
+
+/* Quantize a bf16 [rows, cols] matrix (x or W) to INT8 codes and 128x128
+ * block scales.  cols: positive multiple of 128, <= 2^20;
+ * 0 <= rows <= 65535 * 128. */
+int sqattn_w8a8_quantize(const void* x, int rows, int cols, int8_t* codes, float* scales,
+                         void* stream);
+
+/* y = x W^T (+ b) from codes and scales written by sqattn_w8a8_quantize.
+ *   bias      : float32 [N] or NULL.
+ *   out_dtype : SQATTN_OUT_FP32 or SQATTN_OUT_BF16. */
+int sqattn_w8a8_gemm(const int8_t* x_codes, const float* x_scales, const int8_t* w_codes,
+                     const float* w_scales, const float* bias, int M, int N, int K, int out_dtype,
+                     void* out, void* stream);
+
+/* Bytes of workspace sqattn_w8a8_linear needs (codes and scales of x).
+ * 0 for invalid sizes. */
+size_t sqattn_w8a8_workspace_bytes(int M, int K);
+
+/* The layer on bf16 activations and pre-quantized weights: quantizes x into
+ * the workspace, then sqattn_w8a8_gemm.  workspace: >= sqattn_w8a8_workspace_bytes()
+ * bytes, 256-byte aligned, or NULL for a stream-ordered allocation. */
+int sqattn_w8a8_linear(const void* x, const int8_t* w_codes, const float* w_scales,
+                       const float* bias, int M, int N, int K, int out_dtype, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

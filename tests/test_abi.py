@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 16
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -155,3 +155,69 @@ def test_binding_rejects_non_gpu_tensors():
         sq.forward(q, q, q)
     with pytest.raises(TypeError, match="torch.Tensor"):
         sq.quantize_qk([1.0], q)
+
+
+def _gemm(xc=FAKE, xs=FAKE, wc=FAKE, ws=FAKE, bias=None, M=300, N=200, K=384, od=0, out=FAKE):
+    return sq.lib().sqattn_w8a8_gemm(xc, xs, wc, ws, bias, M, N, K, od, out, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(xc=None), INVALID, "x_codes is NULL"),
+    (dict(ws=None), INVALID, "w_scales is NULL"),
+    (dict(out=FAKE + 8), INVALID, "aligned"),
+    (dict(bias=FAKE + 2), INVALID, "bias"),
+    (dict(K=100), INVALID, "multiple of 128"),
+    (dict(K=0), INVALID, "multiple of 128"),
+    (dict(K=-128), INVALID, "multiple of 128"),
+    (dict(K=(1 << 20) + 128), RANGE, "2^20"),
+    (dict(M=-1), INVALID, "M must be >= 0"),
+    (dict(N=-5), INVALID, "N must be >= 0"),
+    (dict(M=65535 * 128 + 1), RANGE, "65535*128"),
+    (dict(od=2), INVALID, "out_dtype"),
+    (dict(od=-1), INVALID, "out_dtype"),
+])
+def test_w8a8_gemm_validation(kw, code, needle):
+    assert _gemm(**kw) == code
+    assert needle in _err()
+
+
+def test_w8a8_empty_shapes_enqueue_nothing():
+    # M = 0 or N = 0 is a valid empty product: OK without touching the GPU
+    assert _gemm(M=0) == OK
+    assert _gemm(N=0) == OK
+    L = sq.lib()
+    assert L.sqattn_w8a8_quantize(FAKE, 0, 256, FAKE, FAKE, None) == OK
+    assert L.sqattn_w8a8_linear(FAKE, FAKE, FAKE, None, 0, 64, 256, 0, FAKE, None, 0, None) == OK
+    # and the pointers of an empty product are not inspected
+    assert L.sqattn_w8a8_linear(None, None, None, None, 0, 64, 256, 0, None, None, 0, None) == OK
+    assert L.sqattn_w8a8_gemm(None, None, None, None, None, 5, 0, 128, 0, None, None) == OK
+    assert L.sqattn_w8a8_quantize(None, 0, 128, None, None, None) == OK
+    # sizes are still validated
+    assert L.sqattn_w8a8_linear(None, None, None, None, 0, 64, 100, 0, None, None, 0, None) == INVALID
+
+
+def test_w8a8_quantize_and_linear_validation():
+    L = sq.lib()
+    assert L.sqattn_w8a8_quantize(FAKE, 10, 200, FAKE, FAKE, None) == INVALID and "128" in _err()
+    assert L.sqattn_w8a8_quantize(FAKE + 2, 10, 256, FAKE, FAKE, None) == INVALID and "x is not" in _err()
+    assert L.sqattn_w8a8_quantize(FAKE, 10, 256, FAKE, None, None) == INVALID and "scales" in _err()
+    assert L.sqattn_w8a8_quantize(FAKE, -1, 256, FAKE, FAKE, None) == INVALID
+    lin = [FAKE, FAKE, FAKE, None, 300, 200, 384, 0, FAKE, FAKE, 1, None]
+    assert L.sqattn_w8a8_linear(*lin) == WORKSPACE and "needed" in _err()
+    a = list(lin)
+    a[9] = FAKE + 16
+    a[10] = BIG
+    assert L.sqattn_w8a8_linear(*a) == INVALID and "256-byte" in _err()
+    a = list(lin)
+    a[6] = 130
+    assert L.sqattn_w8a8_linear(*a) == INVALID
+
+
+def test_w8a8_workspace_bytes():
+    L = sq.lib()
+    M, K = 32760, 5120
+    need = L.sqattn_w8a8_workspace_bytes(M, K)
+    assert need >= M * K + (-(-M // 128)) * (K // 128) * 4 and need % 256 == 0
+    assert L.sqattn_w8a8_workspace_bytes(M, 100) == 0
+    assert L.sqattn_w8a8_workspace_bytes(-1, K) == 0
+    assert L.sqattn_w8a8_workspace_bytes(0, K) == 0 or L.sqattn_w8a8_workspace_bytes(0, K) < 1024
