@@ -98,6 +98,8 @@ constexpr int LDS_BYTES = SCB + 2 * 4 * 64 * 4;  // 149504 bytes
 constexpr int INST = GT * ROWC / 64;     // 1 KB direct loads per tile (36)
 constexpr int PER = 2 * INST / WAVES;    // per wave per slice (9)
 constexpr int GROUP = 8;                 // M tiles per group of the tile order
+constexpr int OUT_STRIDE = GT + 8;       // bf16 elements per staged output row (528 bytes)
+static_assert(GT * OUT_STRIDE * 2 <= 2 * SLOTB, "the staged output tile must fit in the ring");
 static_assert(2 * INST % WAVES == 0, "loads must split evenly over the waves");
 
 struct GemmParams {
@@ -229,23 +231,57 @@ __global__ __launch_bounds__(NTHR) void w8a8_gemm_kernel(GemmParams p) {
   }
 
   // epilogue: lane holds column l%32 of each 32x32 tile, rows 8(i/4)+4g+i%4
+  const bool full = (m0 + GT <= p.M) && (n0 + GT <= p.N);
+  float bcol[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int col = n0 + wn * 64 + n * 32 + (lane & 31);
-    if (col >= p.N) continue;
-    const float b = p.bias ? p.bias[col] : 0.0f;
+    bcol[n] = (p.bias && col < p.N) ? p.bias[col] : 0.0f;
+  }
+  if (p.out_bf16) {
+    // The bf16 tile goes through LDS (free once every wave is past the last
+    // slice) so that it leaves in 16-byte pieces along whole rows.
+    __syncthreads();
+    uint16_t* st = (uint16_t*)lds;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * 128 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const int c = wn * 64 + n * 32 + (lane & 31);
+          const __bf16 v = (__bf16)(acc[m][n][i] + bcol[n]);
+          st[r * OUT_STRIDE + c] = __builtin_bit_cast(uint16_t, v);
+        }
+    __syncthreads();
+    const bool vec = (p.N & 7) == 0;  // rows start 16-byte aligned
+    const int piece = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+#pragma unroll 4
+    for (int r = r0; r < GT; r += NTHR / 32) {
+      const int row = m0 + r, col = n0 + piece * 8;
+      if (row >= p.M) break;
+      const v4i v = *(const v4i*)(st + r * OUT_STRIDE + piece * 8);
+      uint16_t* dst = (uint16_t*)p.out + (long long)row * p.N + col;
+      if (vec && (full || col + 8 <= p.N)) {
+        *(v4i*)dst = v;
+      } else {
+        for (int e = 0; e < 8 && col + e < p.N; ++e) dst[e] = (uint16_t)(((uint32_t)v[e >> 1]) >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int col = n0 + wn * 64 + n * 32 + (lane & 31);
+    if (!full && col >= p.N) continue;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = m0 + wm * 128 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (row >= p.M) continue;
-        const float v = acc[m][n][i] + b;
-        const long long o = (long long)row * p.N + col;
-        if (p.out_bf16)
-          ((__bf16*)p.out)[o] = (__bf16)v;
-        else
-          ((float*)p.out)[o] = v;
+        if (!full && row >= p.M) continue;
+        ((float*)p.out)[(long long)row * p.N + col] = acc[m][n][i] + bcol[n];
       }
   }
 }

@@ -196,6 +196,12 @@ def _mean_for(d, match):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
+def _short(name: str) -> str:
+    """Kernel name without namespaces' "(anonymous namespace)" part, argument
+    list or template arguments."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
+
+
 def _sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -205,7 +211,7 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     sp = spec(workload)
     w = sp["w"]
     kname = sp["kernel"]
-    is_attn = lambda n: n.split("(")[0].split("<")[0].endswith(kname)
+    is_attn = lambda n: _short(n).endswith(kname)
     is_copy = lambda n: "copybuffer" in n.lower()  # the device-to-device copy of torch copy_
     with open(os.path.join(outdir, "commands.json")) as f:
         meta = json.load(f)
@@ -216,7 +222,7 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     attn_avg_ns = None
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"]
-        short = name.split("(")[0]
+        short = _short(name)
         stat_lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                           f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                           f"{float(r['Percentage']):.1f}% |")
@@ -332,11 +338,11 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
         line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
     res = json.loads(line)
     stats = _rows(outdir, "bench_trace", "kernel_stats.csv")
-    is_attn = lambda n: n.split("(")[0].split("<")[0].endswith(kname)
+    is_attn = lambda n: _short(n).endswith(kname)
     rows = ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     attn = None
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        rows.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        rows.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                     f"{float(r['Percentage']):.1f}% |")
         if is_attn(r["Name"]):

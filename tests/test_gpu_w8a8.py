@@ -104,6 +104,8 @@ def test_quantize_bit_exact(R, C, kind):
     (256, 256, 128, False, "fp32"),
     (300, 300, 8960, True, "fp32"),     # 70 slices: crosses the 64-slice scale staging
     (64, 96, 16512, True, "bf16"),      # 129 slices
+    (200, 203, 256, True, "bf16"),      # rows not 16-byte aligned: element-wise tail stores
+    (520, 264, 384, False, "bf16"),     # ragged in both, vector stores
 ])
 def test_gemm_parity(M, N, K, bias, out):
     print(f"case gemm M={M} N={N} K={K} bias={bias} out={out}", flush=True)
