@@ -19,6 +19,8 @@ paragraph; GVCLab research log 2026-09-02, section 5.5 table):
   attention.attend_bf16  logits from the integer codes, exact softmax, P.V
   attention.attend_fp8   the same with the kernel's online FP8 P rounding
                          mirrored, plus an ambiguity envelope
+  (both take an optional block mask: block-sparse attention over
+  128-row x 64-key blocks)
 
 and, for the W8A8 linear layers on either side of attention (jefxiong.cn
 "AIGC weekend special 5.10", section 1.2 item (4); digipub.cc TurboDiffusion
@@ -40,21 +42,23 @@ __all__ = ["attention", "fp", "quant", "w8a8", "forward_head"]
 
 
 def forward_head(q_bits, k_bits, v_bits, rows, q_block, k_block, scale, pv="bf16",
-                 v_block=64, kv_tile=64):
+                 v_block=64, kv_tile=64, block_mask=None):
     """Run every step for one head; returns a dict of all intermediate results.
 
-    q_bits/k_bits/v_bits: uint16 bf16 bits [N, d]; rows: checked query rows."""
+    q_bits/k_bits/v_bits: uint16 bf16 bits [N, d]; rows: checked query rows;
+    block_mask: optional [ceil(N/128), ceil(N/64)] block-sparse mask."""
     qc, qs = quant.quantize_q(q_bits, q_block)
     kc, ks, mu = quant.quantize_k(k_bits, k_block)
     res = {"q_codes": qc, "q_scale": qs, "k_codes": kc, "k_scale": ks, "k_mean": mu}
     if pv == "bf16":
-        res["out"] = attention.attend_bf16(qc, qs, kc, ks, v_bits, rows, q_block, k_block, scale)
+        res["out"] = attention.attend_bf16(qc, qs, kc, ks, v_bits, rows, q_block, k_block, scale,
+                                           block_mask=block_mask)
         res["envelope"] = None
     elif pv == "fp8":
         vc, vs = quant.quantize_v_fp8(v_bits, v_block)
         res["v_codes"], res["v_scale"] = vc, vs
         o, e, hits = attention.attend_fp8(qc, qs, kc, ks, vc, vs, rows, q_block, k_block, scale,
-                                          v_block=v_block, kv_tile=kv_tile)
+                                          v_block=v_block, kv_tile=kv_tile, block_mask=block_mask)
         res["out"], res["envelope"], res["envelope_hits"] = o, e, hits
     else:
         raise ValueError(pv)

@@ -16,6 +16,12 @@ Readings where the pages are silent:
   * 16-bit P.V: exact two-pass softmax in float64 with V the exact bf16 values
     (the kernel's bf16 rounding of P is not mirrored; it sits far inside the
     output tolerance).
+  * Block-sparse attention (the kernel half of the "sparse + low-bit"
+    composition, digipub.cc TurboDiffusion article, SLA paragraph; GVCLab
+    Video-Generation-101 systems survey, SpargeAttention row): an optional
+    block mask with one entry per (128-row query block, 64-key tile); keys of
+    a zero entry get zero weight in that block's rows (logit -inf).  A row
+    whose blocks are all zero has no softmax; its output is defined as 0.
   * FP8 P.V: the kernel's online schedule is mirrored.  Keys are taken in tiles
     of ``kv_tile`` in ascending order with running max m_t; P~_j =
     exp(s_j - m_t(j)) in (0, 1]; the FP8 operand is E4M3(448 * P~_j); the row
@@ -36,7 +42,17 @@ import numpy as np
 from . import fp
 
 __all__ = ["int_scores", "logits", "softmax_pv", "attention_fp64", "attend_bf16",
-           "attend_fp8", "e4m3_round_f64"]
+           "attend_fp8", "e4m3_round_f64", "MASK_Q", "MASK_K", "key_mask"]
+
+MASK_Q = 128   # query rows per block-mask row
+MASK_K = 64    # keys per block-mask column
+
+
+def key_mask(block_mask, rows, N) -> np.ndarray:
+    """Per-(row, key) keep flags [R, N] of a block mask [ceil(N/128), ceil(N/64)]."""
+    bm = np.asarray(block_mask) != 0
+    rows = np.asarray(rows, np.int64)
+    return bm[rows // MASK_Q][:, np.arange(N) // MASK_K]
 
 
 def int_scores(q_codes: np.ndarray, k_codes: np.ndarray) -> np.ndarray:
@@ -72,8 +88,9 @@ def _bf16_to_f64(bits):
 
 
 def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_block, scale,
-                chunk: int = 256) -> np.ndarray:
-    """Output rows O[rows] (float64 [R, d]) of the 16-bit P.V path for one head."""
+                chunk: int = 256, block_mask=None) -> np.ndarray:
+    """Output rows O[rows] (float64 [R, d]) of the 16-bit P.V path for one head
+    (block_mask: optional [ceil(N/128), ceil(N/64)], nonzero = computed)."""
     rows = np.asarray(rows, np.int64)
     N = k_codes.shape[0]
     sk = np.repeat(np.asarray(k_scale, np.float64), k_block)[:N]
@@ -83,7 +100,15 @@ def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_blo
         r = rows[i:i + chunk]
         D = int_scores(q_codes[r], k_codes)
         S = logits(D, np.asarray(q_scale, np.float64)[r // q_block], sk, scale)
-        out[i:i + chunk] = softmax_pv(S, V)
+        if block_mask is None:
+            out[i:i + chunk] = softmax_pv(S, V)
+            continue
+        keep = key_mask(block_mask, r, N)
+        live = keep.any(axis=1)
+        o = np.zeros((r.size, V.shape[1]), np.float64)
+        if live.any():
+            o[live] = softmax_pv(np.where(keep[live], S[live], -np.inf), V)
+        out[i:i + chunk] = o
     return out
 
 
@@ -105,11 +130,13 @@ def e4m3_round_f64(y: np.ndarray):
 
 def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_block, k_block,
                scale, v_block: int = 64, kv_tile: int = 64, eps_rel: float | None = None,
-               round_p=None, chunk: int = 128):
+               round_p=None, chunk: int = 128, block_mask=None):
     """FP8 P.V path for one head; returns (O [R, d], E [R, d], hits).
 
     ``round_p`` maps 448*P~ to the FP8 operand value (default: E4M3 rounding;
-    the identity turns the mirror into the exact softmax, a self-check)."""
+    the identity turns the mirror into the exact softmax, a self-check).
+    With ``block_mask`` the running max is taken over kept keys only (tiles
+    without a kept key leave it unchanged) and dropped keys have P~ = 0."""
     rows = np.asarray(rows, np.int64)
     N = k_codes.shape[0]
     sk = np.repeat(np.asarray(k_scale, np.float64), k_block)[:N]
@@ -125,24 +152,29 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
         r = rows[i:i + chunk]
         S = logits(int_scores(q_codes[r], k_codes), np.asarray(q_scale, np.float64)[r // q_block],
                    sk, scale)
-        Sp = np.pad(S, ((0, 0), (0, pad)), constant_values=-np.inf)
+        keep = np.ones(S.shape, bool) if block_mask is None else key_mask(block_mask, r, N)
+        live = keep.any(axis=1, keepdims=True)
+        Sk = np.where(keep, S, -np.inf)
+        Sp = np.pad(Sk, ((0, 0), (0, pad)), constant_values=-np.inf)
         tile_max = Sp.reshape(r.size, nt, kv_tile).max(axis=2)
         m_run = np.maximum.accumulate(tile_max, axis=1)          # m_t
         m_key = np.repeat(m_run, kv_tile, axis=1)[:, :N]         # m_t(j)
-        m_T = m_run[:, -1:]
-        Pt = np.exp(S - m_key)                                   # P~ in (0, 1]
+        m_T = np.where(live, m_run[:, -1:], 0.0)
+        m_key = np.where(keep, m_key, 0.0)
+        Pt = np.where(keep, np.exp(np.where(keep, S, 0.0) - m_key), 0.0)   # P~ in (0, 1], 0 if dropped
         y = 448.0 * Pt
         if round_p is None:
             yr, quantum, c = e4m3_round_f64(y)
         else:
             yr = round_p(y)
-        w = np.exp(m_key - m_T)                                  # e^(m_t(j) - m_T)
+        w = np.where(keep, np.exp(m_key - m_T), 0.0)             # e^(m_t(j) - m_T)
         l = (w * Pt).sum(axis=1, keepdims=True)
         num = (w * yr / 448.0) @ Vh
-        O[i:i + chunk] = num / l
+        O[i:i + chunk] = np.where(live, num / np.where(live, l, 1.0), 0.0)
         if round_p is None:
             if eps_rel is None:
-                eps = 2.0 ** -20 * (1.0 + np.abs(S).max(axis=1, keepdims=True) / np.log(2.0))
+                # the largest |logit| among the keys the kernel evaluates (kept keys)
+                eps = 2.0 ** -20 * (1.0 + np.where(keep, np.abs(S), 0.0).max(axis=1, keepdims=True) / np.log(2.0))
             else:
                 eps = eps_rel
             frac = c - np.floor(c)
@@ -151,6 +183,6 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
                 lo = np.floor(c) * quantum
                 hi = np.minimum((np.floor(c) + 1.0) * quantum, fp.E4M3_MAX)
                 dP = np.where(amb, (hi - lo) / 448.0 * w, 0.0)
-                E[i:i + chunk] = (dP @ absV) / l
+                E[i:i + chunk] = np.where(live, (dP @ absV) / np.where(live, l, 1.0), 0.0)
                 hits += int(amb.sum())
     return O, E, hits
