@@ -45,6 +45,9 @@ EXPORTS = {
     "sqattn_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_attend_quantized": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                      _vp]),
+    "sqattn_forward_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "sqattn_attend_quantized_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                            _vp, _vp]),
     "sqattn_w8a8_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "sqattn_w8a8_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_w8a8_workspace_bytes": (_sz, [_i, _i]),
@@ -204,10 +207,24 @@ def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
     return int(lib().sqattn_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
 
 
+def _mask(block_mask, B, H, N):
+    """The block mask as a contiguous uint8 device tensor [B,H,ceil(N/128),ceil(N/64)]."""
+    torch = _torch()
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    _dev(block_mask, "block_mask", torch.uint8)
+    want = (B, H, -(-N // 128), -(-N // 64))
+    if tuple(block_mask.shape) != want:
+        raise ValueError(f"block_mask has shape {tuple(block_mask.shape)}, expected {want}")
+    return block_mask
+
+
 def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
-            workspace=None, out_dtype=None):
+            workspace=None, out_dtype=None, block_mask=None):
     """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> out [B,H,N,d],
-    fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16."""
+    fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16.  block_mask
+    (uint8/bool [B,H,ceil(N/128),ceil(N/64)]): block-sparse attention over
+    the kept (128-row query block, 64-key tile) pairs."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, torch.bfloat16)
@@ -219,6 +236,11 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
     out, od = _out(out, (B, H, N, d), q.device, out_dtype)
     w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
     o = _opts(q_block, od)
+    if block_mask is not None:
+        m = _mask(block_mask, B, H, N)
+        _check(lib().sqattn_forward_sparse(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(m),
+                                           _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
+        return out
     _check(lib().sqattn_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                    _ptr(w), wb, _stream(q), ctypes.byref(o)))
     return out
@@ -240,8 +262,9 @@ def pack_v(v, pv="bf16"):
 
 
 def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
-                     pv="bf16", q_block: int = 128, out=None, out_dtype=None):
-    """The attention kernel alone, on quantized Q/K and packed V (see pack_v)."""
+                     pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
+    """The attention kernel alone, on quantized Q/K and packed V (see pack_v);
+    block_mask as in forward."""
     torch = _torch()
     _dev(q_i8, "q_i8", torch.int8)
     _dev(k_i8, "k_i8", torch.int8)
@@ -257,6 +280,12 @@ def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale
         scale = 1.0 / math.sqrt(d)
     out, od = _out(out, (B, H, N, d), q_i8.device, out_dtype)
     o = _opts(q_block, od)
+    if block_mask is not None:
+        m = _mask(block_mask, B, H, N)
+        _check(lib().sqattn_attend_quantized_sparse(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
+                                                    _ptr(v_packed), _ptr(v_scale), B, H, N, d, float(scale),
+                                                    _PV[pv], _ptr(m), ctypes.byref(o), _ptr(out), _stream(q_i8)))
+        return out
     _check(lib().sqattn_attend_quantized(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_packed),
                                          _ptr(v_scale), B, H, N, d, float(scale), _PV[pv], ctypes.byref(o),
                                          _ptr(out), _stream(q_i8)))

@@ -166,6 +166,14 @@ int validate_forward(const void* q, const void* k, const void* v, int B, int H, 
   return SQATTN_OK;
 }
 
+// Block-sparse attention keeps a work-group's list of key tiles in LDS.
+int check_sparse(int N) {
+  if ((N + sqattn::KT - 1) / sqattn::KT > sqattn::SP_MAXT)
+    return fail(SQATTN_ERR_UNSUPPORTED,
+                "block-sparse attention supports N <= " + std::to_string(sqattn::SP_MAXT * sqattn::KT));
+  return SQATTN_OK;
+}
+
 // W8A8 sizes: K a positive multiple of 128 up to 2^20, 0 <= rows <= 65535*128.
 int check_w8a8_rows(int rows, const char* name) {
   if (rows < 0) return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " must be >= 0");
@@ -265,14 +273,15 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
   return forward_layout(z, pv_dtype, o.q_block).total;
 }
 
-int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
-                      int pv_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                      const sqattn_opts* opts) {
+static int forward_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                        int pv_dtype, const uint8_t* mask, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream, const sqattn_opts* opts) {
   g_err.clear();
   int s;
   Sizes z;
   Opts o;
   if ((s = validate_forward(q, k, v, B, H, N, d, scale, pv_dtype, out, opts, &z, &o))) return s;
+  if (mask && (s = check_sparse(N))) return s;
   const FwdLayout L = forward_layout(z, pv_dtype, o.q_block);
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;
@@ -308,8 +317,27 @@ int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H,
   p.nt = (int)z.nt;
   p.BH = BH;
   p.scale_log2e = scale * kLog2e;
+  p.mask = mask;
+  p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   sqattn::launch_attention(p, d, pv_dtype, st);
-  return hip_check("sqattn_forward launch");
+  return hip_check(mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
+}
+
+int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                      int pv_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                      const sqattn_opts* opts) {
+  return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, nullptr, out, workspace, workspace_bytes, stream, opts);
+}
+
+int sqattn_forward_sparse(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
+                          int pv_dtype, const uint8_t* block_mask, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream, const sqattn_opts* opts) {
+  if (!block_mask) {
+    g_err.clear();
+    return fail(SQATTN_ERR_INVALID_ARG, "block_mask is NULL");
+  }
+  return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, block_mask, out, workspace, workspace_bytes, stream,
+                      opts);
 }
 
 int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
@@ -344,9 +372,9 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
   return hip_check("sqattn_pack_v launch");
 }
 
-int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
-                            const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
-                            int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
+static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                       const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
+                       int pv_dtype, const uint8_t* mask, const sqattn_opts* opts, void* out, void* stream) {
   g_err.clear();
   int s;
   Sizes z;
@@ -376,8 +404,30 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
   p.nt = (int)z.nt;
   p.BH = (int)z.BH;
   p.scale_log2e = scale * kLog2e;
+  if (mask && (s = check_sparse(N))) return s;
+  p.mask = mask;
+  p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   sqattn::launch_attention(p, d, pv_dtype, (hipStream_t)stream);
-  return hip_check("sqattn_attend_quantized launch");
+  return hip_check(mask ? "sqattn_attend_quantized_sparse launch" : "sqattn_attend_quantized launch");
+}
+
+int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
+                            int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
+  return attend_impl(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, B, H, N, d, scale, pv_dtype, nullptr, opts,
+                     out, stream);
+}
+
+int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                   const float* k_scale, const void* v_packed, const float* v_scale, int B, int H,
+                                   int N, int d, float scale, int pv_dtype, const uint8_t* block_mask,
+                                   const sqattn_opts* opts, void* out, void* stream) {
+  if (!block_mask) {
+    g_err.clear();
+    return fail(SQATTN_ERR_INVALID_ARG, "block_mask is NULL");
+  }
+  return attend_impl(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, B, H, N, d, scale, pv_dtype, block_mask,
+                     opts, out, stream);
 }
 
 int sqattn_w8a8_quantize(const void* x, int rows, int cols, int8_t* codes, float* scales, void* stream) {

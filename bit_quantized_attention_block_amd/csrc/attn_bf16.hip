@@ -165,7 +165,7 @@ __device__ __forceinline__ void slot(v16i& sn, v16f& o, v4i a, v4i b, const v16i
 #undef SQ_ST2
 #undef SQ_ST1
 
-template <int D>
+template <int D, bool SP = false>
 struct Ctx {
   using G = Geo<D>;
   uint8_t* lds;
@@ -179,6 +179,11 @@ struct Ctx {
   v16i magic;             // SQ_MAGIC in every element: start of the INT8 accumulation
   v16f o[G::NCB];         // O^T accumulators
   float m, l;             // reference max (log2 units), row sum
+  // block-sparse only: the work-group's tile list (LDS) and whether this
+  // wave's reference is set (it is taken from its first kept tile)
+  const int* list;
+  int cnt;
+  bool has_m;
 
   // ---- global -> LDS (direct).  One boundary refills a K slot (KINST 1 KB
   // chunks, padded rows) and a V slot (VINST chunks); the KINST + VINST chunks
@@ -381,6 +386,47 @@ struct Ctx {
     pv_last(P1, t & (NSLOT - 1));
   }
 
+  // ---- block-sparse: the same pipeline over the work-group's tile list.
+  // Slots follow list positions; loads follow tile numbers.  A listed tile
+  // that this wave's mask row drops gets k = +inf, so its P is exactly 0
+  // (and adds 0 to the row sum); the wave's reference is the max of the first
+  // 32 keys of its first kept tile.
+  __device__ __forceinline__ bool keeps(int e) const { return ((e >> (24 + (wave >> 2))) & 1) != 0; }
+  __device__ __forceinline__ float k_for(int pos, float c, const v16i& s) {
+    const bool act = keeps(list[pos]);
+    if (act && !has_m) {
+      // s was written by MFMAs of the previous iteration's assembly, which
+      // the compiler does not track: cover the matrix-core result latency
+      asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+      m = rowmax(s, c, SQ_MAGIC);
+      has_m = true;
+    }
+    return act ? __builtin_fmaf(SQ_MAGIC_F, c, m) : __builtin_inff();
+  }
+  __device__ __forceinline__ void tiles_sparse(v16i& S0, v16i& S1, v4i (&P0)[2], v4i (&P1)[2], float c) {
+    float k = k_for(0, c, S0);
+    for (int pos = 0; pos < cnt - 1; ++pos) {
+      step<0>(S0, S1, P1, P0, pos, c, k, l);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB));
+      __syncthreads();
+      const Refill rf = refill(list[min(pos + NSLOT, cnt - 1)] & 0xFFFFFF, pos & (NSLOT - 1),
+                               list[min(pos + NSLOT - 1, cnt - 1)] & 0xFFFFFF, (pos - 1) & (NSLOT - 1));
+      const float c_next = cq * k_scale((pos + 1) & (NSLOT - 1));
+      step<1, true>(S1, S0, P0, P1, pos, c, k, l, &rf);
+      c = c_next;
+      k = k_for(pos + 1, c, S0);
+    }
+    const int pos = cnt - 1, t = list[pos] & 0xFFFFFF;
+    float unused = 0.0f;
+    step<0>(S0, S1, P1, P0, pos, c, k, unused);
+    l += tail_sum(P0, t, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    step<1>(S1, S0, P0, P1, pos, c, k, unused);
+    l += tail_sum(P1, t, 1);
+    pv_last(P1, pos & (NSLOT - 1));
+  }
+
   // ---- last tile, half kb: zero P of keys >= N; returns the sum of the kept P
   __device__ __forceinline__ float tail_sum(v4i (&pb)[2], int t, int kb) {
     const int kvalid = N - t * KT - kb * 32;
@@ -430,9 +476,9 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
 
 }  // namespace
 
-template <int D>
+template <int D, bool SP>
 __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
-  using Cx = Ctx<D>;
+  using Cx = Ctx<D, SP>;
   using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -471,15 +517,30 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   const int nt = p.nt;
   v16i S0, S1;
   v4i P0[2], P1[2];
+  // block-sparse: the list of tiles this work-group visits (a dense pass
+  // visits 0 .. nt-1)
+  int npos = nt;
+  int* list = nullptr;
+  if constexpr (SP) {
+    list = (int*)(smem + G::LDS_BYTES);
+    const uint8_t* m0 = p.mask + ((long long)bh * p.mq + 2 * qt) * nt;
+    const uint8_t* m1 = (2 * qt + 1 < p.mq) ? m0 + nt : nullptr;
+    npos = build_tile_list(m0, m1, nt, list, list + SP_MAXT, NTHR);
+    C.list = list;
+    C.cnt = npos;
+    C.has_m = false;
+  }
+  auto tile_at = [&](int j) { return SP ? (list[min(j, npos - 1)] & 0xFFFFFF) : min(j, nt - 1); };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 2 && npos > 0; ++pass) {
     C.init_loads();  // the refills of a pass clamp the K offsets at its end
     if (pass == 1) {
       // Rare path: some row's sum reached 2^HEADROOM.  Take the exact row max
       // over all keys (K tiles one at a time through slot 0) as the reference,
       // so that every P <= 1.
       float mx = -__builtin_inff();
-      for (int t = 0; t < nt; ++t) {
+      for (int j = 0; j < npos; ++j) {
+        const int t = tile_at(j);
         __syncthreads();
         C.load_k(t);
         __builtin_amdgcn_s_waitcnt(0);
@@ -487,9 +548,11 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
         const float c = C.cq * ld_uniform(C.skh + t);
         C.qk_half(S0, 0, 0, zero);
         C.qk_half(S1, 0, 1, zero);
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(C.rowmax(S0, c, 0), C.rowmax(S1, c, 0)));
+        const float r = __builtin_fmaxf(C.rowmax(S0, c, 0), C.rowmax(S1, c, 0));
+        if (!SP || C.keeps(list[j])) mx = __builtin_fmaxf(mx, r);
       }
       C.m = mx;
+      if constexpr (SP) C.has_m = true;
       __syncthreads();
     }
     C.l = 0.0f;
@@ -505,14 +568,17 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     // of boundary t-3 and lets those of t-2 and t-1 (LPB per wave each) stay
     // in flight.
 #pragma unroll
-    for (int j = 0; j < NSLOT; ++j) C.load_kv(min(j, nt - 1), j, min(j, nt - 1), j);
+    for (int j = 0; j < NSLOT; ++j) C.load_kv(tile_at(j), j, tile_at(j), j);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     float c = C.cq * C.k_scale(0);
     C.qk_half(S0, 0, 0, C.magic);
-    if (pass == 0) C.m = C.rowmax(S0, c, SQ_MAGIC);  // reference: max of the first 32 keys
-
-    C.tiles(S0, S1, P0, P1, c);
+    if constexpr (SP) {
+      C.tiles_sparse(S0, S1, P0, P1, c);
+    } else {
+      if (pass == 0) C.m = C.rowmax(S0, c, SQ_MAGIC);  // reference: max of the first 32 keys
+      C.tiles(S0, S1, P0, P1, c);
+    }
     C.l = pair_sum_f(C.l);
     __syncthreads();  // all waves are done with the LDS tiles
     // the sum bounds every P: l < 2^HEADROOM keeps P and O far from overflow
@@ -520,27 +586,39 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     if (pass == 1 || !__syncthreads_or(over)) break;
   }
 
-  // epilogue: O = O^T / l, fp32 or bf16 rows
-  const float inv = 1.0f / C.l;
+  // epilogue: O = O^T / l, fp32 or bf16 rows (block-sparse: rows whose mask
+  // keeps no tile have l = 0 and O = 0 and are written as zeros)
+  if constexpr (SP) {
+    if (npos == 0) {
+      C.l = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < G::NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) C.o[cb][i] = 0.0f;
+    }
+  }
+  const float inv = (SP && !(C.l > 0.0f)) ? 0.0f : 1.0f / C.l;
   if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, inv, C.g);
 }
 
-template <int D>
+template <int D, bool SP>
 static void launch_d(const AttnParams& q, hipStream_t st) {
+  constexpr int lds = Geo<D>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   static bool configured = false;  // the attribute is per kernel, set once per process
   if (!configured) {
-    (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Geo<D>::LDS_BYTES);
+    (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
     configured = true;
   }
-  hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(8 * q.per_xcd), dim3(NTHR), Geo<D>::LDS_BYTES, st, q);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, SP>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
 }
 
 void launch_attention_bf16(const AttnParams& q, int d, hipStream_t st) {
+  const bool sp = q.mask != nullptr;
   if (d == 128)
-    launch_d<128>(q, st);
+    sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
   else
-    launch_d<64>(q, st);
+    sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
 }
 
 }  // namespace sqattn

@@ -95,7 +95,7 @@ struct Geo {
   static constexpr int VBYTES = D * KT;         // packed V tile in HBM
 };
 
-template <int D>
+template <int D, bool SP = false>
 struct Ctx {
   using G = Geo<D>;
   uint8_t* lds;
@@ -174,11 +174,11 @@ struct Ctx {
     return *(const float*)(lds + G::VBASE + slot * G::VS + G::VSC + 4 * lane);
   }
 
-  // ---- S(0) straight from global memory (rows past N read row N-1)
-  __device__ __forceinline__ void qk_first(v16i (&s)[2]) const {
+  // ---- S of K tile t0 straight from global memory (rows past N read row N-1)
+  __device__ __forceinline__ void qk_first(v16i (&s)[2], int t0) const {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(kb * 32 + perm_key(lr), N - 1);
+      const int key = min(t0 * KT + kb * 32 + perm_key(lr), N - 1);
 #pragma unroll
       for (int ch = 0; ch < G::NCH; ++ch) {
         const v4i a = *(const v4i*)(kh + (long long)key * D + ch * 32 + g * 16);
@@ -210,14 +210,19 @@ struct Ctx {
   // ---- one tile iteration t.  QK: the next tile's scores into sn (when
   // QK); PV: V(t-1) (slot vslot, scale svp) times pprev; softmax of sc (tile
   // t, factor c) into pcur.  MASK: last tile, keys >= N excluded.
+  // Block-sparse: t is the list position (slots), tile the tile number; a
+  // listed tile this wave's mask row drops (act false) leaves the running
+  // max alone, gets P = 0 (mp = +inf) and carries weight ep = 0, which also
+  // keeps the first kept tile's 2^(m - mr) from meeting m = mr = -inf.
   template <bool QK, bool MASK>
   __device__ __forceinline__ void iter(const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t,
-                                       float c, float svp, const Refill& rf) {
+                                       float c, float svp, const Refill& rf, int tile = 0, bool act = true) {
     const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
     const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
 
     // running max of tile t
-    const float mn = __builtin_fmaxf(m, (float)tile_max(sc) * c);  // c >= 0
+    float mn = __builtin_fmaxf(m, (float)tile_max(sc) * c);  // c >= 0
+    if constexpr (SP) mn = act ? mn : m;
     const float w = svp * ep;  // tile t-1 relative to mr
 
     // P.V of the previous tile from a zero accumulator, O += w T
@@ -266,12 +271,16 @@ struct Ctx {
       mr = mn;
     }
     m = mn;
-    const float mp = mn - LOG2_448;
+    float mp = mn - LOG2_448;
     ep = __builtin_amdgcn_exp2f(mn - mr);  // tile t relative to mr, <= 2^REBASE
+    if constexpr (SP) {
+      mp = act ? mp : __builtin_inff();
+      ep = act ? ep : 0.0f;
+    }
 
     // P(t) = E4M3(y), y = 448 P~; byte 16 kb + i of the operand is key
     // 32 kb + 16 (i / 8) + 8 g + i % 8, the lane's S(t)[kb][i]
-    const int kvalid = N - t * KT;
+    const int kvalid = N - (SP ? tile : t) * KT;
     float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -316,9 +325,9 @@ struct Ctx {
 
 }  // namespace
 
-template <int D>
+template <int D, bool SP>
 __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
-  using Cx = Ctx<D>;
+  using Cx = Ctx<D, SP>;
   using G = Geo<D>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -360,16 +369,32 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     for (int r = 0; r < 16; ++r) C.o[cb][r] = 0.0f;
 
   const int nt = p.nt;
+  // block-sparse: the list of tiles this work-group visits (dense: 0 .. nt-1);
+  // positions index slots, list entries the tiles
+  int npos = nt;
+  int* list = nullptr;
+  if constexpr (SP) {
+    list = (int*)(smem + G::LDS_BYTES);
+    const uint8_t* m0 = p.mask + ((long long)bh * p.mq + 2 * qt) * nt;
+    const uint8_t* m1 = (2 * qt + 1 < p.mq) ? m0 + nt : nullptr;
+    npos = build_tile_list(m0, m1, nt, list, list + SP_MAXT, NTHR);
+  }
+  auto tile_at = [&](int j) { return SP ? (list[min(j, npos - 1)] & 0xFFFFFF) : min(j, nt - 1); };
+  auto kept = [&](int j) { return SP ? ((list[j] >> (24 + (C.wave >> 2))) & 1) != 0 : true; };
+  if (npos == 0) {  // block-sparse: nothing kept for these rows
+    if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, 0.0f, C.g);
+    return;
+  }
   // Prologue: K(1..4) into K slots 1,2,3,0 and V(0..3) into V slots 0..3 (past
   // the end: the last tile, never read), all landed before the loop; S(0)
   // from global memory meanwhile.  The first iteration multiplies V slot 3 by
   // P(-1) = 0 (a finite tile, so T = 0).
 #pragma unroll
-  for (int j = 0; j < NSLOT; ++j) C.load_kv(min(j + 1, nt - 1), (j + 1) & (NSLOT - 1), min(j, nt - 1), j);
+  for (int j = 0; j < NSLOT; ++j) C.load_kv(tile_at(j + 1), (j + 1) & (NSLOT - 1), tile_at(j), j);
   v16i S0[2], S1[2];
   v8i P0, P1;
-  C.qk_first(S0);
-  float c = C.cq * ld_uniform(C.skh);
+  C.qk_first(S0, tile_at(0));
+  float c = C.cq * ld_uniform(C.skh + tile_at(0));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 #pragma unroll
@@ -381,25 +406,25 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   // first iteration's refill rewrites K slot 0 and V slot 2 with the bytes
   // the prologue put there (read no earlier than iterations 3 and 2, after
   // boundaries that wait for it), so every iteration issues the same loads.
-  typename Cx::Refill rf = C.refill(min(4, nt - 1), 0, min(2, nt - 1), 2);
+  typename Cx::Refill rf = C.refill(tile_at(4), 0, tile_at(2), 2);
   auto step = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
     // K(t+1) and V(t-1) have landed (boundary t-1); their slots are refilled
     // only after this iteration
     const float c_next = C.cq * C.k_scale((t + 1) & (NSLOT - 1));
     const float svp = C.v_scale((t - 1) & (NSLOT - 1));
-    C.template iter<true, false>(sc, sn, pprev, pcur, t, c, svp, rf);
+    C.template iter<true, false>(sc, sn, pprev, pcur, t, c, svp, rf, tile_at(t), kept(t));
     // Wait for our own loads of three boundaries ago and all LDS reads, then
     // a plain barrier (the "memory" clobber keeps every memory access on its
     // side).  __syncthreads() would add a fence that waits for every
     // direct-to-LDS load in flight, which defeats the ring.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB) & ~0x0F00);  // and lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    rf = C.refill(min(t + 5, nt - 1), (t + 1) & (NSLOT - 1), min(t + 3, nt - 1), (t - 1) & (NSLOT - 1));
+    rf = C.refill(tile_at(t + 5), (t + 1) & (NSLOT - 1), tile_at(t + 3), (t - 1) & (NSLOT - 1));
     c = c_next;
   };
   auto last = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
     const float svp = C.v_scale((t - 1) & (NSLOT - 1));
-    C.template iter<false, true>(sc, sn, pprev, pcur, t, c, svp, rf);
+    C.template iter<false, true>(sc, sn, pprev, pcur, t, c, svp, rf, tile_at(t), kept(t));
     // V(t) may still be in flight (issued up to two boundaries ago, by any
     // wave): wait for every load, then a barrier
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -408,38 +433,42 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   };
   // tiles in pairs, so that the score and P registers alternate without copies
   int t = 0;
-  for (; t + 2 < nt; t += 2) {
+  for (; t + 2 < npos; t += 2) {
     step(S0, S1, P1, P0, t);
     step(S1, S0, P0, P1, t + 1);
   }
-  if (t + 1 < nt) {
+  if (t + 1 < npos) {
     step(S0, S1, P1, P0, t);
     last(S1, S0, P0, P1, t + 1);
   } else {
     last(S0, S1, P1, P0, t);
   }
 
-  // epilogue: O = O^T / l, fp32 or bf16 rows
-  const float inv = 1.0f / pair_sum_f(C.l);
+  // epilogue: O = O^T / l, fp32 or bf16 rows (block-sparse: rows whose mask
+  // keeps no listed tile have l = 0 and O = 0 and are written as zeros)
+  const float lsum = pair_sum_f(C.l);
+  const float inv = (SP && !(lsum > 0.0f)) ? 0.0f : 1.0f / lsum;
   if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, inv, C.g);
 }
 
-template <int D>
+template <int D, bool SP>
 static void launch_d(const AttnParams& q, hipStream_t st) {
+  constexpr int lds = Geo<D>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   static bool configured = false;  // the attribute is per kernel, set once per process
   if (!configured) {
-    (void)hipFuncSetAttribute((const void*)attn_fp8_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Geo<D>::LDS_BYTES);
+    (void)hipFuncSetAttribute((const void*)attn_fp8_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
     configured = true;
   }
-  hipLaunchKernelGGL(attn_fp8_kernel<D>, dim3(8 * q.per_xcd), dim3(NTHR), Geo<D>::LDS_BYTES, st, q);
+  hipLaunchKernelGGL((attn_fp8_kernel<D, SP>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
 }
 
 void launch_attention_fp8(const AttnParams& q, int d, hipStream_t st) {
+  const bool sp = q.mask != nullptr;
   if (d == 128)
-    launch_d<128>(q, st);
+    sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
   else
-    launch_d<64>(q, st);
+    sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
 }
 
 }  // namespace sqattn

@@ -20,6 +20,12 @@ constexpr int KT = 64;
 constexpr int ATT_WAVES = 8;
 constexpr int ATT_QW = 32;
 constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
+// Block-sparse attention: one mask row per 128 query rows (waves 0-3 of a
+// work-group read mask row 2 qt, waves 4-7 row 2 qt + 1); at most SP_MAXT key
+// tiles per head (the work-group's list of tiles lives in LDS).
+constexpr int SP_MQ = 128;
+constexpr int SP_MAXT = 4096;
+constexpr int SP_LIST_BYTES = 4 * SP_MAXT + 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -92,6 +98,36 @@ __device__ __forceinline__ void store_out_row(void* out, bool bf16, long long ba
 //   pos(key) = g*32 + (key/16)*8 + key%8 with g = (key/8)%2.
 __host__ __device__ __forceinline__ int fp8_key_pos(int key) {
   return (((key >> 3) & 1) << 5) | ((key >> 4) << 3) | (key & 7);
+}
+
+// Block-sparse attention: the sorted list of key tiles that mask row r0
+// (mrow0) or mask row r0 + 1 (mrow1, null past the last row) keeps, built by
+// all nthr threads of a work-group.  Entry: tile | row r0 keeps it << 24 |
+// row r0 + 1 keeps it << 25.  wcnt: nthr/64 ints of LDS scratch.  Returns
+// the count (uniform); list and count are visible to every wave on return.
+__device__ __forceinline__ int build_tile_list(const uint8_t* mrow0, const uint8_t* mrow1, int nt, int* list,
+                                               int* wcnt, int nthr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = nthr >> 6;
+  int base = 0;
+  for (int t0 = 0; t0 < nt; t0 += nthr) {
+    const int t = t0 + tid;
+    const int f0 = (t < nt && mrow0[t] != 0) ? 1 : 0;
+    const int f1 = (t < nt && mrow1 != nullptr && mrow1[t] != 0) ? 1 : 0;
+    const unsigned long long b = __ballot(f0 | f1);
+    const int before = __builtin_popcountll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) wcnt[wave] = __builtin_popcountll(b);
+    __syncthreads();
+    int off = base, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int c = wcnt[w];
+      off += (w < wave) ? c : 0;
+      tot += c;
+    }
+    if (f0 | f1) list[off + before] = t | (f0 << 24) | (f1 << 25);
+    base += tot;
+    __syncthreads();  // list entries written; wcnt free for the next round
+  }
+  return base;
 }
 
 // Size helpers shared by host code.

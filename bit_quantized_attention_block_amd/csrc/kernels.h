@@ -25,6 +25,8 @@ struct AttnParams {
   const float* sv;
   void* out;      // fp32, or bf16 (round to nearest even) when out_bf16
   int out_bf16;
+  const uint8_t* mask;  // block-sparse mask [BH][mq][nt] (nonzero = computed), or null (dense)
+  int mq;               // mask rows per head: ceil(N / 128)
   int N, nq, q_block, nt, BH, qtiles, per_xcd;
   float scale_log2e;
 };

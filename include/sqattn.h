@@ -193,6 +193,37 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
                             const sqattn_opts* opts, void* out, void* stream);
 
 /*
+ * Block-sparse attention: the same step computed only on the (query block,
+ * key tile) pairs a caller-supplied mask keeps -- the kernel half of the
+ * "sparse + low-bit" composition (digipub.cc TurboDiffusion article, SLA
+ * paragraph: sparse attention built on SageAttention, orthogonal to its
+ * low-bit arithmetic; GVCLab Video-Generation-101 systems survey,
+ * SpargeAttention row: selector, sparse layout, low-bit kernel).  The
+ * selector that produces the mask is the caller's.
+ *   block_mask : device uint8 [B, H, ceil(N/128), ceil(N/64)], row-major;
+ *                entry (b, h, i, j) nonzero = query rows [128i, 128i+128)
+ *                attend to keys [64j, 64j+64).  Read only.
+ * Keys of a zero entry get zero weight (the softmax runs over the kept keys;
+ * quantization, the K mean and every scale are those of the dense step).  A
+ * query row whose mask row keeps nothing is written as zeros.  A work-group
+ * of 256 query rows visits the union of its two mask rows' tiles, so its
+ * work scales with the kept fraction.  Inputs must be finite (a NaN in a
+ * dropped tile's V can reach rows of the other query block of the same
+ * work-group through 0 * NaN).  N <= 262144 (4096 key tiles), else
+ * SQATTN_ERR_UNSUPPORTED.  Everything else as sqattn_forward_ex /
+ * sqattn_attend_quantized.
+ */
+int sqattn_forward_sparse(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                          float scale, int pv_dtype, const uint8_t* block_mask, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const sqattn_opts* opts);
+int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                   const float* k_scale, const void* v_packed,
+                                   const float* v_scale, int B, int H, int N, int d, float scale,
+                                   int pv_dtype, const uint8_t* block_mask,
+                                   const sqattn_opts* opts, void* out, void* stream);
+
+/*
  * W8A8 block-wise INT8 linear layer, y = x W^T (+ b): the projections on
  * either side of attention with weights and activations both quantized to
  * INT8 in 128x128 blocks and the products on the INT8 matrix units

@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 18
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -221,3 +221,22 @@ def test_w8a8_workspace_bytes():
     assert L.sqattn_w8a8_workspace_bytes(M, 100) == 0
     assert L.sqattn_w8a8_workspace_bytes(-1, K) == 0
     assert L.sqattn_w8a8_workspace_bytes(0, K) == 0 or L.sqattn_w8a8_workspace_bytes(0, K) < 1024
+
+
+def test_sparse_validation():
+    L = sq.lib()
+    args = [FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.125, 0, FAKE, FAKE, FAKE, 1, None, None]
+    a = list(args)
+    a[9] = None
+    assert L.sqattn_forward_sparse(*a) == INVALID and "block_mask" in _err()
+    a = list(args)
+    a[5] = 262144 + 1
+    a[12] = BIG
+    assert L.sqattn_forward_sparse(*a) == UNSUPPORTED and "262144" in _err()
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 300, 128, 0.1, 0, FAKE, None, FAKE, None]
+    a = list(base)
+    a[12] = None
+    assert L.sqattn_attend_quantized_sparse(*a) == INVALID and "block_mask" in _err()
+    a = list(base)
+    a[8] = 262144 + 64
+    assert L.sqattn_attend_quantized_sparse(*a) == UNSUPPORTED

@@ -36,7 +36,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "gen_head", "gen_inputs", "sample_rows",
-           "f32_to_bf16_bits", "bf16_bits_to_f32"]
+           "f32_to_bf16_bits", "bf16_bits_to_f32", "gen_block_mask"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -183,3 +183,19 @@ def gen_inputs(w: Workload, N: int | None = None, d: int | None = None, B: int |
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(one, range(B * H)))
     return q, k, v, rows
+
+
+def gen_block_mask(B: int, H: int, N: int, density: float, seed: int, band: int = 2) -> np.ndarray:
+    """A block-sparse mask uint8 [B, H, ceil(N/128), ceil(N/64)] for 128-row
+    query blocks x 64-key tiles: every query block keeps the key tiles within
+    `band` query-block widths of its own rows (a local window), plus each
+    other tile with probability `density` (one PCG64 stream from
+    SeedSequence(seed)).  The pages give no mask; this stands in for a
+    selector's output (locality plus scattered long-range blocks)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    mq, nt = -(-N // 128), -(-N // 64)
+    m = (g.random((B, H, mq, nt)) < density)
+    qi = np.arange(mq)[:, None] * 2          # first 64-key tile of each query block
+    tj = np.arange(nt)[None, :]
+    m |= (np.abs(tj - qi) < 2 * band)[None, None]
+    return m.astype(np.uint8)
