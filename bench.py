@@ -5,6 +5,9 @@
 
 With a W8A8 workload (--workload w8a8-qkv-wan14b-480p and the other w8a8-*
 names) it measures the block-wise INT8 linear layer instead; see bench_w8a8.
+With --block-density D it measures block-sparse attention: a seeded mask
+(local band plus a fraction D of the other 128-row x 64-key blocks) and TOPS
+over the kept blocks' work only; see sparse_ops.
 
 One step is one full sqattn_forward over the workload: exact K mean, INT8
 quantization of Q and smoothed K, V packing (or E4M3 quantization), and the
@@ -154,8 +157,8 @@ def bench_w8a8(a):
         kern()
     k_ms, k_med, k_min, _ = _timed(torch, np, dev, stream, kern, reps)
     q_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_quantize(X), reps)[0]
-    tops = w.ops / (ms * 1e-3) / 1e12
-    k_tops = w.ops / (k_ms * 1e-3) / 1e12
+    tops = ops / (ms * 1e-3) / 1e12
+    k_tops = ops / (k_ms * 1e-3) / 1e12
     res = {
         "metric": W8A8_METRIC,
         "value": round(tops, 3),
@@ -189,9 +192,30 @@ def bench_w8a8(a):
     return 0
 
 
-def cpu_baseline(w, q, k, v, rows, heads=10):
+def sparse_ops(w, mask):
+    """(kept, processed) operation counts of block-sparse attention: kept =
+    4 d x the (query row, key) pairs of the kept blocks; processed = what the
+    kernel computes, each 256-row work-group running the union of its two
+    mask rows' tiles over all its rows."""
+    import numpy as np
+    N, d = w.N, w.d
+    mq, nt = mask.shape[2], mask.shape[3]
+    rows = np.minimum(128, N - 128 * np.arange(mq)).astype(np.float64)
+    keys = np.minimum(64, N - 64 * np.arange(nt)).astype(np.float64)
+    kept = 4.0 * d * np.einsum("bhij,i,j->", mask.astype(np.float64), rows, keys)
+    m = mask.astype(bool)
+    if mq % 2:
+        m = np.concatenate([m, np.zeros(m.shape[:2] + (1, nt), bool)], axis=2)
+    union = m[:, :, 0::2] | m[:, :, 1::2]
+    wrows = np.minimum(256, N - 256 * np.arange(union.shape[2])).astype(np.float64)
+    processed = 4.0 * d * np.einsum("bhij,i,j->", union.astype(np.float64), wrows, keys)
+    return int(kept), int(processed)
+
+
+def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
     """Time the oracle on `heads` heads (full quantization of each head plus
-    its checked rows against all N keys) and scale to the whole workload."""
+    its checked rows against all N keys) and scale to the whole workload
+    (with a block mask: the masked oracle, rated on the kept work `ops`)."""
     import numpy as np
     import oracle
     cores = _cores()
@@ -206,20 +230,22 @@ def cpu_baseline(w, q, k, v, rows, heads=10):
             vc, vs = oracle.quant.quantize_v_fp8(v[b, h], 64)
         t1 = time.perf_counter()
         r = rows[i]
+        bm = None if mask is None else mask[b, h]
         if w.pv == "fp8":
-            oracle.attention.attend_fp8(qc, qs, kc, ks, vc, vs, r, w.q_block, w.k_block, w.scale)
+            oracle.attention.attend_fp8(qc, qs, kc, ks, vc, vs, r, w.q_block, w.k_block, w.scale, block_mask=bm)
         else:
-            oracle.attention.attend_bf16(qc, qs, kc, ks, v[b, h], r, w.q_block, w.k_block, w.scale)
+            oracle.attention.attend_bf16(qc, qs, kc, ks, v[b, h], r, w.q_block, w.k_block, w.scale, block_mask=bm)
         t2 = time.perf_counter()
         t_quant += t1 - t0
         t_attn += t2 - t1
         nrows += len(r)
     BH = w.B * w.H
     t_full = t_quant / heads * BH + t_attn / nrows * (w.N * BH)
-    return {"value": round(w.ops / t_full / 1e12, 6), "unit": "TOPS", "cores": int(cores),
-            "kind": "oracle",
+    return {"value": round((w.ops if ops is None else ops) / t_full / 1e12, 6), "unit": "TOPS",
+            "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} heads of {w.name}: full quantization ({t_quant:.1f} s) + {nrows} query rows "
-                      f"against all {w.N} keys ({t_attn:.1f} s); scaled to {BH} heads x {w.N} rows",
+                      f"against all {w.N} keys ({t_attn:.1f} s); scaled to {BH} heads x {w.N} rows"
+                      + ("" if mask is None else " (block mask applied)"),
             "sample_seconds": round(t_quant + t_attn, 2)}
 
 
@@ -231,6 +257,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="wan14b-480p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=None)
+    ap.add_argument("--block-density", type=float, default=None,
+                    help="block-sparse attention: fraction of the non-local blocks kept")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every head is "
@@ -248,16 +276,23 @@ def main(argv=None):
     w = W.get(a.workload)
     t0 = time.perf_counter()
     q, k, v, rows = W.gen_inputs(w)
+    mask_h = M = None
+    ops = w.ops
+    if a.block_density is not None:
+        mask_h = W.gen_block_mask(w.B, w.H, w.N, a.block_density, seed=w.index)
+        ops, processed = sparse_ops(w, mask_h)
     print(f"[bench] generated {w.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     to = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
     Q, K, V = to(q), to(k), to(v)
+    if mask_h is not None:
+        M = torch.from_numpy(mask_h).to(dev)
     out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     ws = torch.empty(sq.workspace_bytes(w.B, w.H, w.N, w.d, w.pv, w.q_block), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws)
+        sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M)
 
     def timed(fn, n):
         return _timed(torch, np, dev, stream, fn, n)
@@ -279,7 +314,8 @@ def main(argv=None):
         vp = sq.pack_v(V, "bf16")
 
     def kern():
-        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out,
+                            block_mask=M)
 
     reps = a.kernel_reps or a.steps
     for _ in range(2):
@@ -296,8 +332,8 @@ def main(argv=None):
 
     p_ms = timed(prep, reps)[0]
 
-    tops = w.ops / (ms * 1e-3) / 1e12
-    k_tops = w.ops / (k_ms * 1e-3) / 1e12
+    tops = ops / (ms * 1e-3) / 1e12
+    k_tops = ops / (k_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(tops, 3),
@@ -319,12 +355,21 @@ def main(argv=None):
                                  "attention_kernel_min": round(k_min, 4), "quantize_and_pack": round(p_ms, 4)}},
         "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": _traffic(w.name, ATTN_SRC[w.pv]), "avg_launch_ms": round(k_ms, 4),
-                     "ops_per_launch": w.ops},
+                     "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
+                     "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
     }
+    if M is not None:
+        res["metric"] = METRIC.replace("4·B·H·N²·d/s", "4·d·kept query-key pairs/s") + ", block-sparse"
+        res["config"]["block_sparse"] = {
+            "mask": "128-row x 64-key blocks: local band (keys within 256 rows of the query block) plus a "
+                    f"fraction {a.block_density} of the other blocks, seed {w.index}",
+            "kept_fraction": round(ops / w.ops, 4),
+            "processed_fraction": round(processed / w.ops, 4),
+            "dense_equivalent_tops": round(w.ops / (ms * 1e-3) / 1e12, 3)}
+        res["roofline"]["processed_ops_per_launch"] = processed
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows, mask=mask_h, ops=ops)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
