@@ -257,6 +257,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="wan14b-480p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=None)
+    ap.add_argument("--q-block", type=int, default=None,
+                    help="Q scale block (1 = one scale per query row); default: the workload's")
     ap.add_argument("--block-density", type=float, default=None,
                     help="block-sparse attention: fraction of the non-local blocks kept")
     a = ap.parse_args(argv)
@@ -274,6 +276,9 @@ def main(argv=None):
     import workloads as W
 
     w = W.get(a.workload)
+    if a.q_block is not None:
+        import dataclasses
+        w = dataclasses.replace(w, q_block=a.q_block)
     t0 = time.perf_counter()
     q, k, v, rows = W.gen_inputs(w)
     mask_h = M = None

@@ -52,6 +52,14 @@ int check_block(int b, const char* name) {
   return SQATTN_OK;
 }
 
+// Q blocks: a multiple of 16 rows, or 1 (one scale per query row).
+int check_q_block(int b) {
+  if (b == 1) return SQATTN_OK;
+  if (b < 16 || (b % 16) != 0 || b > (1 << 24))
+    return fail(SQATTN_ERR_INVALID_ARG, "q_block must be 1 or a positive multiple of 16");
+  return SQATTN_OK;
+}
+
 int check_ptr(const void* p, const char* name, size_t align) {
   if (!p) return fail(SQATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
   if (!aligned(p, align))
@@ -76,7 +84,7 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   if (o->k_block) r->k_block = o->k_block;
   if (o->v_block) r->v_block = o->v_block;
   int s;
-  if ((s = check_block(r->q_block, "q_block"))) return s;
+  if ((s = check_q_block(r->q_block))) return s;
   if (r->k_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "k_block must be 64 (the attention tile)");
   if (r->v_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "v_block must be 64");
   return SQATTN_OK;
@@ -237,7 +245,7 @@ int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d,
       (s = check_ptr(k_scale, "k_scale", 4)) || (s = check_ptr(k_mean, "k_mean", 4)))
     return s;
   if ((s = check_shape(B, H, N, d, &z))) return s;
-  if ((s = check_block(q_block, "q_block")) || (s = check_block(k_block, "k_block"))) return s;
+  if ((s = check_q_block(q_block)) || (s = check_block(k_block, "k_block"))) return s;
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;
   const size_t need = align_up((size_t)(z.BH * z.S * z.d) * 32);

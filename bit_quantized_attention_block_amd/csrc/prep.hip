@@ -183,6 +183,47 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   }
 }
 
+// grid (ceil(N / RPW), B*H), 256 threads: one scale per row (block = 1, the
+// per-lane granularity of the attention kernel's Q operand: each lane holds
+// one query row).  CPR threads own a row (8 channels each), RPW rows per
+// work-group; the row's absmax is reduced over its CPR lanes, which lie in
+// one wave.  Same rule: s = fl32(absmax/127), code = clamp(rne(fl32(x/s))).
+template <int D>
+__global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __restrict__ x, int N,
+                                                            int8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+  constexpr int CPR = D / 8;
+  constexpr int RPW = 256 / CPR;
+  const long long bh = blockIdx.y;
+  const int t = threadIdx.x, cg = t % CPR;
+  const int r = blockIdx.x * RPW + t / CPR;
+  const bool ok = r < N;
+  const long long base = (bh * N + (ok ? r : 0)) * D + cg * 8;
+  const v4i w = ok ? *(const v4i*)(x + base) : v4i{0, 0, 0, 0};
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = (uint32_t)w[j];
+    amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(u & 0xFFFFu)), fabsf(bf16_bits_to_f32(u >> 16))));
+  }
+#pragma unroll
+  for (int o = CPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float s = amax / 127.0f;  // correctly rounded binary32 division
+  if (!ok) return;
+  if (cg == 0) scales[bh * N + r] = s;
+  const bool zero = !(s > 0.0f);
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t u = (uint32_t)w[j >> 1];
+    const float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
+    int c = 0;
+    if (!zero) c = (int)fminf(fmaxf(rintf(a / s), -127.0f), 127.0f);
+    packed[j >> 2] |= ((uint32_t)(c & 0xFF)) << ((j & 3) * 8);
+  }
+  *(uint2*)(codes + base) = make_uint2(packed[0], packed[1]);
+}
+
 // ---------------------------------------------------------------------------
 // V layouts for the attention kernel
 // ---------------------------------------------------------------------------
@@ -358,6 +399,11 @@ void launch_kmean(const uint16_t* k, int BH, int N, int d, uint64_t* partial, fl
 
 void launch_quant_i8(const uint16_t* x, int BH, int N, int d, int block, const float* mean,
                      int8_t* codes, float* scales, hipStream_t st) {
+  if (block == 1 && mean == nullptr) {  // one scale per row
+    const int rpw = 256 / (d / 8);
+    SQ_DISPATCH_D(d, quant_i8_rows_kernel, dim3((N + rpw - 1) / rpw, BH), dim3(256), st, x, N, codes, scales);
+    return;
+  }
   int nb = (N + block - 1) / block;
   SQ_DISPATCH_D(d, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, N, block, mean, codes, scales);
 }

@@ -82,7 +82,9 @@ typedef enum { SQATTN_PV_BF16 = 0, SQATTN_PV_FP8_E4M3 = 1 } sqattn_pv_dtype;
 typedef enum { SQATTN_OUT_FP32 = 0, SQATTN_OUT_BF16 = 1 } sqattn_out_dtype;
 
 /* Block sizes and output type.  A zero field takes its default.  q_block:
- * any multiple of 16 (default 128).  k_block: 64 (the attention tile;
+ * any multiple of 16 (default 128), or 1 for one scale per query row (the
+ * granularity of the kernel's Q operand, where each lane holds one row; it
+ * costs the attention kernel nothing and helps heavy-tailed Q most).  k_block: 64 (the attention tile;
  * default).  v_block: 64 (FP8 only; default).  out_dtype: SQATTN_OUT_FP32
  * (default) or SQATTN_OUT_BF16, the fp32 result rounded to nearest even. */
 typedef struct sqattn_opts {
@@ -114,8 +116,8 @@ size_t sqattn_quantize_qk_workspace_bytes(int B, int H, int N, int d);
  *   q_i8      : int8 [B,H,N,d] codes of Q;  q_scale : float [B,H,ceil(N/q_block)].
  *   k_i8      : int8 [B,H,N,d] codes of K'; k_scale : float [B,H,ceil(N/k_block)].
  *   k_mean    : float [B,H,d], the mean that was removed from K.
- *   q_block   : multiple of 16; k_block : multiple of 16 (64 for use with
- *               sqattn_attend_quantized).
+ *   q_block   : 1 (one scale per row) or a multiple of 16; k_block :
+ *               multiple of 16 (64 for use with sqattn_attend_quantized).
  *   workspace : device memory of at least sqattn_quantize_qk_workspace_bytes();
  *               NULL makes the library allocate it stream-ordered on `stream`
  *               (and free it after use, stream-ordered).

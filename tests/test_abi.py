@@ -240,3 +240,10 @@ def test_sparse_validation():
     a = list(base)
     a[8] = 262144 + 64
     assert L.sqattn_attend_quantized_sparse(*a) == UNSUPPORTED
+
+
+def test_per_row_q_block_accepted():
+    # q_block = 1 passes validation (the call then stops at the workspace size)
+    assert _fwd(opts=sq.Opts(1, 64, 64, 0)) == WORKSPACE
+    assert _fwd(opts=sq.Opts(2, 64, 64, 0)) == INVALID and "q_block" in _err()
+    assert _fwd(opts=sq.Opts(8, 64, 64, 0)) == INVALID

@@ -254,3 +254,17 @@ def test_full_size_workload(index):
     """The Wan-shaped workloads at full size: quantization bit-exact on every
     row of every head, output on 1024 seeded rows per head."""
     _run_case(W.get(index))
+
+
+@pytest.mark.parametrize("pv,d", [("bf16", 128), ("bf16", 64), ("fp8", 128), ("fp8", 64)])
+def test_per_row_q_scales(pv, d):
+    """q_block = 1: one Q scale per row (the Q operand's per-lane granularity);
+    the bf16 path on the normal workloads, the FP8 path on the heavy-tailed
+    one, as the workload table pairs them."""
+    _run_case(W.get(1 if pv == "bf16" else 3), N=777, d=d, B=1, H=3, q_block=1, pv=pv)
+
+
+@pytest.mark.timeout(900)
+def test_per_row_q_scales_full_size_heavy_tailed():
+    """The heavy-tailed FP8 workload with per-row Q scales, every 8th head."""
+    _run_case(W.get(3), q_block=1, heads=range(0, 40, 8))
