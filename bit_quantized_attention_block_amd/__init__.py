@@ -46,6 +46,8 @@ EXPORTS = {
     "sqattn_attend_quantized": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                      _vp]),
     "sqattn_forward_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "sqattn_forward_strided": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _i, _vp, _vp, _vp, _sz, _vp,
+                                    _vp]),
     "sqattn_attend_quantized_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                             _vp, _vp]),
     "sqattn_w8a8_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
@@ -219,13 +221,34 @@ def _mask(block_mask, B, H, N):
     return block_mask
 
 
+def _row_strides(t, name, dtype):
+    """(b, h, n) element strides of a [B,H,N,d] device tensor whose rows are
+    contiguous (a view, e.g. of a fused QKV projection output)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be [B,H,N,d] with contiguous rows")
+    return tuple(int(x) for x in t.stride()[:3])
+
+
 def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
             workspace=None, out_dtype=None, block_mask=None):
     """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> out [B,H,N,d],
     fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16.  block_mask
     (uint8/bool [B,H,ceil(N/128),ceil(N/64)]): block-sparse attention over
-    the kept (128-row query block, 64-key tile) pairs."""
+    the kept (128-row query block, 64-key tile) pairs.  q, k, v and out may be
+    strided views with contiguous rows (e.g. q = qkv[:, :, 0].transpose(1, 2)
+    of a [B,N,3,H,d] projection output); they go through
+    sqattn_forward_strided."""
     torch = _torch()
+    strided = any(isinstance(t, torch.Tensor) and not t.is_contiguous() for t in (q, k, v, out))
+    if strided:
+        return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, torch.bfloat16)
     B, H, N, d = _shape(q)
@@ -243,6 +266,34 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
         return out
     _check(lib().sqattn_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                    _ptr(w), wb, _stream(q), ctypes.byref(o)))
+    return out
+
+
+def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask):
+    torch = _torch()
+    st = []
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        st += _row_strides(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v shapes differ")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if tuple(out.shape) != (B, H, N, d):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, d)}")
+    ost = _row_strides(out, "out", out_dtype)
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32
+    w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
+    o = _opts(q_block, od)
+    m = _mask(block_mask, B, H, N) if block_mask is not None else None
+    ins = (ctypes.c_int64 * 9)(*st)
+    outs = (ctypes.c_int64 * 3)(*ost)
+    _check(lib().sqattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, float(scale), _PV[pv],
+                                        _ptr(m), _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
     return out
 
 

@@ -250,9 +250,10 @@ int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d,
   Workspace ws;
   const size_t need = align_up((size_t)(z.BH * z.S * z.d) * 32);
   if ((s = ws.acquire(workspace, workspace_bytes, need, st))) return s;
-  sqattn::launch_quant_i8((const uint16_t*)q, (int)z.BH, N, d, q_block, nullptr, q_i8, q_scale, st);
-  sqattn::launch_kmean((const uint16_t*)k, (int)z.BH, N, d, ws.at<uint64_t>(0), k_mean, st);
-  sqattn::launch_quant_i8((const uint16_t*)k, (int)z.BH, N, d, k_block, k_mean, k_i8, k_scale, st);
+  const sqattn::Lay lc = sqattn::contiguous_lay(H, N, d);
+  sqattn::launch_quant_i8((const uint16_t*)q, lc, (int)z.BH, N, d, q_block, nullptr, q_i8, q_scale, st);
+  sqattn::launch_kmean((const uint16_t*)k, lc, (int)z.BH, N, d, ws.at<uint64_t>(0), k_mean, st);
+  sqattn::launch_quant_i8((const uint16_t*)k, lc, (int)z.BH, N, d, k_block, k_mean, k_i8, k_scale, st);
   return hip_check("sqattn_quantize_qk launch");
 }
 
@@ -266,7 +267,8 @@ int sqattn_quantize_v_fp8(const void* v, int B, int H, int N, int d, int v_block
   if ((s = check_shape(B, H, N, d, &z))) return s;
   if (v_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "v_block must be 64");
   hipStream_t st = (hipStream_t)stream;
-  sqattn::launch_quant_v_fp8((const uint16_t*)v, (int)z.BH, N, d, v_fp8, nullptr, v_scale, st);
+  sqattn::launch_quant_v_fp8((const uint16_t*)v, sqattn::contiguous_lay(H, N, d), (int)z.BH, N, d, v_fp8, nullptr,
+                             v_scale, st);
   return hip_check("sqattn_quantize_v_fp8 launch");
 }
 
@@ -283,13 +285,25 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
 
 static int forward_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
                         int pv_dtype, const uint8_t* mask, void* out, void* workspace, size_t workspace_bytes,
-                        void* stream, const sqattn_opts* opts) {
+                        void* stream, const sqattn_opts* opts, const int64_t* in_strides = nullptr,
+                        const int64_t* out_strides = nullptr) {
   g_err.clear();
   int s;
   Sizes z;
   Opts o;
   if ((s = validate_forward(q, k, v, B, H, N, d, scale, pv_dtype, out, opts, &z, &o))) return s;
   if (mask && (s = check_sparse(N))) return s;
+  sqattn::Lay lay[4];
+  for (int i = 0; i < 4; ++i) lay[i] = sqattn::contiguous_lay(H, N, d);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t* st = (i < 3) ? (in_strides ? in_strides + 3 * i : nullptr) : out_strides;
+    if (!st) continue;
+    for (int j = 0; j < 3; ++j)
+      if (st[j] < 0 || st[j] % 8 != 0 || st[j] > (1LL << 40))
+        return fail(SQATTN_ERR_INVALID_ARG,
+                    "strides must be non-negative multiples of 8 elements (16-byte rows), at most 2^40");
+    lay[i] = sqattn::Lay{st[0], st[1], st[2], H};
+  }
   const FwdLayout L = forward_layout(z, pv_dtype, o.q_block);
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;
@@ -300,15 +314,15 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   float* qs = ws.at<float>(L.q_scale);
   float* ks = ws.at<float>(L.k_scale);
   float* km = ws.at<float>(L.k_mean);
-  sqattn::launch_quant_i8((const uint16_t*)q, BH, N, d, o.q_block, nullptr, qi, qs, st);
-  sqattn::launch_kmean((const uint16_t*)k, BH, N, d, ws.at<uint64_t>(L.partial), km, st);
-  sqattn::launch_quant_i8((const uint16_t*)k, BH, N, d, o.k_block, km, ki, ks, st);
+  sqattn::launch_quant_i8((const uint16_t*)q, lay[0], BH, N, d, o.q_block, nullptr, qi, qs, st);
+  sqattn::launch_kmean((const uint16_t*)k, lay[1], BH, N, d, ws.at<uint64_t>(L.partial), km, st);
+  sqattn::launch_quant_i8((const uint16_t*)k, lay[1], BH, N, d, o.k_block, km, ki, ks, st);
   float* vs = nullptr;
   if (pv_dtype == SQATTN_PV_BF16) {
-    sqattn::launch_v_tiles_bf16((const uint16_t*)v, BH, N, d, ws.at<uint16_t>(L.vt), st);
+    sqattn::launch_v_tiles_bf16((const uint16_t*)v, lay[2], BH, N, d, ws.at<uint16_t>(L.vt), st);
   } else {
     vs = ws.at<float>(L.v_scale);
-    sqattn::launch_quant_v_fp8((const uint16_t*)v, BH, N, d, nullptr, ws.at<uint8_t>(L.vt), vs, st);
+    sqattn::launch_quant_v_fp8((const uint16_t*)v, lay[2], BH, N, d, nullptr, ws.at<uint8_t>(L.vt), vs, st);
   }
   sqattn::AttnParams p{};
   p.q = qi;
@@ -327,6 +341,7 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   p.scale_log2e = scale * kLog2e;
   p.mask = mask;
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
+  p.lo = lay[3];
   sqattn::launch_attention(p, d, pv_dtype, st);
   return hip_check(mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
 }
@@ -335,6 +350,18 @@ int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H,
                       int pv_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
                       const sqattn_opts* opts) {
   return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, nullptr, out, workspace, workspace_bytes, stream, opts);
+}
+
+int sqattn_forward_strided(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                           const int64_t* in_strides, const int64_t* out_strides, float scale, int pv_dtype,
+                           const uint8_t* block_mask, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream, const sqattn_opts* opts) {
+  if (!in_strides) {
+    g_err.clear();
+    return fail(SQATTN_ERR_INVALID_ARG, "in_strides is NULL");
+  }
+  return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, block_mask, out, workspace, workspace_bytes, stream,
+                      opts, in_strides, out_strides);
 }
 
 int sqattn_forward_sparse(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
@@ -374,7 +401,8 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
     return fail(SQATTN_ERR_INVALID_ARG, "unknown pv_dtype");
   hipStream_t st = (hipStream_t)stream;
   if (pv_dtype == SQATTN_PV_BF16)
-    sqattn::launch_v_tiles_bf16((const uint16_t*)v, (int)z.BH, N, d, (uint16_t*)v_packed, st);
+    sqattn::launch_v_tiles_bf16((const uint16_t*)v, sqattn::contiguous_lay(H, N, d), (int)z.BH, N, d,
+                                (uint16_t*)v_packed, st);
   else
     sqattn::launch_v_tiles_fp8((const uint8_t*)v, (int)z.BH, N, d, (uint8_t*)v_packed, st);
   return hip_check("sqattn_pack_v launch");
@@ -415,6 +443,7 @@ static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k
   if (mask && (s = check_sparse(N))) return s;
   p.mask = mask;
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
+  p.lo = sqattn::contiguous_lay(H, N, d);
   sqattn::launch_attention(p, d, pv_dtype, (hipStream_t)stream);
   return hip_check(mask ? "sqattn_attend_quantized_sparse launch" : "sqattn_attend_quantized launch");
 }

@@ -598,7 +598,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     }
   }
   const float inv = (SP && !(C.l > 0.0f)) ? 0.0f : 1.0f / C.l;
-  if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, inv, C.g);
+  if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, inv, C.g);
 }
 
 template <int D, bool SP>

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   auto tile_at = [&](int j) { return SP ? (list[min(j, npos - 1)] & 0xFFFFFF) : min(j, nt - 1); };
   auto kept = [&](int j) { return SP ? ((list[j] >> (24 + (C.wave >> 2))) & 1) != 0 : true; };
   if (npos == 0) {  // block-sparse: nothing kept for these rows
-    if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, 0.0f, C.g);
+    if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, 0.0f, C.g);
     return;
   }
   // Prologue: K(1..4) into K slots 1,2,3,0 and V(0..3) into V slots 0..3 (past
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   // keeps no listed tile have l = 0 and O = 0 and are written as zeros)
   const float lsum = pair_sum_f(C.l);
   const float inv = (SP && !(lsum > 0.0f)) ? 0.0f : 1.0f / lsum;
-  if (rok) store_out_row(p.out, p.out_bf16 != 0, hoff + (long long)row * D, C.o, inv, C.g);
+  if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, inv, C.g);
 }
 
 template <int D, bool SP>

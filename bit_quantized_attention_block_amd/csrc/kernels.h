@@ -6,13 +6,26 @@
 
 namespace sqattn {
 
+// Element strides of a [B, H, N, d] operand with d contiguous: row r of head
+// (b, h) starts at b*sb + h*sh + r*sn.  Contiguous: {H*N*d, N*d, d, H}.
+struct Lay {
+  long long sb, sh, sn;
+  int H;
+};
+__host__ __device__ inline Lay contiguous_lay(int H, int N, int d) {
+  return Lay{(long long)H * N * d, (long long)N * d, (long long)d, H};
+}
+__host__ __device__ inline long long lay_row(const Lay& l, long long bh, long long r) {
+  return (bh / l.H) * l.sb + (bh % l.H) * l.sh + r * l.sn;
+}
+
 int kmean_chunks(int BH, int N);
-void launch_kmean(const uint16_t* k, int BH, int N, int d, uint64_t* partial, float* mean,
+void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st);
-void launch_quant_i8(const uint16_t* x, int BH, int N, int d, int block, const float* mean,
+void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
                      int8_t* codes, float* scales, hipStream_t st);
-void launch_v_tiles_bf16(const uint16_t* v, int BH, int N, int d, uint16_t* vt, hipStream_t st);
-void launch_quant_v_fp8(const uint16_t* v, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
+void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st);
+void launch_quant_v_fp8(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
                         float* scales, hipStream_t st);
 void launch_v_tiles_fp8(const uint8_t* codes, int BH, int N, int d, uint8_t* vt, hipStream_t st);
 
@@ -27,6 +40,7 @@ struct AttnParams {
   int out_bf16;
   const uint8_t* mask;  // block-sparse mask [BH][mq][nt] (nonzero = computed), or null (dense)
   int mq;               // mask rows per head: ceil(N / 128)
+  Lay lo;               // element strides of the output rows
   int N, nq, q_block, nt, BH, qtiles, per_xcd;
   float scale_log2e;
 };

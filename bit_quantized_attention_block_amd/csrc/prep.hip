@@ -29,7 +29,7 @@ namespace sqattn {
 // (t % CPR)*8 .. +8 (CPR = D/8 16-byte pieces per row) of rows
 // r0 + t/CPR + j*RPP (RPP = 256/CPR rows per pass).
 template <int D>
-__global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __restrict__ k, int N,
+__global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __restrict__ k, Lay lk, int N,
                                                             int rows_per_chunk,
                                                             uint64_t* __restrict__ partial) {
   constexpr int CPR = D / 8;
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
   const long long bh = blockIdx.y;
   const int t = threadIdx.x;
   const int cg = t % CPR, rg = t / CPR;
-  const uint16_t* kh = k + bh * (long long)N * D;
+  const uint16_t* kh = k + lay_row(lk, bh, 0);
   int r0 = chunk * rows_per_chunk;
   int r1 = min(N, r0 + rows_per_chunk);
 
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
   bool bad = false;
 #pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(kh + (long long)r * D + cg * 8);
+    v4i w = *(const v4i*)(kh + (long long)r * lk.sn + cg * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -118,7 +118,7 @@ __device__ __forceinline__ float block_max_256(float v, float* sh) {
 // grid (nblocks, B*H), 256 threads.  One work-group per block of `block` rows.
 // mean == nullptr: plain Q.  Otherwise x = fl32(K - mean[c]) (IEEE subtract).
 template <int D>
-__global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, int N, int block,
+__global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, Lay lx, int N, int block,
                                                        const float* __restrict__ mean,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   const long long bh = blockIdx.y;
   const int blk = blockIdx.x, nblk = gridDim.x;
   const int t = threadIdx.x, cg = t % CPR, rg = t / CPR;
-  const uint16_t* xh = x + bh * (long long)N * D;
+  const uint16_t* xh = x + lay_row(lx, bh, 0);
   int8_t* ch = codes + bh * (long long)N * D;
   const int r0 = blk * block, r1 = min(N, r0 + block);
 
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   float amax = 0.0f;
 #pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
+    v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
 
 #pragma unroll 2
   for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(xh + (long long)r * D + cg * 8);
+    v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
 // work-group; the row's absmax is reduced over its CPR lanes, which lie in
 // one wave.  Same rule: s = fl32(absmax/127), code = clamp(rne(fl32(x/s))).
 template <int D>
-__global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __restrict__ x, int N,
+__global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __restrict__ x, Lay lx, int N,
                                                             int8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
   constexpr int CPR = D / 8;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __re
   const int r = blockIdx.x * RPW + t / CPR;
   const bool ok = r < N;
   const long long base = (bh * N + (ok ? r : 0)) * D + cg * 8;
-  const v4i w = ok ? *(const v4i*)(x + base) : v4i{0, 0, 0, 0};
+  const v4i w = ok ? *(const v4i*)(x + lay_row(lx, bh, r) + cg * 8) : v4i{0, 0, 0, 0};
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -231,18 +231,18 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __re
 // grid (nt, B*H), 256 threads: V bf16 [N][D] -> Vt [nt][D][64] bf16 (tile t,
 // channel c, key j) with zeros for keys >= N.
 template <int D>
-__global__ __launch_bounds__(256) void v_tiles_bf16_kernel(const uint16_t* __restrict__ v, int N,
+__global__ __launch_bounds__(256) void v_tiles_bf16_kernel(const uint16_t* __restrict__ v, Lay lv, int N,
                                                            uint16_t* __restrict__ vt) {
   __shared__ uint16_t tile[KT][D + 8];
   const long long bh = blockIdx.y;
   const int tt = blockIdx.x, nt = gridDim.x;
   const int t = threadIdx.x;
-  const uint16_t* vh = v + bh * (long long)N * D;
+  const uint16_t* vh = v + lay_row(lv, bh, 0);
   constexpr int CPR = D / 8;
   for (int i = t; i < KT * CPR; i += 256) {
     int r = i / CPR, c8 = (i % CPR) * 8;
     int key = tt * KT + r;
-    v4i w = (key < N) ? *(const v4i*)(vh + (long long)key * D + c8) : v4i{0, 0, 0, 0};
+    v4i w = (key < N) ? *(const v4i*)(vh + (long long)key * lv.sn + c8) : v4i{0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       tile[r][c8 + 2 * j] = (uint16_t)((uint32_t)w[j] & 0xFFFFu);
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void v_tiles_bf16_kernel(const uint16_t* __res
 // and/or the attention tile layout [nt][D][64] with FP8 key positions
 // (if vt != nullptr, zero for keys >= N), and the scale.
 template <int D>
-__global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __restrict__ v, int N,
+__global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __restrict__ v, Lay lv, int N,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ vt,
                                                           float* __restrict__ scales) {
@@ -278,11 +278,11 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
   constexpr int CPR = D / 8;
   constexpr int RPP = 256 / CPR;
   const int cg = t % CPR, rg = t / CPR;
-  const uint16_t* vh = v + bh * (long long)N * D;
+  const uint16_t* vh = v + lay_row(lv, bh, 0);
   const int r0 = tt * KT, r1 = min(N, r0 + KT);
   float amax = 0.0f;
   for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(vh + (long long)r * D + cg * 8);
+    v4i w = *(const v4i*)(vh + (long long)r * lv.sn + cg * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
   for (int r = r0 + rg; r < r0 + KT; r += RPP) {
     uint32_t packed[2] = {0u, 0u};
     if (r < r1) {
-      v4i w = *(const v4i*)(vh + (long long)r * D + cg * 8);
+      v4i w = *(const v4i*)(vh + (long long)r * lv.sn + cg * 8);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint32_t u = (uint32_t)w[j >> 1];
@@ -386,37 +386,38 @@ int kmean_chunks(int BH, int N) {
   return s;
 }
 
-void launch_kmean(const uint16_t* k, int BH, int N, int d, uint64_t* partial, float* mean,
+void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st) {
   int S = kmean_chunks(BH, N);
   int rows = (N + S - 1) / S;
-  SQ_DISPATCH_D(d, kmean_partial_kernel, dim3(S, BH), dim3(256), st, k, N, rows, partial);
+  SQ_DISPATCH_D(d, kmean_partial_kernel, dim3(S, BH), dim3(256), st, k, lk, N, rows, partial);
   if (d == 128)
     hipLaunchKernelGGL(kmean_finalize_kernel<128>, dim3(BH), dim3(128), 0, st, partial, S, N, mean);
   else
     hipLaunchKernelGGL(kmean_finalize_kernel<64>, dim3(BH), dim3(64), 0, st, partial, S, N, mean);
 }
 
-void launch_quant_i8(const uint16_t* x, int BH, int N, int d, int block, const float* mean,
+void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
                      int8_t* codes, float* scales, hipStream_t st) {
   if (block == 1 && mean == nullptr) {  // one scale per row
     const int rpw = 256 / (d / 8);
-    SQ_DISPATCH_D(d, quant_i8_rows_kernel, dim3((N + rpw - 1) / rpw, BH), dim3(256), st, x, N, codes, scales);
+    SQ_DISPATCH_D(d, quant_i8_rows_kernel, dim3((N + rpw - 1) / rpw, BH), dim3(256), st, x, lx, N, codes,
+                  scales);
     return;
   }
   int nb = (N + block - 1) / block;
-  SQ_DISPATCH_D(d, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, N, block, mean, codes, scales);
+  SQ_DISPATCH_D(d, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, lx, N, block, mean, codes, scales);
 }
 
-void launch_v_tiles_bf16(const uint16_t* v, int BH, int N, int d, uint16_t* vt, hipStream_t st) {
+void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st) {
   int nt = (N + KT - 1) / KT;
-  SQ_DISPATCH_D(d, v_tiles_bf16_kernel, dim3(nt, BH), dim3(256), st, v, N, vt);
+  SQ_DISPATCH_D(d, v_tiles_bf16_kernel, dim3(nt, BH), dim3(256), st, v, lv, N, vt);
 }
 
-void launch_quant_v_fp8(const uint16_t* v, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
+void launch_quant_v_fp8(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
                         float* scales, hipStream_t st) {
   int nt = (N + KT - 1) / KT;
-  SQ_DISPATCH_D(d, quant_v_fp8_kernel, dim3(nt, BH), dim3(256), st, v, N, codes, vt, scales);
+  SQ_DISPATCH_D(d, quant_v_fp8_kernel, dim3(nt, BH), dim3(256), st, v, lv, N, codes, vt, scales);
 }
 
 void launch_v_tiles_fp8(const uint8_t* codes, int BH, int N, int d, uint8_t* vt, hipStream_t st) {

@@ -226,6 +226,29 @@ int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, con
                                    const sqattn_opts* opts, void* out, void* stream);
 
 /*
+ * sqattn_forward_ex / sqattn_forward_sparse on strided operands, so that a
+ * DiT block can hand over its tensors without layout copies: Q, K and V as
+ * views of a fused QKV projection output [B, N, 3, H, d], the output written
+ * straight into the [B, N, H, d] (= [B*N, H*d]) input of the output
+ * projection.  (The step right before attention in the DiT block:
+ * digipub.cc TurboDiffusion article, linear-layer and normalization
+ * paragraphs.)
+ *   in_strides  : int64 [9], element strides (b, h, n) of q, then k, then v;
+ *                 the d channels of a row are contiguous.  Row r of head
+ *                 (b, h) of q starts at q + b*s[0] + h*s[1] + r*s[2].
+ *   out_strides : int64 [3] (b, h, n) of out, or NULL for contiguous
+ *                 [B, H, N, d].  Output rows must not overlap.
+ *   block_mask  : as sqattn_forward_sparse, or NULL (dense).
+ * Every stride must be a non-negative multiple of 8 elements (16-byte rows)
+ * and at most 2^40; base pointers 16-byte aligned.  Results are bit-identical
+ * to the contiguous entry points on the same values.
+ */
+int sqattn_forward_strided(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                           const int64_t* in_strides, const int64_t* out_strides, float scale,
+                           int pv_dtype, const uint8_t* block_mask, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream, const sqattn_opts* opts);
+
+/*
  * W8A8 block-wise INT8 linear layer, y = x W^T (+ b): the projections on
  * either side of attention with weights and activations both quantized to
  * INT8 in 128x128 blocks and the products on the INT8 matrix units

@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 19
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -247,3 +247,18 @@ def test_per_row_q_block_accepted():
     assert _fwd(opts=sq.Opts(1, 64, 64, 0)) == WORKSPACE
     assert _fwd(opts=sq.Opts(2, 64, 64, 0)) == INVALID and "q_block" in _err()
     assert _fwd(opts=sq.Opts(8, 64, 64, 0)) == INVALID
+
+
+def test_strided_forward_validation():
+    L = sq.lib()
+    good = (ctypes.c_int64 * 9)(*([3 * 2 * 64 * 64 * 8, 64, 3 * 2 * 64] * 3))
+    bad = (ctypes.c_int64 * 9)(*([3 * 2 * 64 * 64 * 8, 64, 3 * 2 * 64 + 4] * 3))
+    neg = (ctypes.c_int64 * 9)(*([-64, 64, 384] * 3))
+    args = lambda st, ost=None: [FAKE, FAKE, FAKE, 1, 2, 64, 64, st, ost, 0.125, 0, None, FAKE, FAKE, 1, None, None]
+    assert L.sqattn_forward_strided(*args(None)) == INVALID and "in_strides" in _err()
+    assert L.sqattn_forward_strided(*args(bad)) == INVALID and "multiples of 8" in _err()
+    assert L.sqattn_forward_strided(*args(neg)) == INVALID
+    obad = (ctypes.c_int64 * 3)(8, 8, 12)
+    assert L.sqattn_forward_strided(*args(good, obad)) == INVALID
+    # valid strides reach the workspace check
+    assert L.sqattn_forward_strided(*args(good)) == WORKSPACE
