@@ -28,6 +28,8 @@ article, linear-layer quantization paragraph):
 
   w8a8.quantize_blocks   INT8 codes + one scale per 128x128 block
   w8a8.linear            y = x W^T (+ b) from the block codes and scales
+  norm.rmsnorm_quantize  RMSNorm (exact mean square, binary32 steps) fused
+                         with that block quantization
 
 Pins (what ties these functions to something other than themselves) live in
 ``tests/test_oracle_*.py``.  The end-to-end output against the pages is
@@ -36,9 +38,9 @@ step; the quantized-vs-exact gap is reported as a diagnostic only.
 """
 from __future__ import annotations
 
-from . import attention, fp, quant, w8a8  # noqa: F401
+from . import attention, fp, norm, quant, w8a8  # noqa: F401
 
-__all__ = ["attention", "fp", "quant", "w8a8", "forward_head"]
+__all__ = ["attention", "fp", "norm", "quant", "w8a8", "forward_head"]
 
 
 def forward_head(q_bits, k_bits, v_bits, rows, q_block, k_block, scale, pv="bf16",

@@ -1,0 +1,85 @@
+"""Oracle of the RMSNorm that precedes the W8A8 projections, fused with their
+INT8 block quantization.
+
+TEST INFRASTRUCTURE.  Part of the CPU oracle; see ``oracle/__init__.py``.
+
+Method, from the pages: TurboDiffusion rewrites LayerNorm and RMSNorm as
+custom kernels for speed (digipub.cc TurboDiffusion article, paragraph on
+other optimizations), and quantizes the inputs of its linear layers to INT8
+in 128x128 blocks (same article, linear-layer quantization paragraph).  The
+normalization here feeds that quantization directly.
+
+Readings (the pages give no formula; this is the usual RMSNorm with every
+rounding fixed so that a quantization decision never depends on a summation
+order):
+  * For a row x of K bf16 values: S = sum_k x_k^2 exactly, mu2 =
+    fl32(S / K) (the exact quotient rounded once, nearest-even).
+  * r = fl32(1 / fl32(sqrt(fl32(mu2 + eps)))): three binary32 operations,
+    each correctly rounded; eps > 0 is a binary32 number.
+  * y_k = fl32(fl32(x_k * r) * gamma_k) (gamma binary32 [K]; without gamma
+    y_k = fl32(x_k * r)).
+  * The codes and scales are those of the W8A8 rule applied to the binary32
+    y (oracle.w8a8.quantize_blocks): no bf16 round trip in between.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fp, w8a8
+
+__all__ = ["sum_squares_exact", "rms_inverse", "rmsnorm", "rmsnorm_quantize"]
+
+# every bf16 square is an integer multiple of 2^-266 (smallest subnormal^2)
+_UNIT_EXP = -266
+
+
+def sum_squares_exact(x_bits: np.ndarray) -> list:
+    """S_r = sum_k x_rk^2 as exact integers in units of 2^-266, per row.
+
+    x_bits: uint16 bf16 bits [R, K].  A value with biased exponent E and
+    significand M (hidden bit included) squares to M^2 * 2^(2 max(E,1) - 2)
+    units; the M^2 are summed per exponent bucket (exact in float64: below
+    2^36) and the buckets combined in Python integers."""
+    b = np.asarray(x_bits, np.uint16).astype(np.int64)
+    E = (b >> 7) & 0xFF
+    M = (b & 0x7F) | np.where(E > 0, 0x80, 0)
+    e2 = 2 * np.maximum(E, 1) - 2                       # 0 .. 506
+    R = b.shape[0]
+    nb = 2 * 255
+    idx = (np.arange(R, dtype=np.int64)[:, None] * nb + e2).ravel()
+    buckets = np.bincount(idx, weights=(M * M).astype(np.float64).ravel(), minlength=R * nb).reshape(R, nb)
+    out = []
+    for r in range(R):
+        s = 0
+        for e in np.nonzero(buckets[r])[0]:
+            s += int(buckets[r, e]) << int(e)
+        out.append(s)
+    return out
+
+
+def rms_inverse(x_bits: np.ndarray, eps: float):
+    """(mu2, r) per row, float32 [R] each."""
+    x_bits = np.asarray(x_bits, np.uint16)
+    K = x_bits.shape[1]
+    S = sum_squares_exact(x_bits)
+    mu2 = np.array([fp.rational_to_f32(s, K << -_UNIT_EXP) for s in S], np.float32)
+    with np.errstate(divide="ignore"):
+        r = np.float32(1.0) / np.sqrt(mu2 + np.float32(eps))
+    return mu2, r.astype(np.float32)
+
+
+def rmsnorm(x_bits: np.ndarray, gamma, eps: float):
+    """y float32 [R, K] and r float32 [R]."""
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    _, r = rms_inverse(x_bits, eps)
+    y = (x * r[:, None]).astype(np.float32)
+    if gamma is not None:
+        y = (y * np.asarray(gamma, np.float32)[None, :]).astype(np.float32)
+    return y, r
+
+
+def rmsnorm_quantize(x_bits: np.ndarray, gamma, eps: float):
+    """(codes int8 [R, K], scales float32 [ceil(R/128), K/128], r float32 [R])."""
+    y, r = rmsnorm(x_bits, gamma, eps)
+    codes, scales = w8a8.quantize_blocks(y)
+    return codes, scales, r

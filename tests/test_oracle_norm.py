@@ -1,0 +1,97 @@
+"""Pins of the oracle's RMSNorm + INT8 block quantization (oracle/norm.py).
+
+  * mu2 is the binary32 number nearest to the exact mean square (Fraction
+    brute force, subnormal and large inputs included);
+  * y is within a few binary32 roundings of the float64 RMSNorm;
+  * power-of-two scaling of a row leaves y and the codes unchanged and scales
+    r by the inverse power (exact when eps is negligible);
+  * a constant row normalizes to +-gamma; permuting the columns (with gamma)
+    permutes y exactly (the exact sum does not depend on the order).
+"""
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import norm, w8a8
+import workloads as W
+
+
+def _bits(a):
+    return W.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def _f(b):
+    return W.bf16_bits_to_f32(b)
+
+
+def _is_nearest_f32(r, exact: Fraction):
+    r = np.float32(r)
+    d = abs(Fraction(float(r)) - exact)
+    for nb in (np.nextafter(r, np.float32(-np.inf)), np.nextafter(r, np.float32(np.inf))):
+        dn = abs(Fraction(float(nb)) - exact)
+        assert d <= dn
+        if d == dn:
+            assert int(r.view(np.uint32)) & 1 == 0
+
+
+def test_mean_square_is_nearest_binary32():
+    rng = np.random.default_rng(0)
+    rows = [rng.standard_normal(256) * 3,
+            np.concatenate([rng.standard_normal(200) * 1e-39, rng.standard_normal(56)]),   # subnormals
+            rng.standard_normal(256) * 1e15,
+            np.concatenate([[6e4], rng.standard_normal(255) * 1e-30]),
+            np.full(256, 0.0)]
+    x = np.stack([_bits(r) for r in rows])
+    mu2, r = norm.rms_inverse(x, 1e-6)
+    for i in range(len(rows)):
+        exact = sum(Fraction(float(v)) ** 2 for v in _f(x[i])) / 256
+        _is_nearest_f32(mu2[i], exact)
+    assert mu2[4] == 0 and r[4] == np.float32(1) / np.sqrt(np.float32(1e-6))
+
+
+def test_close_to_float64_rmsnorm():
+    rng = np.random.default_rng(1)
+    x = _bits(rng.standard_normal((64, 512)) * rng.uniform(0.01, 100, (64, 1)))
+    g = (rng.standard_normal(512) * 0.5 + 1).astype(np.float32)
+    y, r = norm.rmsnorm(x, g, 1e-6)
+    xf = _f(x).astype(np.float64)
+    ref = xf / np.sqrt((xf ** 2).mean(axis=1, keepdims=True) + np.float64(np.float32(1e-6))) * g.astype(np.float64)
+    assert np.all(np.abs(y - ref) <= 6 * 2.0 ** -24 * np.abs(ref) + 1e-30)
+
+
+def test_power_of_two_scaling_invariance():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((130, 384)).astype(np.float32)
+    g = (rng.standard_normal(384) + 1).astype(np.float32)
+    eps = 2.0 ** -140   # far below every mean square here
+    c0, s0, r0 = norm.rmsnorm_quantize(_bits(x), g, eps)
+    c1, s1, r1 = norm.rmsnorm_quantize(_bits(x * 256), g, eps)
+    np.testing.assert_array_equal(c0, c1)
+    np.testing.assert_array_equal(s0, s1)
+    np.testing.assert_array_equal(r1 * np.float32(256), r0)
+
+
+def test_constant_rows_and_column_permutation():
+    rng = np.random.default_rng(3)
+    g = (rng.standard_normal(256) + 1).astype(np.float32)
+    x = np.zeros((3, 256), np.float32)
+    x[0] = 0.75
+    x[1] = -3.0
+    x[2] = rng.standard_normal(256)
+    y, r = norm.rmsnorm(_bits(x), g, 2.0 ** -140)
+    np.testing.assert_array_equal(y[0], g)   # fl32(0.75 * fl32(1/0.75)) is exactly 1
+    np.testing.assert_array_equal(y[1], -g)
+    p = rng.permutation(256)
+    yp, _ = norm.rmsnorm(_bits(x[:, p]), g[p], 2.0 ** -140)
+    np.testing.assert_array_equal(yp, y[:, p])
+
+
+def test_quantize_matches_block_rule():
+    rng = np.random.default_rng(4)
+    x = _bits(rng.standard_normal((200, 256)))
+    c, s, r = norm.rmsnorm_quantize(x, None, 1e-6)
+    y, r2 = norm.rmsnorm(x, None, 1e-6)
+    c2, s2 = w8a8.quantize_blocks(y)
+    np.testing.assert_array_equal(c, c2)
+    np.testing.assert_array_equal(s, s2)
+    np.testing.assert_array_equal(r, r2)
