@@ -18,7 +18,8 @@ import os
 __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "forward",
            "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
-           "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes"]
+           "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
+           "w8a8_linear_rmsnorm"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -54,6 +55,9 @@ EXPORTS = {
     "sqattn_w8a8_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_w8a8_workspace_bytes": (_sz, [_i, _i]),
     "sqattn_w8a8_linear": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "sqattn_w8a8_rmsnorm_quantize": (_i, [_vp, _vp, _f, _i, _i, _vp, _vp, _vp, _vp]),
+    "sqattn_w8a8_rmsnorm_workspace_bytes": (_sz, [_i, _i]),
+    "sqattn_w8a8_linear_rmsnorm": (_i, [_vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -411,4 +415,48 @@ def w8a8_linear(x, w_codes, w_scales, bias=None, out=None, out_dtype=None, works
     w, wb = _ws(w8a8_workspace_bytes(M, K), x.device, workspace)
     _check(lib().sqattn_w8a8_linear(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(bias), M, N, K, od, _ptr(out),
                                     _ptr(w), wb, _stream(x)))
+    return out
+
+
+def _gamma(gamma, K):
+    torch = _torch()
+    if gamma is None:
+        return None
+    _dev(gamma, "gamma", torch.float32)
+    if tuple(gamma.shape) != (K,):
+        raise ValueError(f"gamma must be [{K}]")
+    return gamma
+
+
+def w8a8_rmsnorm_quantize(x, gamma=None, eps: float = 1e-6):
+    """RMSNorm of bf16 x [R, K] (gamma fp32 [K] or None) fused with the W8A8
+    block quantization: (codes, scales, inv_rms [R])."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    R, C = (int(v) for v in x.shape)
+    codes = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    scales = torch.empty((-(-R // 128), C // 128 if C % 128 == 0 else 0), dtype=torch.float32, device=x.device)
+    r = torch.empty((R,), dtype=torch.float32, device=x.device)
+    g = _gamma(gamma, C)
+    _check(lib().sqattn_w8a8_rmsnorm_quantize(_ptr(x), _ptr(g), float(eps), R, C, _ptr(codes), _ptr(scales), _ptr(r),
+                                              _stream(x)))
+    return codes, scales, r
+
+
+def w8a8_linear_rmsnorm(x, w_codes, w_scales, gamma=None, eps: float = 1e-6, bias=None, out=None, out_dtype=None,
+                        workspace=None):
+    """RMSNorm(x) W^T (+ bias): the normalization, the INT8 block quantization
+    and the block-scaled GEMM, with no normalized activations in HBM."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, N, K = _w8a8_shapes(x.shape, w_codes, w_scales, bias)
+    g = _gamma(gamma, K)
+    out, od = _out(out, (M, N), x.device, out_dtype)
+    w, wb = _ws(int(lib().sqattn_w8a8_rmsnorm_workspace_bytes(M, K)), x.device, workspace)
+    _check(lib().sqattn_w8a8_linear_rmsnorm(_ptr(x), _ptr(g), float(eps), _ptr(w_codes), _ptr(w_scales), _ptr(bias),
+                                            M, N, K, od, _ptr(out), _ptr(w), wb, _stream(x)))
     return out

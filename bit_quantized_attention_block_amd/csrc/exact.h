@@ -126,11 +126,13 @@ SQ_HD bool limb_any_below(const uint32_t* q, int pos) {
   return false;
 }
 
-// fl32(value(a) / N), nearest-even, N >= 1.  Exact: the accumulator shifted
-// left by 64 bits is divided by N in 32-bit limbs; the quotient has at least
-// 41 significant bits for any nonzero sum, so its bits below the 24 kept ones
-// plus the remainder decide the rounding.
-SQ_HD float acc192_mean_f32(Acc192 a, uint32_t N) {
+// fl32(a * 2^unit_exp / N + tiny), nearest-even, N >= 1, where `sticky`
+// says that a positive amount far below the result's last bit was left out
+// of a (it can only break ties, upward).  Exact: the accumulator shifted left
+// by 64 bits is divided by N in 32-bit limbs; the quotient has at least 41
+// significant bits for any nonzero value, so its bits below the 24 kept ones,
+// the remainder and `sticky` decide the rounding.  Overflows to +-inf.
+SQ_HD float acc192_div_f32(Acc192 a, uint32_t N, int unit_exp, bool sticky_in) {
   bool neg = (a.w2 >> 63) != 0;
   if (neg) acc192_neg(a.w0, a.w1, a.w2);
   uint32_t x[8] = {0u, 0u, (uint32_t)a.w0, (uint32_t)(a.w0 >> 32), (uint32_t)a.w1,
@@ -144,19 +146,20 @@ SQ_HD float acc192_mean_f32(Acc192 a, uint32_t N) {
   }
   int top = 7;
   while (top >= 0 && q[top] == 0) --top;
-  if (top < 0) return 0.0f;  // exact zero mean
+  if (top < 0) return 0.0f;  // exact zero (a positive sticky rest is below every binary32)
   int nb = 32 * top + (32 - __builtin_clz(q[top]));
   // value = (Q + rem/N) * 2^e
-  const int e = KMEAN_UNIT_EXP - 64;
+  const int e = unit_exp - 64;
   int lsb = e + nb - 24;
   if (lsb < -149) lsb = -149;
   int sh = lsb - e;  // >= 17
   uint32_t mant = limb_bits(q, 8, sh, 24 + 1);  // may need the 25th bit only if nb - sh == 25 (never)
   mant &= 0x1FFFFFFu;
   uint32_t rbit = limb_bits(q, 8, sh - 1, 1);
-  bool sticky = (rem != 0) || limb_any_below(q, sh - 1);
+  bool sticky = (rem != 0) || limb_any_below(q, sh - 1) || sticky_in;
   if (rbit && (sticky || (mant & 1u))) mant += 1;
   uint32_t bits = mant + ((uint32_t)(lsb + 149) << 23);
+  if (bits >= 0x7F800000u) bits = 0x7F800000u;  // past the largest binary32
   if (neg) bits |= 0x80000000u;
   union {
     uint32_t u;
@@ -165,5 +168,8 @@ SQ_HD float acc192_mean_f32(Acc192 a, uint32_t N) {
   cvt.u = bits;
   return cvt.f;
 }
+
+// fl32(value(a) / N): the K mean (units 2^-133, nothing left out).
+SQ_HD float acc192_mean_f32(Acc192 a, uint32_t N) { return acc192_div_f32(a, N, KMEAN_UNIT_EXP, false); }
 
 }  // namespace sqattn

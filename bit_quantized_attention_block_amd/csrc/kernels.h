@@ -53,6 +53,9 @@ void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 
 // W8A8 linear layer: 128x128 block quantizer and the block-scaled INT8 GEMM.
 void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* scales, hipStream_t st);
+// RMSNorm (per-row inverse RMS into inv_rms) fused with the block quantization
+void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int R, int C, int8_t* codes,
+                               float* scales, float* inv_rms, hipStream_t st);
 void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
                       int M, int N, int K, void* out, int out_bf16, hipStream_t st);
 

@@ -300,6 +300,34 @@ int sqattn_w8a8_linear(const void* x, const int8_t* w_codes, const float* w_scal
                        const float* bias, int M, int N, int K, int out_dtype, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * RMSNorm fused with the W8A8 quantization of the projection input: the
+ * normalization in front of the QKV projection of a DiT block, written as a
+ * custom kernel (digipub.cc TurboDiffusion article, paragraph on other
+ * optimizations: LayerNorm and RMSNorm reimplemented for speed).  Per row of
+ * x [rows, cols] (bf16):
+ *   mu2 = fl32(S / cols), S = sum of x^2 computed exactly (rounded once);
+ *   r   = fl32(1 / fl32(sqrt(fl32(mu2 + eps))))   (binary32 operations);
+ *   y   = fl32(fl32(x * r) * gamma)   (gamma fp32 [cols], or NULL: fl32(x * r));
+ * then y (binary32, not rounded to bf16) gets the codes and 128x128 block
+ * scales of sqattn_w8a8_quantize.
+ *   inv_rms : fp32 [rows] output, r per row (NaN for a row holding Inf/NaN).
+ *   eps     : finite, > 0.
+ * Sizes as sqattn_w8a8_quantize.
+ */
+int sqattn_w8a8_rmsnorm_quantize(const void* x, const float* gamma, float eps, int rows, int cols,
+                                 int8_t* codes, float* scales, float* inv_rms, void* stream);
+
+/* Workspace of sqattn_w8a8_linear_rmsnorm (codes, scales, inverse RMS). */
+size_t sqattn_w8a8_rmsnorm_workspace_bytes(int M, int K);
+
+/* y = RMSNorm(x) W^T (+ b) on bf16 x [M, K]: sqattn_w8a8_rmsnorm_quantize
+ * into the workspace, then sqattn_w8a8_gemm. */
+int sqattn_w8a8_linear_rmsnorm(const void* x, const float* gamma, float eps, const int8_t* w_codes,
+                               const float* w_scales, const float* bias, int M, int N, int K,
+                               int out_dtype, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 19
+    assert len(names) == 22
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -262,3 +262,16 @@ def test_strided_forward_validation():
     assert L.sqattn_forward_strided(*args(good, obad)) == INVALID
     # valid strides reach the workspace check
     assert L.sqattn_forward_strided(*args(good)) == WORKSPACE
+
+
+def test_rmsnorm_validation():
+    L = sq.lib()
+    args = lambda eps=1e-6, rows=10, cols=256, x=FAKE, inv=FAKE: [x, None, eps, rows, cols, FAKE, FAKE, inv, None]
+    assert L.sqattn_w8a8_rmsnorm_quantize(*args(eps=0.0)) == INVALID and "eps" in _err()
+    assert L.sqattn_w8a8_rmsnorm_quantize(*args(eps=float("nan"))) == INVALID
+    assert L.sqattn_w8a8_rmsnorm_quantize(*args(cols=200)) == INVALID
+    assert L.sqattn_w8a8_rmsnorm_quantize(*args(inv=None)) == INVALID and "inv_rms" in _err()
+    assert L.sqattn_w8a8_rmsnorm_quantize(*args(rows=0, x=None, inv=None)) == OK
+    assert L.sqattn_w8a8_rmsnorm_workspace_bytes(100, 256) > 100 * 256
+    lin = [FAKE, None, 1e-6, FAKE, FAKE, None, 300, 200, 384, 0, FAKE, FAKE, 1, None]
+    assert L.sqattn_w8a8_linear_rmsnorm(*lin) == WORKSPACE
