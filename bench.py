@@ -138,8 +138,15 @@ def bench_w8a8(a):
     wsb = torch.empty(sq.w8a8_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    G = torch.ones(w.K, dtype=torch.float32, device=dev) * 1.25 if a.rmsnorm else None
+    if a.rmsnorm:
+        wsb = torch.empty(sq.w8a8_rmsnorm_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+
     def step():
-        sq.w8a8_linear(X, wc, ws, bias=B, out=Y, workspace=wsb)
+        if a.rmsnorm:
+            sq.w8a8_linear_rmsnorm(X, wc, ws, gamma=G, eps=1e-6, bias=B, out=Y, workspace=wsb)
+        else:
+            sq.w8a8_linear(X, wc, ws, bias=B, out=Y, workspace=wsb)
 
     for _ in range(a.warmup):
         step()
@@ -156,7 +163,9 @@ def bench_w8a8(a):
     for _ in range(2):
         kern()
     k_ms, k_med, k_min, _ = _timed(torch, np, dev, stream, kern, reps)
+    ops = w.ops
     q_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_quantize(X), reps)[0]
+    n_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_rmsnorm_quantize(X, G, 1e-6), reps)[0]
     tops = ops / (ms * 1e-3) / 1e12
     k_tops = ops / (k_ms * 1e-3) / 1e12
     res = {
@@ -177,7 +186,9 @@ def bench_w8a8(a):
                    "out": "bf16",
                    "stages_ms": {"step_median": round(ms_med, 4), "step_min": round(ms_min, 4),
                                  "gemm_kernel": round(k_ms, 4), "gemm_kernel_median": round(k_med, 4),
-                                 "gemm_kernel_min": round(k_min, 4), "quantize_x": round(q_ms, 4)}},
+                                 "gemm_kernel_min": round(k_min, 4), "quantize_x": round(q_ms, 4),
+                                 "rmsnorm_quantize_x": round(n_ms, 4)},
+                   "rmsnorm": bool(a.rmsnorm)},
         "roofline": {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
                      "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
@@ -259,6 +270,8 @@ def main(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=None)
     ap.add_argument("--q-block", type=int, default=None,
                     help="Q scale block (1 = one scale per query row); default: the workload's")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="W8A8 workloads: the step is RMSNorm + quantization + GEMM (fused normalization)")
     ap.add_argument("--block-density", type=float, default=None,
                     help="block-sparse attention: fraction of the non-local blocks kept")
     a = ap.parse_args(argv)

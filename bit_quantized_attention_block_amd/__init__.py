@@ -19,7 +19,7 @@ __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "f
            "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
-           "w8a8_linear_rmsnorm"]
+           "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -428,6 +428,10 @@ def _gamma(gamma, K):
     return gamma
 
 
+def w8a8_rmsnorm_workspace_bytes(M, K) -> int:
+    return int(lib().sqattn_w8a8_rmsnorm_workspace_bytes(M, K))
+
+
 def w8a8_rmsnorm_quantize(x, gamma=None, eps: float = 1e-6):
     """RMSNorm of bf16 x [R, K] (gamma fp32 [K] or None) fused with the W8A8
     block quantization: (codes, scales, inv_rms [R])."""
@@ -456,7 +460,7 @@ def w8a8_linear_rmsnorm(x, w_codes, w_scales, gamma=None, eps: float = 1e-6, bia
     M, N, K = _w8a8_shapes(x.shape, w_codes, w_scales, bias)
     g = _gamma(gamma, K)
     out, od = _out(out, (M, N), x.device, out_dtype)
-    w, wb = _ws(int(lib().sqattn_w8a8_rmsnorm_workspace_bytes(M, K)), x.device, workspace)
+    w, wb = _ws(w8a8_rmsnorm_workspace_bytes(M, K), x.device, workspace)
     _check(lib().sqattn_w8a8_linear_rmsnorm(_ptr(x), _ptr(g), float(eps), _ptr(w_codes), _ptr(w_scales), _ptr(bias),
                                             M, N, K, od, _ptr(out), _ptr(w), wb, _stream(x)))
     return out

@@ -52,6 +52,7 @@ constexpr int QB = 128;                  // scale block edge
 // final rounding needs.  The 64 lane sums are combined exactly in-wave and
 // the quotient by C rounded once.
 constexpr int RMS_WINDOW = 150;
+constexpr int RMS_FAST = RMS_WINDOW - 40;  // fast 64-bit window: shifts 110 .. 150
 
 __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ x, int R, int C, float eps,
                                                       float* __restrict__ inv_rms) {
@@ -71,10 +72,19 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
   const int ulow = 2 * max(emax, 1) - 2 - RMS_WINDOW;  // window unit (exponent, units of 2^-266)
+  // squares within 2^40 of the largest go to a 64-bit window (each below
+  // 2^56; the window is emptied into the full accumulator every 16 loads,
+  // 128 squares, so it stays below 2^63), the rest to the full accumulator
+  // or, below the window, to the sticky bit
   Acc192 acc;
   acc192_zero(acc);
+  uint64_t win = 0;
   bool sticky = false;
-  for (int k = lane * 8; k < C; k += 512) {
+  for (int k = lane * 8, it = 0; k < C; k += 512, ++it) {
+    if ((it & 15) == 15) {
+      acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
+      win = 0;
+    }
     const v4i w = *(const v4i*)(xr + k);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -82,13 +92,17 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict
       const uint32_t E = (b >> 7) & 0xFF;
       const uint32_t M = (b & 0x7F) | (E ? 0x80u : 0u);
       const int sh = 2 * (int)(E ? E : 1) - 2 - ulow;
-      if (M == 0) continue;
-      if (sh < 0)
-        sticky = true;
-      else
-        acc192_add_shifted(acc, M * M, sh, false);
+      if (sh >= RMS_FAST) {
+        win += (uint64_t)(M * M) << (sh - RMS_FAST);
+      } else if (M != 0) {
+        if (sh < 0)
+          sticky = true;
+        else
+          acc192_add_shifted(acc, M * M, sh, false);
+      }
     }
   }
+  acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     Acc192 t;

@@ -83,3 +83,18 @@ def test_full_size_qkv_input():
     c_ref, s_ref, _ = norm.rmsnorm_quantize(x[rows], g, 1e-6)
     assert np.array_equal(host(scales)[blocks].view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(host(codes)[rows], c_ref)
+
+
+def test_long_rows_fill_the_fast_window():
+    """Rows of 131072 values of the largest significand at one exponent: every
+    square sits at the top of the 64-bit window, which must be emptied into
+    the full accumulator before it overflows."""
+    R, C = 8, 131072
+    rng = np.random.default_rng(9)
+    x = np.where(rng.random((R, C)) < 0.5, -1.9921875, 1.9921875).astype(np.float32)
+    x[1] *= 2.0 ** 40
+    x[2, ::3] = 2.0 ** -20          # squares far below the window's top
+    xb = W.f32_to_bf16_bits(x)
+    codes, scales, r = sq.w8a8_rmsnorm_quantize(dev_bf16(xb), None, 1e-6)
+    torch.cuda.synchronize()
+    _check(xb, None, 1e-6, codes, scales, r)
