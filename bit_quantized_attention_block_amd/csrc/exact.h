@@ -84,6 +84,26 @@ SQ_HD void acc192_add_i64_shl(Acc192& a, int64_t v, int s) {
   acc192_add(a, 0, v1, v2);
 }
 
+// a += v * 2^s for an unsigned 64-bit v, 0 <= s < 192 (bits past 2^192 are lost).
+SQ_HD void acc192_add_u64_shl(Acc192& a, uint64_t v, int s) {
+  uint64_t w0 = 0, w1 = 0, w2 = 0;
+  if (s < 64) {
+    w0 = v << s;
+    w1 = s ? v >> (64 - s) : 0;
+  } else if (s < 128) {
+    const int t = s - 64;
+    w1 = v << t;
+    w2 = t ? v >> (64 - t) : 0;
+  } else {
+    w2 = v << (s - 128);
+  }
+  acc192_add(a, w0, w1, w2);
+}
+
+SQ_HD bool acc192_is_zero(const Acc192& a) { return (a.w0 | a.w1 | a.w2) == 0; }
+
+SQ_HD bool acc192_is_neg(const Acc192& a) { return (a.w2 >> 63) != 0; }
+
 // Adds one bf16 value (16-bit pattern) to the window or the full accumulator.
 // Returns true if the value is out of range (|x| >= 2^33, Inf or NaN).
 SQ_HD bool kmean_accumulate(Acc192& acc, int64_t& win, uint32_t b) {

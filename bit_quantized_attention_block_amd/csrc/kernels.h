@@ -52,6 +52,10 @@ void launch_attention_bf16(const AttnParams& p, int d, hipStream_t st);
 void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 
 // W8A8 linear layer: 128x128 block quantizer and the block-scaled INT8 GEMM.
+// RMSNorm: inv_rms[r] = fl32(1 / fl32(sqrt(fl32(mean_k x[r,k]^2 + eps)))), the mean
+// square rounded once from its exact value (norm.hip).
+void launch_rms_inverse(const uint16_t* x, int R, int C, float eps, float* inv_rms, hipStream_t st);
+
 void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* scales, hipStream_t st);
 // RMSNorm (per-row inverse RMS into inv_rms) fused with the block quantization
 void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int R, int C, int8_t* codes,

@@ -38,92 +38,6 @@ constexpr int QB = 128;                  // scale block edge
 // quantizer
 // ---------------------------------------------------------------------------
 
-// ---------------------------------------------------------------------------
-// RMSNorm (the normalization in front of the projections; digipub.cc
-// TurboDiffusion article, paragraph on other optimizations): per row,
-// mu2 = fl32(S / C) with S = sum x^2 exact, r = fl32(1 / fl32(sqrt(fl32(mu2 + eps)))).
-// ---------------------------------------------------------------------------
-
-// One wave per row (4 rows per 256-thread work-group).  Pass 1 finds the
-// row's largest exponent; pass 2 adds every square exactly into a 192-bit
-// fixed-point accumulator whose unit sits 150 bits below the largest square
-// (a square of biased exponent E and significand M is M^2 * 2^(2 max(E,1) - 2)
-// units of 2^-266); smaller squares only set a sticky bit, which is all the
-// final rounding needs.  The 64 lane sums are combined exactly in-wave and
-// the quotient by C rounded once.
-constexpr int RMS_WINDOW = 150;
-constexpr int RMS_FAST = RMS_WINDOW - 40;  // fast 64-bit window: shifts 110 .. 150
-
-__global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ x, int R, int C, float eps,
-                                                      float* __restrict__ inv_rms) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;  // whole waves leave
-  const uint16_t* xr = x + (long long)row * C;
-  int emax = 0;
-  for (int k = lane * 8; k < C; k += 512) {
-    const v4i w = *(const v4i*)(xr + k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t u = (uint32_t)w[j];
-      emax = max(emax, max((int)((u >> 7) & 0xFF), (int)((u >> 23) & 0xFF)));
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
-  const int ulow = 2 * max(emax, 1) - 2 - RMS_WINDOW;  // window unit (exponent, units of 2^-266)
-  // squares within 2^40 of the largest go to a 64-bit window (each below
-  // 2^56; the window is emptied into the full accumulator every 16 loads,
-  // 128 squares, so it stays below 2^63), the rest to the full accumulator
-  // or, below the window, to the sticky bit
-  Acc192 acc;
-  acc192_zero(acc);
-  uint64_t win = 0;
-  bool sticky = false;
-  for (int k = lane * 8, it = 0; k < C; k += 512, ++it) {
-    if ((it & 15) == 15) {
-      acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
-      win = 0;
-    }
-    const v4i w = *(const v4i*)(xr + k);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t E = (b >> 7) & 0xFF;
-      const uint32_t M = (b & 0x7F) | (E ? 0x80u : 0u);
-      const int sh = 2 * (int)(E ? E : 1) - 2 - ulow;
-      if (sh >= RMS_FAST) {
-        win += (uint64_t)(M * M) << (sh - RMS_FAST);
-      } else if (M != 0) {
-        if (sh < 0)
-          sticky = true;
-        else
-          acc192_add_shifted(acc, M * M, sh, false);
-      }
-    }
-  }
-  acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    Acc192 t;
-    t.w0 = __shfl_xor(acc.w0, o, 64);
-    t.w1 = __shfl_xor(acc.w1, o, 64);
-    t.w2 = __shfl_xor(acc.w2, o, 64);
-    acc192_add(acc, t);
-    sticky |= __shfl_xor((int)sticky, o, 64) != 0;
-  }
-  if (lane == 0) {
-    float r;
-    if (emax == 255) {
-      r = __builtin_nanf("");  // Inf or NaN in the row
-    } else {
-      const float mu2 = acc192_div_f32(acc, (uint32_t)C, ulow - 266, sticky);
-      r = 1.0f / sqrtf(mu2 + eps);  // binary32, each operation correctly rounded
-    }
-    inv_rms[row] = r;
-  }
-}
-
 // grid (C/128, ceil(R/128)), 256 threads.  Thread t holds columns
 // 8 (t % 16) .. +8 of rows t/16 + 16 j (j < 8) of the block.  NORM: the
 // block of y = fl32(fl32(x * r_row) * gamma_col) (gamma may be null) instead
@@ -399,7 +313,7 @@ void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* sc
 
 void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int R, int C, int8_t* codes,
                                float* scales, float* inv_rms, hipStream_t st) {
-  hipLaunchKernelGGL(rms_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, st, x, R, C, eps, inv_rms);
+  launch_rms_inverse(x, R, C, eps, inv_rms, st);
   hipLaunchKernelGGL(w8a8_quant_kernel<true>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
                      scales, inv_rms, gamma);
 }

@@ -98,3 +98,22 @@ def test_long_rows_fill_the_fast_window():
     codes, scales, r = sq.w8a8_rmsnorm_quantize(dev_bf16(xb), None, 1e-6)
     torch.cuda.synchronize()
     _check(xb, None, 1e-6, codes, scales, r)
+
+
+def test_mean_square_next_to_a_midpoint():
+    """Rows whose kept squares leave the mean square just under a binary32
+    midpoint and whose squares 2^150 and 2^300 below the largest decide the
+    rounding: tie (to even), above and below, settled one or two levels
+    down.  Each row's two candidates give different inverse RMS values."""
+    import norm_cases as NC
+    rows = [NC.mean_square_row(kind, seed=11 * i) for i, kind in enumerate(NC.KINDS)]
+    x1 = np.stack([b for b, _, _, _ in rows])
+    want = np.array([w for _, _, _, w in rows], np.float32)
+    # each row also tiled 4 times (1024 columns, same mean square, every
+    # level sum and gap scaled by 4: the same decisions, over two loads a lane)
+    for xb in (x1, np.tile(x1, (1, 4))):
+        print(f"case midpoint rows R={xb.shape[0]} C={xb.shape[1]}", flush=True)
+        codes, scales, r = sq.w8a8_rmsnorm_quantize(dev_bf16(xb), None, NC.EPS)
+        torch.cuda.synchronize()
+        _check(xb, None, NC.EPS, codes, scales, r)
+        assert np.array_equal(host(r), np.float32(1) / np.sqrt(want + np.float32(NC.EPS)))

@@ -95,3 +95,24 @@ def test_quantize_matches_block_rule():
     np.testing.assert_array_equal(c, c2)
     np.testing.assert_array_equal(s, s2)
     np.testing.assert_array_equal(r, r2)
+
+
+def test_mean_square_next_to_a_midpoint():
+    """Crafted rows (tests/norm_cases.py) whose exact mean square is, by
+    construction, exactly on, just above or just below the midpoint of two
+    adjacent binary32 numbers, the deciding squares lying 2^150 and 2^300
+    below the row's largest: the oracle's mean square must be the intended
+    neighbour (even one for the tie) and the nearest binary32 by brute force."""
+    import norm_cases as NC
+    for i, kind in enumerate(NC.KINDS):
+        bits, lo, hi, want = NC.mean_square_row(kind, seed=11 * i)
+        exact = NC.exact_mean_square(bits)
+        mid = (Fraction(float(lo)) + Fraction(float(hi))) / 2
+        side = {"even": 0, "hi": 1, "lo": -1}[NC.KINDS[kind]]
+        assert (exact > mid) - (exact < mid) == side, kind
+        mu2, r = norm.rms_inverse(bits[None, :], NC.EPS)
+        assert mu2[0] == want, kind
+        _is_nearest_f32(mu2[0], exact)
+        for reps in (2, 4):      # tiled rows: same mean square
+            mu2t, _ = norm.rms_inverse(np.tile(bits, reps)[None, :], NC.EPS)
+            assert mu2t[0] == want, kind
