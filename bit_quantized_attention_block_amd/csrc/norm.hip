@@ -116,6 +116,42 @@ __device__ float settle_rounding(const uint16_t* xr, int C, int lane, const Acc1
   return lo;  // not reached: below the third level no square is left out
 }
 
+__device__ __forceinline__ int chunk_emax(const v4i w) {
+  int e = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = (uint32_t)w[j];
+    e = max(e, max((int)((u >> 7) & 0xFF), (int)((u >> 23) & 0xFF)));
+  }
+  return e;
+}
+
+// The 8 squares of one 16-byte chunk: within 2^40 of the level's top into the
+// 64-bit window `win` (each below 2^56), the rest of the level into `acc`,
+// below it into the sticky bit.  Zero values add nothing.
+__device__ __forceinline__ void chunk_add(const v4i w, int u0, Acc192& acc, uint64_t& win, bool& sticky) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t E = (b >> 7) & 0xFF;
+    const uint32_t M = (b & 0x7F) | (E ? 0x80u : 0u);
+    const int sh = 2 * (int)(E ? E : 1) - 2 - u0;
+    if (sh >= RMS_FAST) {
+      win += (uint64_t)(M * M) << (sh - RMS_FAST);
+    } else if (M != 0) {
+      if (sh < 0)
+        sticky = true;
+      else
+        acc192_add_shifted(acc, M * M, sh, false);
+    }
+  }
+}
+
+// Two passes over the row (the second mostly from cache); the window is
+// emptied into the full accumulator every 16 chunks (128 squares, so it
+// stays below 2^63).  The pass is bound by the ~14 integer operations per
+// square, not by memory: a variant that kept rows of up to 6144 columns in
+// registers (one read) needed 170 VGPRs and ran slower.
 __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ x, int R, int C, float eps,
                                                       float* __restrict__ inv_rms) {
   const int lane = threadIdx.x & 63;
@@ -123,21 +159,10 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict
   if (row >= R) return;  // whole waves leave
   const uint16_t* xr = x + (long long)row * C;
   int emax = 0;
-  for (int k = lane * 8; k < C; k += 512) {
-    const v4i w = *(const v4i*)(xr + k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t u = (uint32_t)w[j];
-      emax = max(emax, max((int)((u >> 7) & 0xFF), (int)((u >> 23) & 0xFF)));
-    }
-  }
+  for (int k = lane * 8; k < C; k += 512) emax = max(emax, chunk_emax(*(const v4i*)(xr + k)));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) emax = max(emax, __shfl_xor(emax, o, 64));
   const int u0 = 2 * max(emax, 1) - 2 - RMS_WINDOW;
-  // squares within 2^40 of the largest go to a 64-bit window (each below
-  // 2^56; the window is emptied into the full accumulator every 16 loads,
-  // 128 squares, so it stays below 2^63), the rest of the level to the full
-  // accumulator, and below it to the sticky bit
   Acc192 acc;
   acc192_zero(acc);
   uint64_t win = 0;
@@ -147,22 +172,7 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict
       acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
       win = 0;
     }
-    const v4i w = *(const v4i*)(xr + k);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t E = (b >> 7) & 0xFF;
-      const uint32_t M = (b & 0x7F) | (E ? 0x80u : 0u);
-      const int sh = 2 * (int)(E ? E : 1) - 2 - u0;
-      if (sh >= RMS_FAST) {
-        win += (uint64_t)(M * M) << (sh - RMS_FAST);
-      } else if (M != 0) {
-        if (sh < 0)
-          sticky = true;
-        else
-          acc192_add_shifted(acc, M * M, sh, false);
-      }
-    }
+    chunk_add(*(const v4i*)(xr + k), u0, acc, win, sticky);
   }
   acc192_add_i64_shl(acc, (int64_t)win, RMS_FAST);
   wave_sum(acc, sticky);
