@@ -374,7 +374,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-480p")
     ap.add_argument("--reps", type=int, default=3)
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
     if a.cmd == "target":
