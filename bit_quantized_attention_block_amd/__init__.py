@@ -19,7 +19,7 @@ __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "f
            "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
-           "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes"]
+           "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes", "forward_qknorm"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -49,6 +49,9 @@ EXPORTS = {
     "sqattn_forward_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "sqattn_forward_strided": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _i, _vp, _vp, _vp, _sz, _vp,
                                     _vp]),
+    "sqattn_forward_qknorm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _vp]),
+    "sqattn_forward_qknorm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _i, _vp, _vp, _vp,
+                                   _sz, _vp, _vp]),
     "sqattn_attend_quantized_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                             _vp, _vp]),
     "sqattn_w8a8_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
@@ -273,7 +276,24 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
     return out
 
 
-def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask):
+def forward_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps: float = 1e-6, scale: float | None = None, pv="bf16",
+                   q_block: int = 128, out=None, workspace=None, out_dtype=None, block_mask=None):
+    """Attention with the per-token RMSNorm of q and k (over each token's H*d
+    features, weights gamma_q / gamma_k fp32 [H*d] or None) fused into their
+    quantization; sqattn_forward_qknorm.  q, k, v: bf16 [B,H,N,d] views whose
+    q and k head stride is d (e.g. slices of a fused [B,N,3,H,d] projection
+    output, permuted)."""
+    torch = _torch()
+    for g, n in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k")):
+        if g is not None:
+            _dev(g, n, torch.float32)
+            if g.numel() != q.shape[1] * q.shape[3]:
+                raise ValueError(f"{n} has {g.numel()} elements, expected H*d = {q.shape[1] * q.shape[3]}")
+    return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask,
+                            qkn=(gamma_q, gamma_k, float(eps)))
+
+
+def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask, qkn=None):
     torch = _torch()
     st = []
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -291,13 +311,21 @@ def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, blo
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, d)}")
     ost = _row_strides(out, "out", out_dtype)
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32
-    w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
     o = _opts(q_block, od)
     m = _mask(block_mask, B, H, N) if block_mask is not None else None
     ins = (ctypes.c_int64 * 9)(*st)
     outs = (ctypes.c_int64 * 3)(*ost)
-    _check(lib().sqattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, float(scale), _PV[pv],
-                                        _ptr(m), _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
+    if qkn is None:
+        w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
+        _check(lib().sqattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, float(scale),
+                                            _PV[pv], _ptr(m), _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
+    else:
+        need = int(lib().sqattn_forward_qknorm_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
+        w, wb = _ws(need, q.device, workspace)
+        gq, gk, eps = qkn
+        _check(lib().sqattn_forward_qknorm(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, _ptr(gq), _ptr(gk),
+                                           eps, float(scale), _PV[pv], _ptr(m), _ptr(out), _ptr(w), wb,
+                                           _stream(q), ctypes.byref(o)))
     return out
 
 

@@ -283,10 +283,19 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
   return forward_layout(z, pv_dtype, o.q_block).total;
 }
 
+// q/k RMSNorm fused into the quantization: the per-token factors of q and
+// of k, B*N floats each, after the forward's own workspace
+struct QkNorm {
+  const float* gamma_q;
+  const float* gamma_k;
+  float eps;
+};
+size_t qknorm_extra(const Sizes& z, int B) { return align_up((size_t)(2LL * B * z.N) * 4); }
+
 static int forward_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
                         int pv_dtype, const uint8_t* mask, void* out, void* workspace, size_t workspace_bytes,
                         void* stream, const sqattn_opts* opts, const int64_t* in_strides = nullptr,
-                        const int64_t* out_strides = nullptr) {
+                        const int64_t* out_strides = nullptr, const QkNorm* qkn = nullptr) {
   g_err.clear();
   int s;
   Sizes z;
@@ -304,19 +313,38 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
                     "strides must be non-negative multiples of 8 elements (16-byte rows), at most 2^40");
     lay[i] = sqattn::Lay{st[0], st[1], st[2], H};
   }
+  if (qkn) {
+    if (!(qkn->eps > 0.0f) || !std::isfinite(qkn->eps))
+      return fail(SQATTN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if ((qkn->gamma_q && (s = check_ptr(qkn->gamma_q, "gamma_q", 4))) ||
+        (qkn->gamma_k && (s = check_ptr(qkn->gamma_k, "gamma_k", 4))))
+      return s;
+    if (H > 1 && (lay[0].sh != d || lay[1].sh != d))
+      return fail(SQATTN_ERR_INVALID_ARG,
+                  "q/k RMSNorm needs each token's H*d values of q and k contiguous (head stride d)");
+  }
   const FwdLayout L = forward_layout(z, pv_dtype, o.q_block);
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;
-  if ((s = ws.acquire(workspace, workspace_bytes, L.total, st))) return s;
+  if ((s = ws.acquire(workspace, workspace_bytes, L.total + (qkn ? qknorm_extra(z, B) : 0), st))) return s;
   const int BH = (int)z.BH;
   int8_t* qi = ws.at<int8_t>(L.q_i8);
   int8_t* ki = ws.at<int8_t>(L.k_i8);
   float* qs = ws.at<float>(L.q_scale);
   float* ks = ws.at<float>(L.k_scale);
   float* km = ws.at<float>(L.k_mean);
-  sqattn::launch_quant_i8((const uint16_t*)q, lay[0], BH, N, d, o.q_block, nullptr, qi, qs, st);
-  sqattn::launch_kmean((const uint16_t*)k, lay[1], BH, N, d, ws.at<uint64_t>(L.partial), km, st);
-  sqattn::launch_quant_i8((const uint16_t*)k, lay[1], BH, N, d, o.k_block, km, ki, ks, st);
+  sqattn::RowNorm nq, nk;
+  if (qkn) {
+    float* rq = ws.at<float>(L.total);
+    float* rk = rq + (size_t)B * N;
+    sqattn::launch_rms_inverse_rows((const uint16_t*)q, B, N, H * d, lay[0].sb, lay[0].sn, qkn->eps, rq, st);
+    sqattn::launch_rms_inverse_rows((const uint16_t*)k, B, N, H * d, lay[1].sb, lay[1].sn, qkn->eps, rk, st);
+    nq = sqattn::RowNorm{rq, qkn->gamma_q};
+    nk = sqattn::RowNorm{rk, qkn->gamma_k};
+  }
+  sqattn::launch_quant_i8((const uint16_t*)q, lay[0], BH, N, d, o.q_block, nullptr, qi, qs, st, nq);
+  sqattn::launch_kmean((const uint16_t*)k, lay[1], BH, N, d, ws.at<uint64_t>(L.partial), km, st, nk);
+  sqattn::launch_quant_i8((const uint16_t*)k, lay[1], BH, N, d, o.k_block, km, ki, ks, st, nk);
   float* vs = nullptr;
   if (pv_dtype == SQATTN_PV_BF16) {
     sqattn::launch_v_tiles_bf16((const uint16_t*)v, lay[2], BH, N, d, ws.at<uint16_t>(L.vt), st);
@@ -343,7 +371,8 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   p.lo = lay[3];
   sqattn::launch_attention(p, d, pv_dtype, st);
-  return hip_check(mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
+  return hip_check(qkn ? "sqattn_forward_qknorm launch"
+                       : mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
 }
 
 int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
@@ -373,6 +402,32 @@ int sqattn_forward_sparse(const void* q, const void* k, const void* v, int B, in
   }
   return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, block_mask, out, workspace, workspace_bytes, stream,
                       opts);
+}
+
+size_t sqattn_forward_qknorm_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sqattn_opts* opts) {
+  std::string keep = g_err;
+  Sizes z;
+  Opts o;
+  if (check_shape(B, H, N, d, &z) || (pv_dtype != 0 && pv_dtype != 1) || resolve_opts(opts, &o)) {
+    g_err = keep;
+    return 0;
+  }
+  return forward_layout(z, pv_dtype, o.q_block).total + qknorm_extra(z, B);
+}
+
+int sqattn_forward_qknorm(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                          const int64_t* in_strides, const int64_t* out_strides, const float* gamma_q,
+                          const float* gamma_k, float eps, float scale, int pv_dtype, const uint8_t* block_mask,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream,
+                          const sqattn_opts* opts) {
+  if (!in_strides && H > 1) {
+    g_err.clear();
+    return fail(SQATTN_ERR_INVALID_ARG,
+                "q/k RMSNorm needs in_strides with head stride d for q and k (each token's H*d values contiguous)");
+  }
+  const QkNorm n{gamma_q, gamma_k, eps};
+  return forward_impl(q, k, v, B, H, N, d, scale, pv_dtype, block_mask, out, workspace, workspace_bytes, stream,
+                      opts, in_strides, out_strides, &n);
 }
 
 int sqattn_forward(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,

@@ -19,11 +19,20 @@ __host__ __device__ inline long long lay_row(const Lay& l, long long bh, long lo
   return (bh / l.H) * l.sb + (bh % l.H) * l.sh + r * l.sn;
 }
 
+// RMSNorm applied on load (the per-token q/k normalization in front of
+// attention): a bf16 value x of token n of batch b, head h, channel c is read
+// as bf16(fl32(fl32(x * r[b*N + n]) * gamma[h*d + c])) (gamma NULL: weight 1),
+// bf16 rounding to nearest even.  Inactive when r is NULL.
+struct RowNorm {
+  const float* r = nullptr;
+  const float* gamma = nullptr;
+};
+
 int kmean_chunks(int BH, int N);
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
-                  hipStream_t st);
+                  hipStream_t st, const RowNorm& nm = RowNorm{});
 void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
-                     int8_t* codes, float* scales, hipStream_t st);
+                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm = RowNorm{});
 void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st);
 void launch_quant_v_fp8(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
                         float* scales, hipStream_t st);
@@ -55,6 +64,10 @@ void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 // RMSNorm: inv_rms[r] = fl32(1 / fl32(sqrt(fl32(mean_k x[r,k]^2 + eps)))), the mean
 // square rounded once from its exact value (norm.hip).
 void launch_rms_inverse(const uint16_t* x, int R, int C, float eps, float* inv_rms, hipStream_t st);
+// the same over B*N token rows of C contiguous values each, row (b, n) at
+// x + b*sb + n*sn, into inv_rms[b*N + n]
+void launch_rms_inverse_rows(const uint16_t* x, int B, int N, int C, long long sb, long long sn, float eps,
+                             float* inv_rms, hipStream_t st);
 
 void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* scales, hipStream_t st);
 // RMSNorm (per-row inverse RMS into inv_rms) fused with the block quantization

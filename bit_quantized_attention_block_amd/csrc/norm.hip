@@ -152,12 +152,14 @@ __device__ __forceinline__ void chunk_add(const v4i w, int u0, Acc192& acc, uint
 // stays below 2^63).  The pass is bound by the ~14 integer operations per
 // square, not by memory: a variant that kept rows of up to 6144 columns in
 // registers (one read) needed 170 VGPRs and ran slower.
-__global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ x, int R, int C, float eps,
+// Row `row` (of R) starts at x + (row / rn) * sb + (row % rn) * sn.
+__global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict__ x, int R, int C, int rn,
+                                                      long long sb, long long sn, float eps,
                                                       float* __restrict__ inv_rms) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;  // whole waves leave
-  const uint16_t* xr = x + (long long)row * C;
+  const uint16_t* xr = x + (long long)(row / rn) * sb + (long long)(row % rn) * sn;
   int emax = 0;
   for (int k = lane * 8; k < C; k += 512) emax = max(emax, chunk_emax(*(const v4i*)(xr + k)));
 #pragma unroll
@@ -190,7 +192,14 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const uint16_t* __restrict
 }  // namespace
 
 void launch_rms_inverse(const uint16_t* x, int R, int C, float eps, float* inv_rms, hipStream_t st) {
-  hipLaunchKernelGGL(rms_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, st, x, R, C, eps, inv_rms);
+  hipLaunchKernelGGL(rms_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, st, x, R, C, R, 0LL, (long long)C, eps,
+                     inv_rms);
+}
+
+void launch_rms_inverse_rows(const uint16_t* x, int B, int N, int C, long long sb, long long sn, float eps,
+                             float* inv_rms, hipStream_t st) {
+  const int R = B * N;
+  hipLaunchKernelGGL(rms_inv_kernel, dim3((R + 3) / 4), dim3(256), 0, st, x, R, C, N, sb, sn, eps, inv_rms);
 }
 
 }  // namespace sqattn

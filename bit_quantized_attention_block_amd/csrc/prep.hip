@@ -21,6 +21,35 @@
 namespace sqattn {
 
 // ---------------------------------------------------------------------------
+// RMSNorm on load (RowNorm): the q/k normalization over each token's H*d
+// features (digipub.cc TurboDiffusion article, paragraph on other
+// optimizations), applied to 16-byte chunks of eight bf16 values of one row
+// as they are read, with the per-token factor r computed beforehand
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t bf16_rne(float y) {
+  const uint32_t u = __float_as_uint(y);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;  // NaN: a quiet NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;                             // nearest even (Inf stays)
+}
+// bf16(fl32(fl32(x * r) * g)) for the eight values of w (g = 1 without a weight: exact)
+__device__ __forceinline__ v4i norm_chunk(v4i w, float r, const float (&g)[8]) {
+  v4i o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = (uint32_t)w[j];
+    const uint32_t lo = bf16_rne((bf16_bits_to_f32(u & 0xFFFFu) * r) * g[2 * j]);
+    const uint32_t hi = bf16_rne((bf16_bits_to_f32(u >> 16) * r) * g[2 * j + 1]);
+    o[j] = (int)(lo | (hi << 16));
+  }
+  return o;
+}
+// the weights of channels c0 .. c0+7 of head bh % H
+__device__ __forceinline__ void norm_weights(const RowNorm& nm, long long bh, int H, int D, int c0, float (&g)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) g[j] = nm.gamma ? nm.gamma[(bh % H) * D + c0 + j] : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
 // exact K mean
 // ---------------------------------------------------------------------------
 
@@ -28,10 +57,10 @@ namespace sqattn {
 // [c*rows_per_chunk, min(N, (c+1)*rows_per_chunk)).  Thread t reads channels
 // (t % CPR)*8 .. +8 (CPR = D/8 16-byte pieces per row) of rows
 // r0 + t/CPR + j*RPP (RPP = 256/CPR rows per pass).
-template <int D>
+template <int D, bool NORM>
 __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __restrict__ k, Lay lk, int N,
                                                             int rows_per_chunk,
-                                                            uint64_t* __restrict__ partial) {
+                                                            uint64_t* __restrict__ partial, RowNorm nm) {
   constexpr int CPR = D / 8;
   constexpr int RPP = 256 / CPR;
   const int chunk = blockIdx.x, S = gridDim.x;
@@ -50,9 +79,13 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
     win[j] = 0;
   }
   bool bad = false;
+  float gw[8];
+  if constexpr (NORM) norm_weights(nm, bh, lk.H, D, cg * 8, gw);
+  const float* rr = NORM ? nm.r + (bh / lk.H) * N : nullptr;
 #pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(kh + (long long)r * lk.sn + cg * 8);
+    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -117,11 +150,11 @@ __device__ __forceinline__ float block_max_256(float v, float* sh) {
 
 // grid (nblocks, B*H), 256 threads.  One work-group per block of `block` rows.
 // mean == nullptr: plain Q.  Otherwise x = fl32(K - mean[c]) (IEEE subtract).
-template <int D>
+template <int D, bool NORM>
 __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, Lay lx, int N, int block,
                                                        const float* __restrict__ mean,
                                                        int8_t* __restrict__ codes,
-                                                       float* __restrict__ scales) {
+                                                       float* __restrict__ scales, RowNorm nm) {
   constexpr int CPR = D / 8;
   constexpr int RPP = 256 / CPR;
   __shared__ float sh[4];
@@ -140,10 +173,14 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
     mean_nan |= (mu[j] != mu[j]);
   }
 
+  float gw[8];
+  if constexpr (NORM) norm_weights(nm, bh, lx.H, D, cg * 8, gw);
+  const float* rr = NORM ? nm.r + (bh / lx.H) * N : nullptr;
   float amax = 0.0f;
 #pragma unroll 4
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
+    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -165,6 +202,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
 #pragma unroll 2
   for (int r = r0 + rg; r < r1; r += RPP) {
     v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
+    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -188,10 +226,10 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
 // one query row).  CPR threads own a row (8 channels each), RPW rows per
 // work-group; the row's absmax is reduced over its CPR lanes, which lie in
 // one wave.  Same rule: s = fl32(absmax/127), code = clamp(rne(fl32(x/s))).
-template <int D>
+template <int D, bool NORM>
 __global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __restrict__ x, Lay lx, int N,
                                                             int8_t* __restrict__ codes,
-                                                            float* __restrict__ scales) {
+                                                            float* __restrict__ scales, RowNorm nm) {
   constexpr int CPR = D / 8;
   constexpr int RPW = 256 / CPR;
   const long long bh = blockIdx.y;
@@ -199,7 +237,12 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __re
   const int r = blockIdx.x * RPW + t / CPR;
   const bool ok = r < N;
   const long long base = (bh * N + (ok ? r : 0)) * D + cg * 8;
-  const v4i w = ok ? *(const v4i*)(x + lay_row(lx, bh, r) + cg * 8) : v4i{0, 0, 0, 0};
+  v4i w = ok ? *(const v4i*)(x + lay_row(lx, bh, r) + cg * 8) : v4i{0, 0, 0, 0};
+  if constexpr (NORM) {
+    float gw[8];
+    norm_weights(nm, bh, lx.H, D, cg * 8, gw);
+    if (ok) w = norm_chunk(w, nm.r[(bh / lx.H) * N + r], gw);
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -373,6 +416,18 @@ __global__ __launch_bounds__(256) void v_tiles_fp8_kernel(const uint8_t* __restr
       hipLaunchKernelGGL(KERNEL<64>, GRID, BLOCK, 0, STREAM, __VA_ARGS__);          \
   } while (0)
 
+#define SQ_DISPATCH_DN(d, norm, KERNEL, GRID, BLOCK, STREAM, ...)                  \
+  do {                                                                              \
+    if ((d) == 128 && (norm))                                                       \
+      hipLaunchKernelGGL((KERNEL<128, true>), GRID, BLOCK, 0, STREAM, __VA_ARGS__); \
+    else if ((d) == 128)                                                            \
+      hipLaunchKernelGGL((KERNEL<128, false>), GRID, BLOCK, 0, STREAM, __VA_ARGS__); \
+    else if (norm)                                                                  \
+      hipLaunchKernelGGL((KERNEL<64, true>), GRID, BLOCK, 0, STREAM, __VA_ARGS__);  \
+    else                                                                            \
+      hipLaunchKernelGGL((KERNEL<64, false>), GRID, BLOCK, 0, STREAM, __VA_ARGS__); \
+  } while (0)
+
 int kmean_chunks(int BH, int N) {
   // enough work-groups to cover the chip a few times, each at least 256 rows;
   // at most 2^18 rows per chunk so that each thread adds at most 2^14 values
@@ -387,10 +442,11 @@ int kmean_chunks(int BH, int N) {
 }
 
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
-                  hipStream_t st) {
+                  hipStream_t st, const RowNorm& nm) {
   int S = kmean_chunks(BH, N);
   int rows = (N + S - 1) / S;
-  SQ_DISPATCH_D(d, kmean_partial_kernel, dim3(S, BH), dim3(256), st, k, lk, N, rows, partial);
+  SQ_DISPATCH_DN(d, nm.r != nullptr, kmean_partial_kernel, dim3(S, BH), dim3(256), st, k, lk, N, rows, partial,
+                 nm);
   if (d == 128)
     hipLaunchKernelGGL(kmean_finalize_kernel<128>, dim3(BH), dim3(128), 0, st, partial, S, N, mean);
   else
@@ -398,15 +454,16 @@ void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64
 }
 
 void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
-                     int8_t* codes, float* scales, hipStream_t st) {
+                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm) {
+  const bool norm = nm.r != nullptr;
   if (block == 1 && mean == nullptr) {  // one scale per row
     const int rpw = 256 / (d / 8);
-    SQ_DISPATCH_D(d, quant_i8_rows_kernel, dim3((N + rpw - 1) / rpw, BH), dim3(256), st, x, lx, N, codes,
-                  scales);
+    SQ_DISPATCH_DN(d, norm, quant_i8_rows_kernel, dim3((N + rpw - 1) / rpw, BH), dim3(256), st, x, lx, N, codes,
+                   scales, nm);
     return;
   }
   int nb = (N + block - 1) / block;
-  SQ_DISPATCH_D(d, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, lx, N, block, mean, codes, scales);
+  SQ_DISPATCH_DN(d, norm, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, lx, N, block, mean, codes, scales, nm);
 }
 
 void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st) {

@@ -249,6 +249,38 @@ int sqattn_forward_strided(const void* q, const void* k, const void* v, int B, i
                            size_t workspace_bytes, void* stream, const sqattn_opts* opts);
 
 /*
+ * sqattn_forward_strided with the per-token RMSNorm of Q and K fused into
+ * their quantization: the q/k normalization a DiT attention block applies
+ * over each token's H*d features right after its QKV projection, the step
+ * in front of Q/K quantization (digipub.cc TurboDiffusion article, paragraph
+ * on other optimizations: RMSNorm rewritten as a custom kernel).  Bit for
+ * bit the same as normalizing Q and K into bf16 tensors and calling
+ * sqattn_forward_strided on them, without writing them to memory:
+ *   q'[b,h,n,c] = bf16(fl32(fl32(q[b,h,n,c] * r_q[b,n]) * gamma_q[h*d + c]))
+ *   r_q[b,n]    = fl32(1 / fl32(sqrt(fl32(mu2 + eps)))),
+ *   mu2         = fl32(sum over h, c of q[b,h,n,c]^2 / (H*d)), the exact sum
+ *                 rounded once (as sqattn_w8a8_rmsnorm_quantize),
+ * likewise k' with gamma_k; bf16 rounding is nearest-even (a NaN stays a
+ * NaN; a token holding Inf or NaN gets r = NaN).
+ *   gamma_q, gamma_k : float32 [H*d] device pointers, or NULL (weight 1).
+ *   eps              : finite, > 0.
+ *   in_strides       : as sqattn_forward_strided, required when H > 1: each
+ *                      token's H*d values of q and of k must be contiguous
+ *                      (head stride in_strides[1] = in_strides[4] = d), as in
+ *                      a fused QKV projection output [B, N, 3, H, d].
+ * V, out_strides, block_mask, opts and the rest as sqattn_forward_strided.
+ * workspace: >= sqattn_forward_qknorm_workspace_bytes() bytes (the forward's
+ * workspace plus 2*B*N floats), 256-byte aligned, or NULL.
+ */
+size_t sqattn_forward_qknorm_workspace_bytes(int B, int H, int N, int d, int pv_dtype,
+                                             const sqattn_opts* opts);
+int sqattn_forward_qknorm(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                          const int64_t* in_strides, const int64_t* out_strides, const float* gamma_q,
+                          const float* gamma_k, float eps, float scale, int pv_dtype,
+                          const uint8_t* block_mask, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream, const sqattn_opts* opts);
+
+/*
  * W8A8 block-wise INT8 linear layer, y = x W^T (+ b): the projections on
  * either side of attention with weights and activations both quantized to
  * INT8 in 128x128 blocks and the products on the INT8 matrix units

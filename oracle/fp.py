@@ -205,6 +205,24 @@ def rne_to_int(q: np.ndarray) -> np.ndarray:
     return np.where(n == 1, -k, k)
 
 
+def f32_to_bf16(y: np.ndarray) -> np.ndarray:
+    """binary32 -> bfloat16 bit patterns, nearest-even (exact, integers only).
+
+    bf16 keeps the upper 16 bits of binary32; the lower 16 decide the
+    rounding: above half rounds up, exactly half rounds to the even upper
+    part.  A carry into the exponent is the correct next binade (the largest
+    finite values round to infinity).  NaN maps to the quiet NaN with the same
+    sign and upper payload bits; infinities stay."""
+    u = np.ascontiguousarray(y, dtype=np.float32).view(np.uint32).astype(np.int64)
+    hi = u >> 16
+    lo = u & 0xFFFF
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & 1) == 1))
+    out = hi + up.astype(np.int64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    out = np.where(nan, hi | 0x40, out)
+    return out.astype(np.uint16)
+
+
 # ---------------------------------------------------------------------------
 # OCP E4M3FN
 # ---------------------------------------------------------------------------

@@ -20,6 +20,9 @@ order):
     y_k = fl32(x_k * r)).
   * The codes and scales are those of the W8A8 rule applied to the binary32
     y (oracle.w8a8.quantize_blocks): no bf16 round trip in between.
+  * In front of attention (q/k normalization over each token's H*d features,
+    ``qk_rmsnorm``) y is stored in bf16, nearest-even, as the attention
+    inputs are; the attention oracle then takes those bf16 tensors.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ import numpy as np
 
 from . import fp, w8a8
 
-__all__ = ["sum_squares_exact", "rms_inverse", "rmsnorm", "rmsnorm_quantize"]
+__all__ = ["sum_squares_exact", "rms_inverse", "rmsnorm", "rmsnorm_quantize", "qk_rmsnorm"]
 
 # every bf16 square is an integer multiple of 2^-266 (smallest subnormal^2)
 _UNIT_EXP = -266
@@ -83,3 +86,17 @@ def rmsnorm_quantize(x_bits: np.ndarray, gamma, eps: float):
     y, r = rmsnorm(x_bits, gamma, eps)
     codes, scales = w8a8.quantize_blocks(y)
     return codes, scales, r
+
+
+def qk_rmsnorm(x_bits: np.ndarray, gamma, eps: float) -> np.ndarray:
+    """The per-token q (or k) normalization in front of attention, stored in
+    bf16 as the attention inputs are: for x [B, H, N, d] (bf16 bits) each
+    token (b, n) is the row of its H*d values (head-major), normalized as
+    ``rmsnorm`` with gamma [H*d] (or None) and rounded to bf16 (nearest even).
+    Returns bf16 bits [B, H, N, d]."""
+    x = np.asarray(x_bits, np.uint16)
+    B, H, N, d = x.shape
+    rows = x.transpose(0, 2, 1, 3).reshape(B * N, H * d)
+    y, _ = rmsnorm(rows, gamma, eps)
+    yb = fp.f32_to_bf16(y)
+    return np.ascontiguousarray(yb.reshape(B, N, H, d).transpose(0, 2, 1, 3))

@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 22
+    assert len(names) == 24
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -275,3 +275,31 @@ def test_rmsnorm_validation():
     assert L.sqattn_w8a8_rmsnorm_workspace_bytes(100, 256) > 100 * 256
     lin = [FAKE, None, 1e-6, FAKE, FAKE, None, 300, 200, 384, 0, FAKE, FAKE, 1, None]
     assert L.sqattn_w8a8_linear_rmsnorm(*lin) == WORKSPACE
+
+
+def test_qknorm_forward_validation():
+    L = sq.lib()
+    H, N, d = 2, 64, 64
+    fused = [3 * H * d * N, d, 3 * H * d]                 # [B, N, 3, H, d] views: head stride d
+    good = (ctypes.c_int64 * 9)(*(fused * 3))
+    bhnd = (ctypes.c_int64 * 9)(*([H * N * d, N * d, d] * 3))
+
+    def call(st=good, eps=1e-6, gq=None, gk=None, H=H, wsb=1):
+        return L.sqattn_forward_qknorm(FAKE, FAKE, FAKE, 1, H, N, d, st, None, gq, gk, eps, 0.125, 0, None, FAKE,
+                                       FAKE, wsb, None, None)
+
+    assert call(st=None) == INVALID and "in_strides" in _err()
+    assert call(st=bhnd) == INVALID and "contiguous" in _err()
+    assert call(eps=0.0) == INVALID and "eps" in _err()
+    assert call(eps=float("inf")) == INVALID
+    assert call(gq=FAKE + 2) == INVALID and "gamma_q" in _err()
+    # valid arguments reach the workspace check, which counts the per-token factors
+    assert call() == WORKSPACE
+    plain = L.sqattn_workspace_bytes(1, H, N, d, 0, None)
+    need = L.sqattn_forward_qknorm_workspace_bytes(1, H, N, d, 0, None)
+    assert need >= plain + 2 * N * 4
+    assert call(wsb=plain) == WORKSPACE
+    # one head: any layout (the token's d values are a row)
+    one = (ctypes.c_int64 * 9)(*([N * d, N * d, d] * 3))
+    assert call(st=one, H=1) == WORKSPACE
+    assert L.sqattn_forward_qknorm_workspace_bytes(1, H, N, 96, 0, None) == 0

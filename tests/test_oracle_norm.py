@@ -12,7 +12,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from oracle import norm, w8a8
+from oracle import fp, norm, w8a8
 import workloads as W
 
 
@@ -116,3 +116,46 @@ def test_mean_square_next_to_a_midpoint():
         for reps in (2, 4):      # tiled rows: same mean square
             mu2t, _ = norm.rms_inverse(np.tile(bits, reps)[None, :], NC.EPS)
             assert mu2t[0] == want, kind
+
+
+def test_f32_to_bf16_matches_torch_rounding():
+    """The oracle's integer-decided nearest-even rounding to bf16 against
+    torch's CPU float32 -> bfloat16 conversion (an independent routine), on
+    random values over the whole binary32 range, exact ties in both
+    directions, values next to the overflow threshold, subnormals, zeros and
+    infinities; NaN stays a NaN of the same sign."""
+    import torch
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, 2000, dtype=np.uint32) << 16) | 0x8000
+    edge = np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00008000, 0x00018000, 0x00000001, 0x80000000, 0,
+                     0x7F800000, 0xFF800000, 0x7FC00000, 0x3F808000, 0x3F818000], np.uint32)
+    bits = np.concatenate([u, ties, edge])
+    bits = bits[(bits & 0x7FFFFFFF) <= 0x7F800000]             # finite or infinite
+    y = bits.view(np.float32)
+    got = fp.f32_to_bf16(y)
+    ref = torch.from_numpy(y.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    # NaN (torch writes its own pattern): a NaN of the same sign
+    nan = np.array([0x7FC00000, 0xFFC00001, 0x7F800001], np.uint32)
+    nb = fp.f32_to_bf16(nan.view(np.float32)).astype(np.uint32)
+    assert np.all((nb & 0x7F80) == 0x7F80) and np.all((nb & 0x7F) != 0)
+    np.testing.assert_array_equal(nb >> 15, nan >> 31)
+
+
+def test_qk_rmsnorm_rows_are_tokens():
+    """qk_rmsnorm normalizes each token over its H*d values: the same as
+    rmsnorm on the [B*N, H*d] token rows, rounded to bf16; and scaling one
+    token by a power of two leaves every output unchanged."""
+    rng = np.random.default_rng(6)
+    B, H, N, d = 2, 3, 5, 64
+    x = _bits(rng.standard_normal((B, H, N, d)) * rng.uniform(0.1, 10, (B, 1, N, 1)))
+    g = (rng.standard_normal(H * d) * 0.2 + 1).astype(np.float32)
+    out = norm.qk_rmsnorm(x, g, 1e-6)
+    rows = x.transpose(0, 2, 1, 3).reshape(B * N, H * d)
+    y, _ = norm.rmsnorm(rows, g, 1e-6)
+    want = fp.f32_to_bf16(y).reshape(B, N, H, d).transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(out, want)
+    x2 = x.copy()
+    x2[1, :, 3, :] = _bits(_f(x[1, :, 3, :]) * np.float32(2.0 ** 10))
+    np.testing.assert_array_equal(norm.qk_rmsnorm(x2, g, 2.0 ** -140), norm.qk_rmsnorm(x, g, 2.0 ** -140))
