@@ -272,6 +272,9 @@ def main(argv=None):
                     help="Q scale block (1 = one scale per query row); default: the workload's")
     ap.add_argument("--rmsnorm", action="store_true",
                     help="W8A8 workloads: the step is RMSNorm + quantization + GEMM (fused normalization)")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="attention workloads: Q, K, V as views of a fused [B, N, 3, H, d] projection output and "
+                         "the step is attention with the per-token q/k RMSNorm fused into the quantization")
     ap.add_argument("--block-density", type=float, default=None,
                     help="block-sparse attention: fraction of the non-local blocks kept")
     a = ap.parse_args(argv)
@@ -311,6 +314,29 @@ def main(argv=None):
 
     def step():
         sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M)
+
+    plain_ms = None
+    if a.qk_norm:
+        # Q, K, V inside one fused projection output [B, N, 3, H, d]; weights of
+        # the q and k normalization ~ 1 + N(0, 0.1^2)
+        qkv = torch.stack([t.permute(0, 2, 1, 3) for t in (Q, K, V)], dim=2).contiguous()
+        qv, kv, vv = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.index)
+        Gq, Gk = (1.0 + 0.1 * torch.randn(w.H * w.d, generator=g, device=dev) for _ in range(2))
+        wsn = torch.empty(sq.forward_qknorm_workspace_bytes(w.B, w.H, w.N, w.d, w.pv, w.q_block),
+                          dtype=torch.uint8, device=dev)
+
+        def plain():
+            sq.forward(qv, kv, vv, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M)
+
+        for _ in range(2):
+            plain()
+        plain_ms = _timed(torch, np, dev, stream, plain, a.steps)[0]
+
+        def step():
+            sq.forward_qknorm(qv, kv, vv, Gq, Gk, 1e-6, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out,
+                              workspace=wsn, block_mask=M)
 
     def timed(fn, n):
         return _timed(torch, np, dev, stream, fn, n)
@@ -376,6 +402,11 @@ def main(argv=None):
                      "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
                      "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
     }
+    if a.qk_norm:
+        res["config"]["qk_norm"] = {
+            "layout": "q, k, v as views of a fused [B, N, 3, H, d] projection output",
+            "step": "attention with the per-token q/k RMSNorm (over H*d) fused into the quantization",
+            "forward_without_norm_ms": round(plain_ms, 4)}
     if M is not None:
         res["metric"] = METRIC.replace("4·B·H·N²·d/s", "4·d·kept query-key pairs/s") + ", block-sparse"
         res["config"]["block_sparse"] = {

@@ -19,7 +19,8 @@ __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "f
            "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
-           "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes", "forward_qknorm"]
+           "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes", "forward_qknorm",
+           "forward_qknorm_workspace_bytes"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -276,6 +277,11 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
     return out
 
 
+def forward_qknorm_workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
+    o = _opts(q_block, OUT_FP32)
+    return int(lib().sqattn_forward_qknorm_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
+
+
 def forward_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps: float = 1e-6, scale: float | None = None, pv="bf16",
                    q_block: int = 128, out=None, workspace=None, out_dtype=None, block_mask=None):
     """Attention with the per-token RMSNorm of q and k (over each token's H*d
@@ -320,8 +326,7 @@ def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, blo
         _check(lib().sqattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, float(scale),
                                             _PV[pv], _ptr(m), _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
     else:
-        need = int(lib().sqattn_forward_qknorm_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
-        w, wb = _ws(need, q.device, workspace)
+        w, wb = _ws(forward_qknorm_workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
         gq, gk, eps = qkn
         _check(lib().sqattn_forward_qknorm(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, _ptr(gq), _ptr(gk),
                                            eps, float(scale), _PV[pv], _ptr(m), _ptr(out), _ptr(w), wb,
