@@ -159,3 +159,78 @@ def test_qk_rmsnorm_rows_are_tokens():
     x2 = x.copy()
     x2[1, :, 3, :] = _bits(_f(x[1, :, 3, :]) * np.float32(2.0 ** 10))
     np.testing.assert_array_equal(norm.qk_rmsnorm(x2, g, 2.0 ** -140), norm.qk_rmsnorm(x, g, 2.0 ** -140))
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm
+# ---------------------------------------------------------------------------
+
+def _ln_rows():
+    rng = np.random.default_rng(7)
+    rows = [rng.standard_normal(256) * 3 + 5,
+            rng.standard_normal(256) * 1e-3 - 40.0,                        # mean far above the spread
+            np.concatenate([[1e18, -3e17], rng.standard_normal(254) * 1e-30]),
+            np.concatenate([rng.standard_normal(200) * 1e-39, rng.standard_normal(56) * 1e-36]),  # subnormals
+            np.full(256, -2.5),
+            rng.standard_normal(256) * 1e15]
+    return np.stack([_bits(r) for r in rows])
+
+
+def test_layernorm_stats_are_nearest_binary32():
+    x = _ln_rows()
+    mu, var, r = norm.layernorm_stats(x, 1e-6)
+    K = x.shape[1]
+    for i in range(x.shape[0]):
+        vals = [Fraction(float(v)) for v in _f(x[i])]
+        _is_nearest_f32(mu[i], sum(vals) / K)
+        d = (_f(x[i]) - mu[i]).astype(np.float32)                  # binary32 differences
+        _is_nearest_f32(var[i], sum(Fraction(float(v)) ** 2 for v in d) / K)
+    assert var[4] == 0 and mu[4] == np.float32(-2.5)
+
+
+def test_layernorm_close_to_float64():
+    rng = np.random.default_rng(8)
+    x = _bits(rng.standard_normal((64, 512)) * rng.uniform(0.01, 100, (64, 1)) + rng.uniform(-1, 1, (64, 1)))
+    g = (rng.standard_normal(512) * 0.5 + 1).astype(np.float32)
+    b = (rng.standard_normal(512) * 0.1).astype(np.float32)
+    y, _, _ = norm.layernorm(x, g, b, 1e-6)
+    xf = _f(x).astype(np.float64)
+    m = xf.mean(axis=1, keepdims=True)
+    ref = (xf - m) / np.sqrt(((xf - m) ** 2).mean(axis=1, keepdims=True) + np.float64(np.float32(1e-6)))
+    ref = ref * g.astype(np.float64) + b.astype(np.float64)
+    scale = np.abs(xf - m).max(axis=1, keepdims=True) / np.sqrt(((xf - m) ** 2).mean(axis=1, keepdims=True))
+    assert np.all(np.abs(y - ref) <= 2.0 ** -20 * (scale * np.abs(g) + np.abs(b)) + 1e-30)
+
+
+def test_layernorm_power_of_two_scaling_and_constant_rows():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((130, 384)).astype(np.float32) + 0.5
+    g = (rng.standard_normal(384) + 1).astype(np.float32)
+    b = (rng.standard_normal(384) * 0.2).astype(np.float32)
+    eps = 2.0 ** -140
+    c0, s0, m0, r0 = norm.layernorm_quantize(_bits(x), g, b, eps)
+    c1, s1, m1, r1 = norm.layernorm_quantize(_bits(x * 1024), g, b, eps)
+    np.testing.assert_array_equal(c0, c1)
+    np.testing.assert_array_equal(s0, s1)
+    np.testing.assert_array_equal(m1, m0 * np.float32(1024))
+    np.testing.assert_array_equal(r1 * np.float32(1024), r0)
+    y, _, _ = norm.layernorm(_bits(np.full((2, 256), 3.0, np.float32)), g[:256], b[:256], 1e-6)
+    np.testing.assert_array_equal(y, np.broadcast_to(b[:256], (2, 256)))     # d = 0: y = beta
+    c, s, _, _ = norm.layernorm_quantize(_bits(x), g, b, 1e-6)
+    y2, _, _ = norm.layernorm(_bits(x), g, b, 1e-6)
+    c2, s2 = w8a8.quantize_blocks(y2)
+    np.testing.assert_array_equal(c, c2)
+    np.testing.assert_array_equal(s, s2)
+
+
+def test_layernorm_variance_next_to_a_midpoint():
+    """Rows [x, -x] with x a crafted RMS row (tests/norm_cases.py): the exact
+    mean is 0, so d = x and the variance is the crafted mean square, which
+    lies exactly on, just above or just below a binary32 midpoint with the
+    deciding squares 2^150 and 2^300 below the largest."""
+    import norm_cases as NC
+    for i, kind in enumerate(NC.KINDS):
+        bits, lo, hi, want = NC.mean_square_row(kind, seed=11 * i)
+        row = np.concatenate([bits, bits ^ np.uint16(0x8000)])
+        mu, var, _ = norm.layernorm_stats(row[None, :], NC.EPS)
+        assert mu[0] == 0 and var[0] == want, kind
