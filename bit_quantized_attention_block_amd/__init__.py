@@ -20,7 +20,8 @@ __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "f
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
            "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes", "forward_qknorm",
-           "forward_qknorm_workspace_bytes"]
+           "forward_qknorm_workspace_bytes", "w8a8_layernorm_quantize", "w8a8_layernorm_workspace_bytes",
+           "w8a8_linear_layernorm"]
 
 PV_BF16 = 0
 PV_FP8 = 1
@@ -62,6 +63,9 @@ EXPORTS = {
     "sqattn_w8a8_rmsnorm_quantize": (_i, [_vp, _vp, _f, _i, _i, _vp, _vp, _vp, _vp]),
     "sqattn_w8a8_rmsnorm_workspace_bytes": (_sz, [_i, _i]),
     "sqattn_w8a8_linear_rmsnorm": (_i, [_vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "sqattn_w8a8_layernorm_quantize": (_i, [_vp, _vp, _vp, _f, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "sqattn_w8a8_layernorm_workspace_bytes": (_sz, [_i, _i]),
+    "sqattn_w8a8_linear_layernorm": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -496,4 +500,43 @@ def w8a8_linear_rmsnorm(x, w_codes, w_scales, gamma=None, eps: float = 1e-6, bia
     w, wb = _ws(w8a8_rmsnorm_workspace_bytes(M, K), x.device, workspace)
     _check(lib().sqattn_w8a8_linear_rmsnorm(_ptr(x), _ptr(g), float(eps), _ptr(w_codes), _ptr(w_scales), _ptr(bias),
                                             M, N, K, od, _ptr(out), _ptr(w), wb, _stream(x)))
+    return out
+
+
+def w8a8_layernorm_workspace_bytes(M, K) -> int:
+    return int(lib().sqattn_w8a8_layernorm_workspace_bytes(M, K))
+
+
+def w8a8_layernorm_quantize(x, gamma=None, beta=None, eps: float = 1e-6):
+    """LayerNorm of bf16 x [R, K] (gamma, beta fp32 [K] or None) fused with
+    the W8A8 block quantization: (codes, scales, mean [R], rstd [R])."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    R, C = (int(v) for v in x.shape)
+    codes = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    scales = torch.empty((-(-R // 128), C // 128 if C % 128 == 0 else 0), dtype=torch.float32, device=x.device)
+    mu = torch.empty((R,), dtype=torch.float32, device=x.device)
+    r = torch.empty((R,), dtype=torch.float32, device=x.device)
+    g, b = _gamma(gamma, C), _gamma(beta, C)
+    _check(lib().sqattn_w8a8_layernorm_quantize(_ptr(x), _ptr(g), _ptr(b), float(eps), R, C, _ptr(codes),
+                                                _ptr(scales), _ptr(mu), _ptr(r), _stream(x)))
+    return codes, scales, mu, r
+
+
+def w8a8_linear_layernorm(x, w_codes, w_scales, gamma=None, beta=None, eps: float = 1e-6, bias=None, out=None,
+                          out_dtype=None, workspace=None):
+    """LayerNorm(x) W^T (+ bias): normalization, INT8 block quantization and
+    the block-scaled GEMM, with no normalized activations in HBM."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, N, K = _w8a8_shapes(x.shape, w_codes, w_scales, bias)
+    g, b = _gamma(gamma, K), _gamma(beta, K)
+    out, od = _out(out, (M, N), x.device, out_dtype)
+    w, wb = _ws(w8a8_layernorm_workspace_bytes(M, K), x.device, workspace)
+    _check(lib().sqattn_w8a8_linear_layernorm(_ptr(x), _ptr(g), _ptr(b), float(eps), _ptr(w_codes), _ptr(w_scales),
+                                              _ptr(bias), M, N, K, od, _ptr(out), _ptr(w), wb, _stream(x)))
     return out

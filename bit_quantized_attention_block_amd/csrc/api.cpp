@@ -635,4 +635,59 @@ int sqattn_w8a8_linear_rmsnorm(const void* x, const float* gamma, float eps, con
   return hip_check("sqattn_w8a8_linear_rmsnorm launch");
 }
 
+int sqattn_w8a8_layernorm_quantize(const void* x, const float* gamma, const float* beta, float eps, int rows,
+                                   int cols, int8_t* codes, float* scales, float* mean, float* rstd,
+                                   void* stream) {
+  g_err.clear();
+  int s;
+  if ((s = check_w8a8_rows(rows, "rows")) || (s = check_w8a8_k(cols))) return s;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return fail(SQATTN_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (rows == 0) return SQATTN_OK;  // empty: pointers are not inspected
+  if ((s = check_ptr(x, "x", 16)) || (s = check_ptr(codes, "codes", 16)) || (s = check_ptr(scales, "scales", 4)) ||
+      (s = check_ptr(mean, "mean", 4)) || (s = check_ptr(rstd, "rstd", 4)))
+    return s;
+  if ((gamma && (s = check_ptr(gamma, "gamma", 4))) || (beta && (s = check_ptr(beta, "beta", 4)))) return s;
+  sqattn::launch_w8a8_layernorm_quant((const uint16_t*)x, gamma, beta, eps, rows, cols, codes, scales, mean, rstd,
+                                      (hipStream_t)stream);
+  return hip_check("sqattn_w8a8_layernorm_quantize launch");
+}
+
+size_t sqattn_w8a8_layernorm_workspace_bytes(int M, int K) {
+  std::string keep = g_err;
+  if (check_w8a8_rows(M, "M") || check_w8a8_k(K)) {
+    g_err = keep;
+    return 0;
+  }
+  return align_up((size_t)M * K) + align_up(w8a8_scale_bytes(M, K)) + 2 * align_up((size_t)M * 4);
+}
+
+int sqattn_w8a8_linear_layernorm(const void* x, const float* gamma, const float* beta, float eps,
+                                 const int8_t* w_codes, const float* w_scales, const float* bias, int M, int N, int K,
+                                 int out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int s;
+  if ((s = check_w8a8_rows(M, "M")) || (s = check_w8a8_rows(N, "N")) || (s = check_w8a8_k(K)) ||
+      (s = check_out_dtype(out_dtype)))
+    return s;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return fail(SQATTN_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (M == 0 || N == 0) return SQATTN_OK;  // empty: pointers are not inspected
+  if ((s = check_ptr(x, "x", 16)) || (s = check_ptr(w_codes, "w_codes", 16)) ||
+      (s = check_ptr(w_scales, "w_scales", 4)) || (s = check_ptr(out, "out", 16)))
+    return s;
+  if ((gamma && (s = check_ptr(gamma, "gamma", 4))) || (beta && (s = check_ptr(beta, "beta", 4))) ||
+      (bias && (s = check_ptr(bias, "bias", 4))))
+    return s;
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  const size_t cb = align_up((size_t)M * K), sb = align_up(w8a8_scale_bytes(M, K)), rb = align_up((size_t)M * 4);
+  if ((s = ws.acquire(workspace, workspace_bytes, cb + sb + 2 * rb, st))) return s;
+  int8_t* xc = ws.at<int8_t>(0);
+  float* xs = ws.at<float>(cb);
+  float* mu = ws.at<float>(cb + sb);
+  float* r = ws.at<float>(cb + sb + rb);
+  sqattn::launch_w8a8_layernorm_quant((const uint16_t*)x, gamma, beta, eps, M, K, xc, xs, mu, r, st);
+  sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st);
+  return hip_check("sqattn_w8a8_linear_layernorm launch");
+}
+
 }  // extern "C"

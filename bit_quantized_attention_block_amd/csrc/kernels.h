@@ -64,6 +64,10 @@ void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 // RMSNorm: inv_rms[r] = fl32(1 / fl32(sqrt(fl32(mean_k x[r,k]^2 + eps)))), the mean
 // square rounded once from its exact value (norm.hip).
 void launch_rms_inverse(const uint16_t* x, int R, int C, float eps, float* inv_rms, hipStream_t st);
+// LayerNorm statistics: mean[r] = fl32(sum_k x[r,k] / C) (exact sum rounded once),
+// rstd[r] = fl32(1 / fl32(sqrt(fl32(var + eps)))), var = fl32(sum_k d^2 / C) with
+// d = fl32(x - mean) (exact sum of the binary32 squares rounded once) (norm.hip).
+void launch_layernorm_stats(const uint16_t* x, int R, int C, float eps, float* mean, float* rstd, hipStream_t st);
 // the same over B*N token rows of C contiguous values each, row (b, n) at
 // x + b*sb + n*sn, into inv_rms[b*N + n]
 void launch_rms_inverse_rows(const uint16_t* x, int B, int N, int C, long long sb, long long sn, float eps,
@@ -73,6 +77,9 @@ void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* sc
 // RMSNorm (per-row inverse RMS into inv_rms) fused with the block quantization
 void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int R, int C, int8_t* codes,
                                float* scales, float* inv_rms, hipStream_t st);
+// LayerNorm (mean, rstd per row) fused with the block quantization
+void launch_w8a8_layernorm_quant(const uint16_t* x, const float* gamma, const float* beta, float eps, int R, int C,
+                                 int8_t* codes, float* scales, float* mean, float* rstd, hipStream_t st);
 void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
                       int M, int N, int K, void* out, int out_bf16, hipStream_t st);
 

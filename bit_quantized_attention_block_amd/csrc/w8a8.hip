@@ -42,29 +42,43 @@ constexpr int QB = 128;                  // scale block edge
 // 8 (t % 16) .. +8 of rows t/16 + 16 j (j < 8) of the block.  NORM: the
 // block of y = fl32(fl32(x * r_row) * gamma_col) (gamma may be null) instead
 // of x.
-template <bool NORM>
+// NORM: 0 plain x; 1 RMSNorm, y = fl32(fl32(x * r_row) * gamma_col); 2
+// LayerNorm, y = fl32(fl32(fl32(fl32(x - mean_row) * r_row) * gamma_col) +
+// beta_col) (gamma, beta may be null).  The steps are separately rounded
+// operations (no contraction into a fused multiply-add).
+template <int NORM>
 __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restrict__ x, int R, int C,
                                                          int8_t* __restrict__ codes,
                                                          float* __restrict__ scales,
                                                          const float* __restrict__ inv_rms,
-                                                         const float* __restrict__ gamma) {
+                                                         const float* __restrict__ gamma,
+                                                         const float* __restrict__ mean = nullptr,
+                                                         const float* __restrict__ beta = nullptr) {
   __shared__ float sh[4];
   const int cb = blockIdx.x, rb = blockIdx.y;
   const int t = threadIdx.x, piece = t & 15, r = t >> 4;
   const long long col = (long long)cb * QB + piece * 8;
   v4i w[8];
-  float rr[8], gm[8];
-  if constexpr (NORM) {
+  float rr[8], gm[8], bt[8], mr[8];
+  if constexpr (NORM != 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) gm[e] = gamma ? gamma[col + e] : 1.0f;
+  }
+  if constexpr (NORM == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bt[e] = beta ? beta[col + e] : 0.0f;
   }
   // element e of piece j as the value to quantize
   auto val = [&](int j, int e) {
     const uint32_t u = (uint32_t)w[j][e >> 1];
     float a = bf16_bits_to_f32((e & 1) ? (u >> 16) : (u & 0xFFFFu));
-    if constexpr (NORM) {
+    if constexpr (NORM == 1) {
       a = a * rr[j];                 // fl32(x r)
       if (gamma) a = a * gm[e];      // fl32(. gamma)
+    } else if constexpr (NORM == 2) {
+      a = __fmul_rn(__fsub_rn(a, mr[j]), rr[j]);  // fl32(fl32(x - mu) r)
+      if (gamma) a = __fmul_rn(a, gm[e]);
+      if (beta) a = __fadd_rn(a, bt[e]);
     }
     return a;
   };
@@ -73,7 +87,8 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
   for (int j = 0; j < 8; ++j) {
     const int row = rb * QB + r + 16 * j;
     w[j] = (row < R) ? *(const v4i*)(x + (long long)row * C + col) : v4i{0, 0, 0, 0};
-    if constexpr (NORM) rr[j] = (row < R) ? inv_rms[row] : 0.0f;
+    if constexpr (NORM != 0) rr[j] = (row < R) ? inv_rms[row] : 0.0f;
+    if constexpr (NORM == 2) mr[j] = (row < R) ? mean[row] : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(val(j, e)));
   }
@@ -307,15 +322,22 @@ __global__ __launch_bounds__(NTHR) void w8a8_gemm_kernel(GemmParams p) {
 }  // namespace
 
 void launch_w8a8_quant(const uint16_t* x, int R, int C, int8_t* codes, float* scales, hipStream_t st) {
-  hipLaunchKernelGGL(w8a8_quant_kernel<false>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
-                     scales, nullptr, nullptr);
+  hipLaunchKernelGGL(w8a8_quant_kernel<0>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
+                     scales, nullptr, nullptr, nullptr, nullptr);
 }
 
 void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int R, int C, int8_t* codes,
                                float* scales, float* inv_rms, hipStream_t st) {
   launch_rms_inverse(x, R, C, eps, inv_rms, st);
-  hipLaunchKernelGGL(w8a8_quant_kernel<true>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
-                     scales, inv_rms, gamma);
+  hipLaunchKernelGGL(w8a8_quant_kernel<1>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
+                     scales, inv_rms, gamma, nullptr, nullptr);
+}
+
+void launch_w8a8_layernorm_quant(const uint16_t* x, const float* gamma, const float* beta, float eps, int R, int C,
+                                 int8_t* codes, float* scales, float* mean, float* rstd, hipStream_t st) {
+  launch_layernorm_stats(x, R, C, eps, mean, rstd, st);
+  hipLaunchKernelGGL(w8a8_quant_kernel<2>, dim3(C / QB, (R + QB - 1) / QB), dim3(256), 0, st, x, R, C, codes,
+                     scales, rstd, gamma, mean, beta);
 }
 
 void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,

@@ -360,6 +360,40 @@ int sqattn_w8a8_linear_rmsnorm(const void* x, const float* gamma, float eps, con
                                int out_dtype, void* out, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * LayerNorm fused with the W8A8 quantization of the projection input: the
+ * normalization in front of a DiT block's QKV projection (its modulation,
+ * x_norm * (1 + scale) + shift, as gamma = 1 + scale and beta = shift),
+ * written as a custom kernel (digipub.cc TurboDiffusion article, paragraph
+ * on other optimizations: LayerNorm and RMSNorm reimplemented).  Per row of
+ * x [rows, cols] (bf16), every result rounded once and independent of the
+ * summation order:
+ *   mu   = fl32(sum x / cols)              (exact sum);
+ *   d    = fl32(x - mu);
+ *   var  = fl32(sum d^2 / cols)            (exact sum of the binary32 squares);
+ *   rstd = fl32(1 / fl32(sqrt(fl32(var + eps))));
+ *   y    = fl32(fl32(fl32(d * rstd) * gamma) + beta)
+ *          (gamma, beta fp32 [cols], each may be NULL: no multiply / no add);
+ * then y (binary32) gets the codes and 128x128 block scales of
+ * sqattn_w8a8_quantize.
+ *   mean, rstd : fp32 [rows] outputs (NaN for a row holding Inf or NaN).
+ *   eps        : finite, > 0.
+ * Sizes as sqattn_w8a8_quantize.  Inputs are meant to be finite.
+ */
+int sqattn_w8a8_layernorm_quantize(const void* x, const float* gamma, const float* beta, float eps,
+                                   int rows, int cols, int8_t* codes, float* scales, float* mean,
+                                   float* rstd, void* stream);
+
+/* Workspace of sqattn_w8a8_linear_layernorm (codes, scales, mean, rstd). */
+size_t sqattn_w8a8_layernorm_workspace_bytes(int M, int K);
+
+/* y = LayerNorm(x) W^T (+ b) on bf16 x [M, K]: sqattn_w8a8_layernorm_quantize
+ * into the workspace, then sqattn_w8a8_gemm. */
+int sqattn_w8a8_linear_layernorm(const void* x, const float* gamma, const float* beta, float eps,
+                                 const int8_t* w_codes, const float* w_scales, const float* bias,
+                                 int M, int N, int K, int out_dtype, void* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 24
+    assert len(names) == 27
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -303,3 +303,17 @@ def test_qknorm_forward_validation():
     one = (ctypes.c_int64 * 9)(*([N * d, N * d, d] * 3))
     assert call(st=one, H=1) == WORKSPACE
     assert L.sqattn_forward_qknorm_workspace_bytes(1, H, N, 96, 0, None) == 0
+
+
+def test_layernorm_validation():
+    L = sq.lib()
+    args = lambda eps=1e-6, rows=10, cols=256, x=FAKE, mean=FAKE, beta=None: [x, None, beta, eps, rows, cols, FAKE,
+                                                                               FAKE, mean, FAKE, None]
+    assert L.sqattn_w8a8_layernorm_quantize(*args(eps=-1.0)) == INVALID and "eps" in _err()
+    assert L.sqattn_w8a8_layernorm_quantize(*args(cols=100)) == INVALID
+    assert L.sqattn_w8a8_layernorm_quantize(*args(mean=None)) == INVALID and "mean" in _err()
+    assert L.sqattn_w8a8_layernorm_quantize(*args(beta=FAKE + 1)) == INVALID and "beta" in _err()
+    assert L.sqattn_w8a8_layernorm_quantize(*args(rows=0, x=None, mean=None)) == OK
+    assert L.sqattn_w8a8_layernorm_workspace_bytes(100, 256) > L.sqattn_w8a8_rmsnorm_workspace_bytes(100, 256)
+    lin = [FAKE, None, None, 1e-6, FAKE, FAKE, None, 300, 200, 384, 0, FAKE, FAKE, 1, None]
+    assert L.sqattn_w8a8_linear_layernorm(*lin) == WORKSPACE
