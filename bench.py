@@ -138,13 +138,18 @@ def bench_w8a8(a):
     wsb = torch.empty(sq.w8a8_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    G = torch.ones(w.K, dtype=torch.float32, device=dev) * 1.25 if a.rmsnorm else None
+    G = torch.ones(w.K, dtype=torch.float32, device=dev) * 1.25
+    Be = torch.full((w.K,), 0.1, dtype=torch.float32, device=dev)
     if a.rmsnorm:
         wsb = torch.empty(sq.w8a8_rmsnorm_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
+    if a.layernorm:
+        wsb = torch.empty(sq.w8a8_layernorm_workspace_bytes(w.M, w.K), dtype=torch.uint8, device=dev)
 
     def step():
         if a.rmsnorm:
             sq.w8a8_linear_rmsnorm(X, wc, ws, gamma=G, eps=1e-6, bias=B, out=Y, workspace=wsb)
+        elif a.layernorm:
+            sq.w8a8_linear_layernorm(X, wc, ws, gamma=G, beta=Be, eps=1e-6, bias=B, out=Y, workspace=wsb)
         else:
             sq.w8a8_linear(X, wc, ws, bias=B, out=Y, workspace=wsb)
 
@@ -166,6 +171,7 @@ def bench_w8a8(a):
     ops = w.ops
     q_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_quantize(X), reps)[0]
     n_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_rmsnorm_quantize(X, G, 1e-6), reps)[0]
+    l_ms = _timed(torch, np, dev, stream, lambda: sq.w8a8_layernorm_quantize(X, G, Be, 1e-6), reps)[0]
     tops = ops / (ms * 1e-3) / 1e12
     k_tops = ops / (k_ms * 1e-3) / 1e12
     res = {
@@ -187,8 +193,8 @@ def bench_w8a8(a):
                    "stages_ms": {"step_median": round(ms_med, 4), "step_min": round(ms_min, 4),
                                  "gemm_kernel": round(k_ms, 4), "gemm_kernel_median": round(k_med, 4),
                                  "gemm_kernel_min": round(k_min, 4), "quantize_x": round(q_ms, 4),
-                                 "rmsnorm_quantize_x": round(n_ms, 4)},
-                   "rmsnorm": bool(a.rmsnorm)},
+                                 "rmsnorm_quantize_x": round(n_ms, 4), "layernorm_quantize_x": round(l_ms, 4)},
+                   "rmsnorm": bool(a.rmsnorm), "layernorm": bool(a.layernorm)},
         "roofline": {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
                      "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
@@ -272,6 +278,8 @@ def main(argv=None):
                     help="Q scale block (1 = one scale per query row); default: the workload's")
     ap.add_argument("--rmsnorm", action="store_true",
                     help="W8A8 workloads: the step is RMSNorm + quantization + GEMM (fused normalization)")
+    ap.add_argument("--layernorm", action="store_true",
+                    help="W8A8 workloads: the step is LayerNorm + quantization + GEMM (fused normalization)")
     ap.add_argument("--qk-norm", action="store_true",
                     help="attention workloads: Q, K, V as views of a fused [B, N, 3, H, d] projection output and "
                          "the step is attention with the per-token q/k RMSNorm fused into the quantization")
