@@ -216,6 +216,15 @@ constexpr int LN_WINDOW = 120;       // bits of one level of the squares
 constexpr int LN_DROP_BITS = 46;     // a left-out square is below 2^46 units of its level
 constexpr int LN_SQ_UNIT = -300;     // exponent of the units of e2 (squares)
 constexpr int LN_S1_UNIT = -133;     // exponent of the units of the sum
+constexpr int LN_FAST = LN_WINDOW - 64;  // 128-bit fast window of the squares: shifts 56 .. 120
+
+// a += (hi:lo) * 2^s, 0 <= s < 64, (hi:lo) < 2^120
+__device__ __forceinline__ void acc192_add_u128_shl(Acc192& a, uint64_t lo, uint64_t hi, int s) {
+  const uint64_t w0 = lo << s;
+  const uint64_t w1 = s ? (hi << s) | (lo >> (64 - s)) : hi;
+  const uint64_t w2 = s ? hi >> (64 - s) : 0;
+  acc192_add(a, w0, w1, w2);
+}
 
 struct U320 {
   uint64_t w0, w1, w2, w3, w4;
@@ -440,7 +449,16 @@ __global__ __launch_bounds__(256) void ln_stats_kernel(const uint16_t* __restric
   Acc192 acc;
   acc192_zero(acc);
   bool sticky = false;
-  for (int k = lane * 8; k < C; k += 512) {
+  // squares within 2^64 of the level's top (shifts LN_FAST .. LN_WINDOW) go
+  // to a 128-bit window (each below 2^112; emptied every 16 loads, 128
+  // squares, so it stays below 2^119), the rest of the level to the full
+  // accumulator, smaller ones to the sticky bit
+  uint64_t wlo = 0, whi = 0;
+  for (int k = lane * 8, it = 0; k < C; k += 512, ++it) {
+    if ((it & 15) == 15) {
+      acc192_add_u128_shl(acc, wlo, whi, LN_FAST);
+      wlo = whi = 0;
+    }
     const v4i w = *(const v4i*)(xr + k);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -449,13 +467,20 @@ __global__ __launch_bounds__(256) void ln_stats_kernel(const uint16_t* __restric
       int e2;
       f32_square(__uint_as_float(b << 16) - mu, m2, e2);
       const int sh = e2 - u0;
-      if (m2 == 0) continue;
-      if (sh < 0)
-        sticky = true;
-      else
-        acc192_add_u64_shl(acc, m2, sh);
+      if (sh >= LN_FAST) {
+        const int t = sh - LN_FAST;  // 0 .. 64
+        const uint64_t lo = t < 64 ? m2 << t : 0, hi = t ? m2 >> (64 - t) : 0;
+        wlo += lo;
+        whi += hi + (wlo < lo);
+      } else if (m2 != 0) {
+        if (sh < 0)
+          sticky = true;
+        else
+          acc192_add_u64_shl(acc, m2, sh);
+      }
     }
   }
+  acc192_add_u128_shl(acc, wlo, whi, LN_FAST);
   wave_sum(acc, sticky);
   float var = acc192_div_f32(acc, (uint32_t)C, u0 + LN_SQ_UNIT, sticky);
   if (sticky) var = ln_settle(xr, C, lane, mu, acc, u0, var);
