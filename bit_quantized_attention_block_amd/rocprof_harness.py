@@ -202,6 +202,13 @@ def _short(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
 
 
+def _shown(name: str) -> str:
+    """Kernel name as listed: without the "(anonymous namespace)" part and the
+    argument list, with template arguments (they tell instantiations apart)."""
+    n = name.replace("(anonymous namespace)::", "")
+    return n[:n.index(">") + 1] if "<" in n.split("(")[0] else n.split("(")[0]
+
+
 def _sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -312,7 +319,8 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
 # ---------------------------------------------------------------------------
 # bench-trace: the kernel trace of bench.py itself
 # ---------------------------------------------------------------------------
-def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: int) -> int:
+def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: int, extra: str = "",
+                tag: str = "") -> int:
     """rocprofv3 --kernel-trace --stats around `python3 bench.py` (the same
     command that produces the bench line, without the CPU baseline), then
     profiles/<kernel>_<workload>_bench_trace.md with the per-kernel durations
@@ -324,7 +332,8 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
     os.makedirs(outdir, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
     bench = ["python3", os.path.join(ROOT, "bench.py"), "--workload", w.name, "--steps", str(steps),
-             "--warmup", str(warmup), "--no-cpu-baseline"]
+             "--warmup", str(warmup), "--no-cpu-baseline", *shlex.split(extra)]
+    wname = w.name + (f"-{tag}" if tag else "")
     cmd = ["timeout", "-s", "KILL", "600", "rocprofv3", "--kernel-trace", "--stats", "-d",
            os.path.join(outdir, "bench_trace"), "-o", "bench_trace", "--output-format", "csv", "--", *bench]
     print(f"[bench-trace] {' '.join(shlex.quote(c) for c in cmd)}", flush=True)
@@ -334,6 +343,17 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
     print(f"[bench-trace] rc={rc}", flush=True)
     if rc != 0:
         return rc
+    return bench_trace_summary(workload, outdir, profiles, bench, extra, tag)
+
+
+def bench_trace_summary(workload: str, outdir: str, profiles: str, bench: list, extra: str = "",
+                        tag: str = "") -> int:
+    """profiles/<kernel>_<workload>[-tag]_bench_trace.md from the output of a
+    bench-trace run in outdir (bench: the traced bench.py command)."""
+    sp = spec(workload)
+    w = sp["w"]
+    kname = sp["kernel"]
+    wname = w.name + (f"-{tag}" if tag else "")
     with open(os.path.join(outdir, "bench_trace.json")) as f:
         line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
     res = json.loads(line)
@@ -342,16 +362,17 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
     rows = ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     attn = None
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        rows.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        rows.append(f"| `{_shown(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                     f"{float(r['Percentage']):.1f}% |")
         if is_attn(r["Name"]):
             attn = float(r["AverageNs"]) / 1e6
     shown = " ".join(c if not c.startswith(ROOT) else c.replace(ROOT, ".") for c in bench)
-    lines = [f"# `{kname}` on {w.name}: kernel trace of the bench command", "",
+    lines = [f"# `{kname}` on {wname}: kernel trace of the bench command", "",
              f"Command (from /tmp with TMPDIR=/tmp): `rocprofv3 --kernel-trace --stats -d <out>/bench_trace "
              f"-o bench_trace --output-format csv -- {shown}`, run by `python -m "
-             f"bit_quantized_attention_block_amd.rocprof_harness bench-trace --workload {w.name}`.", "",
+             f"bit_quantized_attention_block_amd.rocprof_harness bench-trace --workload {w.name}"
+             + (f" --extra='{extra}' --tag {tag}" if extra else "") + "`.", "",
              "## Kernel durations (rocprofv3 --kernel-trace --stats)", ""] + rows + [""]
     k_ev = res["roofline"]["avg_launch_ms"]
     lines += [f"- `{kname}`, rocprofv3 average over all its launches in the run: {attn:.4f} ms",
@@ -361,7 +382,7 @@ def bench_trace(workload: str, outdir: str, profiles: str, steps: int, warmup: i
               f"value {res['value']} {res['unit']}", "",
               "Bench line of the traced run:", "", "```", line, "```"]
     os.makedirs(profiles, exist_ok=True)
-    with open(os.path.join(profiles, f"{kname}_{w.name}_bench_trace.md"), "w") as f:
+    with open(os.path.join(profiles, f"{kname}_{wname}_bench_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return 0
@@ -376,6 +397,8 @@ def main(argv=None) -> int:
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--extra", default="", help="bench-trace: further bench.py options (one string)")
+    ap.add_argument("--tag", default="", help="bench-trace: suffix of the workload in the summary's name")
     a = ap.parse_args(argv)
     if a.cmd == "target":
         run_target(a.workload, a.reps)
@@ -383,7 +406,7 @@ def main(argv=None) -> int:
     if a.cmd == "collect":
         return collect(a.workload, a.out, a.reps)
     if a.cmd == "bench-trace":
-        return bench_trace(a.workload, a.out, a.profiles, a.steps, a.warmup)
+        return bench_trace(a.workload, a.out, a.profiles, a.steps, a.warmup, a.extra, a.tag)
     return summarize(a.workload, a.out, a.profiles)
 
 
