@@ -138,6 +138,21 @@ __global__ __launch_bounds__(D) void kmean_finalize_kernel(const uint64_t* __res
 // per-block INT8 quantization
 // ---------------------------------------------------------------------------
 
+// rne(fl32(a / s)) with one multiply in the common case.  With y = RN(1/s)
+// (a correctly rounded division, once per thread) and q = RN(a y), both
+// within 2^-24 relative, |q - fl32(a/s)| < 1.5 * 2^-23 |a/s| < 2^-15 for
+// |a/s| <= 128 (every value of a block against its own scale).  Where q is
+// farther than 2^-15 from every half-integer, fl32(a/s) lies in the same
+// open interval (k - 1/2, k + 1/2) and rounds to the same k; otherwise (ties
+// included) the correctly rounded quotient is formed.  Needs a finite 1/s:
+// callers take the division for s < 2^-125.
+__device__ __forceinline__ float rne_quotient(float a, float s, float y) {
+  const float q = a * y;
+  const float r = rintf(q);
+  if (__builtin_expect(fabsf(q - r) > 0.5f - 0x1p-15f, 0)) return rintf(a / s);
+  return r;
+}
+
 __device__ __forceinline__ float block_max_256(float v, float* sh) {
   // max over the 256 threads of the work-group (all values >= 0 or NaN-free)
 #pragma unroll
@@ -198,6 +213,8 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   const float s = amax / 127.0f;  // correctly rounded binary32 division
   if (t == 0) scales[bh * nblk + blk] = (nanflag > 0.0f) ? __builtin_nanf("") : s;
   const bool zero = !(s > 0.0f) || (nanflag > 0.0f);
+  const bool fast = s >= 0x1p-125f;  // 1/s finite
+  const float y = 1.0f / s;          // correctly rounded
 
 #pragma unroll 2
   for (int r = r0 + rg; r < r1; r += RPP) {
@@ -211,7 +228,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
       if (mean) a = a - mu[j];
       int c = 0;
       if (!zero) {
-        float qv = rintf(a / s);  // rne of the correctly rounded quotient
+        float qv = fast ? rne_quotient(a, s, y) : rintf(a / s);  // rne of the correctly rounded quotient
         qv = fminf(fmaxf(qv, -127.0f), 127.0f);
         c = (int)qv;
       }
@@ -255,13 +272,15 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(const uint16_t* __re
   if (!ok) return;
   if (cg == 0) scales[bh * N + r] = s;
   const bool zero = !(s > 0.0f);
+  const bool fast = s >= 0x1p-125f;  // 1/s finite
+  const float y = 1.0f / s;          // correctly rounded
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t u = (uint32_t)w[j >> 1];
     const float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
     int c = 0;
-    if (!zero) c = (int)fminf(fmaxf(rintf(a / s), -127.0f), 127.0f);
+    if (!zero) c = (int)fminf(fmaxf(fast ? rne_quotient(a, s, y) : rintf(a / s), -127.0f), 127.0f);
     packed[j >> 2] |= ((uint32_t)(c & 0xFF)) << ((j & 3) * 8);
   }
   *(uint2*)(codes + base) = make_uint2(packed[0], packed[1]);
