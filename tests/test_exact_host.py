@@ -116,3 +116,31 @@ def test_e4m3_host_build_matches_oracle(driver):
     text = "e4m3 %d\n%s\n" % (y.size, " ".join(str(int(u)) for u in y.view(np.uint32)))
     got = np.array([int(s) for s in _run(driver, text)], np.uint8)
     assert np.array_equal(got, fp.e4m3_encode(y))
+
+
+def test_quotient_shortcut_matches_division():
+    """The quantizers' rne(fl32(a/s)) shortcut (csrc/prep.hip rne_quotient),
+    emulated in IEEE float32 with numpy: q = RN(a * RN(1/s)), the division
+    where q lies within 2^-15 of a half-integer.  It must equal rint of the
+    correctly rounded quotient on every value of a block against its own
+    scale s = fl32(amax/127): random values, exact ties k + 1/2, and the
+    values one ulp either side of a tie."""
+    import numpy as np
+    rng = np.random.default_rng(12)
+    f = np.float32
+    amax = (np.ldexp(rng.uniform(1, 2, 4000), rng.integers(-100, 100, 4000))).astype(f)
+    s = (amax / f(127)).astype(f)
+    y = (f(1) / s).astype(f)
+    cols = [rng.uniform(-1, 1, (4000, 400)).astype(f) * amax[:, None]]
+    k = rng.integers(-127, 127, (4000, 60)).astype(f)
+    tie = ((k + f(0.5)) * s[:, None]).astype(f)                      # often exactly representable
+    cols += [tie, np.nextafter(tie, f(np.inf)), np.nextafter(tie, f(-np.inf)), amax[:, None], -amax[:, None]]
+    a = np.concatenate(cols, axis=1)
+    a = np.clip(a, -amax[:, None], amax[:, None])
+    exact = np.rint((a / s[:, None]).astype(f))
+    q = (a * y[:, None]).astype(f)
+    r = np.rint(q)
+    near = np.abs((q - r).astype(f)) > f(0.5 - 2.0 ** -15)
+    short = np.where(near, exact, r)
+    assert np.array_equal(short, exact)
+    assert near[:, :400].mean() < 1e-3     # on the random values the division is the exception
