@@ -29,6 +29,22 @@ constexpr int SP_LIST_BYTES = 4 * SP_MAXT + 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// rne(fl32(a / s)) with one multiply in the common case.  With y = RN(1/s)
+// (a correctly rounded division, once per thread) and q = RN(a y), both
+// within 2^-24 relative, |q - fl32(a/s)| < 1.5 * 2^-23 |a/s| < 2^-15 for
+// |a/s| <= 128 (every value of a block against its own scale).  Where q is
+// farther than 2^-15 from every half-integer, fl32(a/s) lies in the same
+// open interval (k - 1/2, k + 1/2) and rounds to the same k; otherwise (ties
+// included) the correctly rounded quotient is formed.  Needs a finite 1/s:
+// callers take the division for s < 2^-125.
+__device__ __forceinline__ float rne_quotient(float a, float s, float y) {
+  const float q = a * y;
+  const float r = rintf(q);
+  if (__builtin_expect(fabsf(q - r) > 0.5f - 0x1p-15f, 0)) return rintf(a / s);
+  return r;
+}
+
+
 // Two floats to packed bf16 (round to nearest even), the first in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   v2bf v;

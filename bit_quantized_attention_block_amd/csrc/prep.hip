@@ -138,21 +138,6 @@ __global__ __launch_bounds__(D) void kmean_finalize_kernel(const uint64_t* __res
 // per-block INT8 quantization
 // ---------------------------------------------------------------------------
 
-// rne(fl32(a / s)) with one multiply in the common case.  With y = RN(1/s)
-// (a correctly rounded division, once per thread) and q = RN(a y), both
-// within 2^-24 relative, |q - fl32(a/s)| < 1.5 * 2^-23 |a/s| < 2^-15 for
-// |a/s| <= 128 (every value of a block against its own scale).  Where q is
-// farther than 2^-15 from every half-integer, fl32(a/s) lies in the same
-// open interval (k - 1/2, k + 1/2) and rounds to the same k; otherwise (ties
-// included) the correctly rounded quotient is formed.  Needs a finite 1/s:
-// callers take the division for s < 2^-125.
-__device__ __forceinline__ float rne_quotient(float a, float s, float y) {
-  const float q = a * y;
-  const float r = rintf(q);
-  if (__builtin_expect(fabsf(q - r) > 0.5f - 0x1p-15f, 0)) return rintf(a / s);
-  return r;
-}
-
 __device__ __forceinline__ float block_max_256(float v, float* sh) {
   // max over the 256 threads of the work-group (all values >= 0 or NaN-free)
 #pragma unroll

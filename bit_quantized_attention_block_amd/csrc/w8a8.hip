@@ -100,6 +100,8 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
   const float s = amax / 127.0f;  // correctly rounded binary32 division
   if (t == 0) scales[(long long)rb * gridDim.x + cb] = s;
   const bool zero = !(s > 0.0f);
+  const bool fast = s >= 0x1p-125f;  // 1/s finite
+  const float y = 1.0f / s;          // correctly rounded
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int row = rb * QB + r + 16 * j;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
     for (int e = 0; e < 8; ++e) {
       const float a = val(j, e);
       int c = 0;
-      if (!zero) c = (int)fminf(fmaxf(rintf(a / s), -127.0f), 127.0f);  // rne of the rounded quotient
+      if (!zero) c = (int)fminf(fmaxf(fast ? rne_quotient(a, s, y) : rintf(a / s), -127.0f), 127.0f);
       packed[e >> 2] |= ((uint32_t)(c & 0xFF)) << ((e & 3) * 8);
     }
     *(uint2*)(codes + (long long)row * C + col) = make_uint2(packed[0], packed[1]);

@@ -121,3 +121,23 @@ def test_empty_rows():
     codes, scales, mu, r = sq.w8a8_layernorm_quantize(X)
     torch.cuda.synchronize()
     assert codes.shape == (0, 256) and mu.shape == (0,)
+
+
+def test_long_rows_fill_the_windows():
+    """Rows of 131072 values of the largest significand: the mean's 64-bit
+    window and the squares' 128-bit window fill at their top and must be
+    emptied before they overflow; one row adds a large offset (its mean is
+    far from 0), one mixes in values 2^-60 below the rest (the mean's slow
+    320-bit path)."""
+    R, C = 6, 131072
+    rng = np.random.default_rng(10)
+    x = np.where(rng.random((R, C)) < 0.5, -1.9921875, 1.9921875).astype(np.float32)
+    x[1] *= 2.0 ** 40
+    x[2] += 512.0
+    x[3, ::3] = 2.0 ** -60
+    x[4] = np.where(rng.random(C) < 0.5, 1.9921875, 1.984375).astype(np.float32) * 2.0 ** -100
+    xb = W.f32_to_bf16_bits(x)
+    print(f"case layernorm long rows R={R} C={C}", flush=True)
+    codes, scales, mu, r = sq.w8a8_layernorm_quantize(dev_bf16(xb), None, None, 1e-6)
+    torch.cuda.synchronize()
+    _check(xb, None, None, 1e-6, codes, scales, mu, r)
