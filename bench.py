@@ -263,7 +263,11 @@ def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
             "sample": f"{heads} heads of {w.name}: full quantization ({t_quant:.1f} s) + {nrows} query rows "
                       f"against all {w.N} keys ({t_attn:.1f} s); scaled to {BH} heads x {w.N} rows"
                       + ("" if mask is None else " (block mask applied)"),
-            "sample_seconds": round(t_quant + t_attn, 2)}
+            "sample_seconds": round(t_quant + t_attn, 2),
+            # query rows per second: of the whole job (quantization included,
+            # as scaled above) and of the attention alone on the sample
+            "rows_per_s": round(w.N * BH / t_full, 3),
+            "attention_rows_per_s": round(nrows / t_attn, 3)}
 
 
 def main(argv=None):
