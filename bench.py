@@ -270,6 +270,80 @@ def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
             "attention_rows_per_s": round(nrows / t_attn, 3)}
 
 
+def bench_dit_block(a):
+    """The DiT attention block of the Wan-14B-480p shape from the library's
+    fused pieces: LayerNorm (modulation as gamma, beta) fused into the W8A8
+    QKV projection, attention with the q/k RMSNorm fused on views of its
+    output, the W8A8 output projection on the attention output in place."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_attention_block_amd as sq
+    import workloads as W
+
+    w = W.get("wan14b-480p")
+    B, N, H, d = w.B, w.N, w.H, w.d
+    C = H * d
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.index)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev)
+    x = (rnd(B * N, C) * 2 + 0.3).to(torch.bfloat16)
+    wqc, wqs = sq.w8a8_quantize((rnd(3 * C, C) / C ** 0.5).to(torch.bfloat16))
+    woc, wos = sq.w8a8_quantize((rnd(C, C) / C ** 0.5).to(torch.bfloat16))
+    bqkv, bo = rnd(3 * C), rnd(C)
+    gamma, beta = 1 + 0.2 * rnd(C), 0.1 * rnd(C)
+    gq, gk = 1 + 0.1 * rnd(C), 1 + 0.1 * rnd(C)
+    y = torch.empty((B * N, 3 * C), dtype=torch.bfloat16, device=dev)
+    att = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((B * N, C), dtype=torch.bfloat16, device=dev)
+    ws1 = torch.empty(sq.w8a8_layernorm_workspace_bytes(B * N, C), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(sq.forward_qknorm_workspace_bytes(B, H, N, d, w.pv, w.q_block), dtype=torch.uint8,
+                      device=dev)
+    ws3 = torch.empty(sq.w8a8_workspace_bytes(B * N, C), dtype=torch.uint8, device=dev)
+    qkv = y.view(B, N, 3, H, d)
+    views = [qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3)]
+    stream = torch.cuda.current_stream(dev)
+
+    def s1():
+        sq.w8a8_linear_layernorm(x, wqc, wqs, gamma=gamma, beta=beta, eps=1e-6, bias=bqkv, out=y, workspace=ws1)
+
+    def s2():
+        sq.forward_qknorm(*views, gq, gk, 1e-6, scale=w.scale, pv=w.pv, q_block=w.q_block,
+                          out=att.permute(0, 2, 1, 3), workspace=ws2)
+
+    def s3():
+        sq.w8a8_linear(att.view(B * N, C), woc, wos, bias=bo, out=z, workspace=ws3)
+
+    def step():
+        s1()
+        s2()
+        s3()
+
+    for _ in range(a.warmup):
+        step()
+    ms, ms_med, ms_min, _ = _timed(torch, np, dev, stream, step, a.steps)
+    t1, t2, t3 = (_timed(torch, np, dev, stream, f, a.steps)[0] for f in (s1, s2, s3))
+    ops_qkv, ops_att, ops_out = 2 * B * N * 3 * C * C, w.ops, 2 * B * N * C * C
+    ops = ops_qkv + ops_att + ops_out
+    tops = ops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "DiT attention block TOPS (LayerNorm+W8A8 QKV, q/k-RMSNorm quantized attention, W8A8 out) "
+                  "+ % of MI355X INT8 MFMA peak",
+        "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8+bf16", "data": "synthetic", "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+        "config": {"workload": "dit-block-wan14b-480p", "B": B, "N": N, "H": H, "d": d, "pv": w.pv,
+                   "ops": {"qkv": ops_qkv, "attention": ops_att, "out": ops_out},
+                   "stages_ms": {"block_median": round(ms_med, 4), "block_min": round(ms_min, 4),
+                                 "layernorm_qkv_projection": round(t1, 4), "qknorm_attention": round(t2, 4),
+                                 "out_projection": round(t3, 4)}},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +358,9 @@ def main(argv=None):
                     help="W8A8 workloads: the step is RMSNorm + quantization + GEMM (fused normalization)")
     ap.add_argument("--layernorm", action="store_true",
                     help="W8A8 workloads: the step is LayerNorm + quantization + GEMM (fused normalization)")
+    ap.add_argument("--dit-block", action="store_true",
+                    help="time the Wan-14B-480p DiT attention block built from the fused pieces "
+                         "(LayerNorm+W8A8 QKV, q/k-RMSNorm attention, W8A8 out)")
     ap.add_argument("--qk-norm", action="store_true",
                     help="attention workloads: Q, K, V as views of a fused [B, N, 3, H, d] projection output and "
                          "the step is attention with the per-token q/k RMSNorm fused into the quantization")
@@ -296,6 +373,8 @@ def main(argv=None):
         return 2
     if a.workload.startswith("w8a8-"):
         return bench_w8a8(a)
+    if a.dit_block:
+        return bench_dit_block(a)
 
     import numpy as np
     import torch

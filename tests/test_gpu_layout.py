@@ -91,3 +91,54 @@ def test_dit_attention_block_without_copies():
         assert torch.equal(a.permute(0, 2, 1, 3), a2)
         assert torch.equal(z, z2)
         assert torch.isfinite(z.float()).all()
+
+
+def test_dit_block_with_fused_norms():
+    """A Wan-style DiT attention block from the library's fused pieces, with
+    no normalized tensor and no layout copy in memory:
+      LayerNorm (modulation as gamma = 1 + scale, beta = shift) fused into the
+      W8A8 QKV projection -> attention with the q/k RMSNorm fused, on views of
+      the projection output -> W8A8 output projection on the attention output
+      in place;
+    against the chain taken step by step: LayerNorm + quantization, GEMM, the
+    q/k normalization by the oracle into contiguous bf16 tensors, the plain
+    forward, a copy into the projection layout, the output projection.  Bit
+    for bit."""
+    from oracle import norm
+    B, N, H, d = 1, 900, 4, 128
+    C = H * d
+    rng = np.random.default_rng(1)
+    xb = W.f32_to_bf16_bits((rng.standard_normal((B * N, C)) * 3 + 0.5).astype(np.float32))
+    x = dev_bf16(xb)
+    f = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()
+    gamma, beta = f(1 + 0.2 * rng.standard_normal(C)), f(0.1 * rng.standard_normal(C))
+    gq, gk = (1 + 0.1 * rng.standard_normal(C)).astype(np.float32), (1 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    wqkv = dev_bf16(W.f32_to_bf16_bits((rng.standard_normal((3 * C, C)) / math.sqrt(C)).astype(np.float32)))
+    wo = dev_bf16(W.f32_to_bf16_bits((rng.standard_normal((C, C)) / math.sqrt(C)).astype(np.float32)))
+    bqkv, bo = f(rng.standard_normal(3 * C)), f(rng.standard_normal(C))
+    wqc, wqs = sq.w8a8_quantize(wqkv)
+    woc, wos = sq.w8a8_quantize(wo)
+    for pv in ("bf16", "fp8"):
+        print(f"case dit block fused norms pv={pv} N={N} H={H} d={d}", flush=True)
+        y = sq.w8a8_linear_layernorm(x, wqc, wqs, gamma=gamma, beta=beta, eps=1e-6, bias=bqkv,
+                                     out_dtype=torch.bfloat16)                          # [B*N, 3C]
+        qkv = y.view(B, N, 3, H, d)
+        a = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+        sq.forward_qknorm(*(qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3)), torch.from_numpy(gq).cuda(),
+                          torch.from_numpy(gk).cuda(), 1e-6, pv=pv, out=a.permute(0, 2, 1, 3))
+        z = sq.w8a8_linear(a.view(B * N, C), woc, wos, bias=bo, out_dtype=torch.bfloat16)
+        # step by step
+        xc, xs, _, _ = sq.w8a8_layernorm_quantize(x, gamma, beta, 1e-6)
+        y2 = sq.w8a8_gemm(xc, xs, wqc, wqs, bias=bqkv, out_dtype=torch.bfloat16)
+        yh = y2.view(B, N, 3, H, d).cpu().view(torch.int16).numpy().view(np.uint16)
+        qn = norm.qk_rmsnorm(np.ascontiguousarray(yh[:, :, 0].transpose(0, 2, 1, 3)), gq, 1e-6)
+        kn = norm.qk_rmsnorm(np.ascontiguousarray(yh[:, :, 1].transpose(0, 2, 1, 3)), gk, 1e-6)
+        vc = y2.view(B, N, 3, H, d)[:, :, 2].permute(0, 2, 1, 3).contiguous()
+        a2 = sq.forward(dev_bf16(qn), dev_bf16(kn), vc, pv=pv, out_dtype=torch.bfloat16)   # [B,H,N,d]
+        z2 = sq.w8a8_linear(a2.permute(0, 2, 1, 3).contiguous().view(B * N, C), woc, wos, bias=bo,
+                            out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        assert torch.equal(a.permute(0, 2, 1, 3), a2)
+        assert torch.equal(z, z2)
+        assert torch.isfinite(z.float()).all()
