@@ -106,6 +106,17 @@ SQ_HD bool acc192_is_neg(const Acc192& a) { return (a.w2 >> 63) != 0; }
 
 // Adds one bf16 value (16-bit pattern) to the window or the full accumulator.
 // Returns true if the value is out of range (|x| >= 2^33, Inf or NaN).
+// A value outside the fast window into the 192-bit accumulator; true if it is
+// out of range (biased exponent >= KMEAN_RANGE_EXP: Inf, NaN, |x| >= 2^33).
+SQ_HD bool kmean_add_outside(Acc192& acc, uint32_t b) {
+  uint32_t E = (b >> 7) & 0xFFu;
+  uint32_t M = (b & 0x7Fu) | (E ? 0x80u : 0u);
+  int s = (int)(E ? E : 1u) - 1;
+  if (E >= KMEAN_RANGE_EXP) return true;
+  if (M) acc192_add_shifted(acc, M, s, (b & 0x8000u) != 0);
+  return false;
+}
+
 SQ_HD bool kmean_accumulate(Acc192& acc, int64_t& win, uint32_t b) {
   uint32_t E = (b >> 7) & 0xFFu;
   uint32_t M = (b & 0x7Fu) | (E ? 0x80u : 0u);
@@ -117,14 +128,39 @@ SQ_HD bool kmean_accumulate(Acc192& acc, int64_t& win, uint32_t b) {
     win += neg ? -v : v;
     return false;
   }
-  if (E >= KMEAN_RANGE_EXP) return true;
-  if (M) acc192_add_shifted(acc, M, s, neg);
-  return false;
+  return kmean_add_outside(acc, b);
 }
 
 SQ_HD void kmean_flush_window(Acc192& acc, int64_t& win) {
   acc192_add_i64_shl(acc, win, KMEAN_W0);
   win = 0;
+}
+
+// The same window as a binary64 sum.  A bf16 value in the window (biased
+// exponent W0 + 1 .. W0 + WBITS) is a multiple of 2^(W0 + UNIT_EXP) = 2^-33
+// below 2^14 in magnitude, so a double that has added at most
+// KMEAN_F64_ADDS of them holds their exact sum (below 2^20: a multiple of
+// 2^-33 with at most 53 significant bits); each add is then exact.
+constexpr int KMEAN_F64_ADDS = 64;
+SQ_HD bool kmean_in_window(uint32_t b) {
+  return ((b >> 7) & 0xFFu) - (uint32_t)(KMEAN_W0 + 1) < (uint32_t)KMEAN_WBITS;
+}
+// b as a double if it is in the window, else 0 (exact: a normal bf16 widened)
+SQ_HD double kmean_window_value(uint32_t b) {
+  const uint32_t u = kmean_in_window(b) ? (b << 16) : 0u;
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return (double)f;
+}
+// acc += win, win = 0.  win * 2^33 is an integer below 2^53: split into
+// hi * 2^32 + lo with both parts converted exactly.
+SQ_HD void kmean_flush_f64(Acc192& acc, double& win) {
+  const double v = win * 0x1p33;
+  const double hi = __builtin_floor(v * 0x1p-32);
+  const double lo = v - hi * 0x1p32;  // in [0, 2^32)
+  const int64_t iv = (int64_t)(int32_t)hi * 4294967296LL + (int64_t)(uint32_t)lo;
+  acc192_add_i64_shl(acc, iv, KMEAN_W0);
+  win = 0.0;
 }
 
 // 32-bit limb helpers for the final division (little-endian limbs).

@@ -72,43 +72,75 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
   int r1 = min(N, r0 + rows_per_chunk);
 
   Acc192 acc[8];
-  int64_t win[8];
+  double win[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     acc192_zero(acc[j]);
-    win[j] = 0;
+    win[j] = 0.0;
   }
   bool bad = false;
   float gw[8];
   if constexpr (NORM) norm_weights(nm, bh, lk.H, D, cg * 8, gw);
   const float* rr = NORM ? nm.r + (bh / lk.H) * N : nullptr;
+  // values in the fast window add into the doubles (exact for up to
+  // KMEAN_F64_ADDS rows, then flushed); a chunk holding any other value
+  // sends those into the 192-bit accumulators
+  for (int rb = r0 + rg; rb < r1; rb += KMEAN_F64_ADDS * RPP) {
+    const int re = min(r1, rb + KMEAN_F64_ADDS * RPP);
 #pragma unroll 4
-  for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(kh + (long long)r * lk.sn + cg * 8);
-    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+    for (int r = rb; r < re; r += RPP) {
+      v4i w = *(const v4i*)(kh + (long long)r * lk.sn + cg * 8);
+      if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+      bool inside = true;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t u = (uint32_t)w[j];
-      bad |= kmean_accumulate(acc[2 * j], win[2 * j], u & 0xFFFFu);
-      bad |= kmean_accumulate(acc[2 * j + 1], win[2 * j + 1], u >> 16);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        inside &= kmean_in_window(b);
+        win[j] += kmean_window_value(b);
+      }
+      if (!inside) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          if (!kmean_in_window(b)) bad |= kmean_add_outside(acc[j], b);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kmean_flush_f64(acc[j], win[j]);
+  }
+
+  // reduce the RPP row groups of each channel: the 64 / CPR groups of a wave
+  // by lane exchanges, then the 4 waves through LDS
+  const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+  for (int o = CPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint64_t v[3] = {acc[j].w0, acc[j].w1, acc[j].w2};
+      uint64_t x[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const uint32_t lo = __shfl_xor((uint32_t)v[i], o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(v[i] >> 32), o, 64);
+        x[i] = ((uint64_t)hi << 32) | lo;
+      }
+      acc192_add(acc[j], x[0], x[1], x[2]);
     }
   }
+  __shared__ Acc192 red[4][D];
+  __shared__ int redbad[4];
+  const bool wbad = __any(bad);
+  if (lane < CPR) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kmean_flush_window(acc[j], win[j]);
-
-  // reduce the RPP row groups of each channel through LDS
-  __shared__ Acc192 red[RPP][D];
-  __shared__ int redbad[256];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) red[rg][cg * 8 + j] = acc[j];
-  redbad[t] = bad ? 1 : 0;
+    for (int j = 0; j < 8; ++j) red[wave][cg * 8 + j] = acc[j];
+  }
+  if (lane == 0) redbad[wave] = wbad ? 1 : 0;
   __syncthreads();
   if (t < D) {
-    Acc192 s;
-    acc192_zero(s);
-    int anybad = 0;
-    for (int g = 0; g < RPP; ++g) acc192_add(s, red[g][t]);
-    for (int i = 0; i < 256; ++i) anybad |= redbad[i];
+    Acc192 s = red[0][t];
+    for (int g = 1; g < 4; ++g) acc192_add(s, red[g][t]);
+    const int anybad = redbad[0] | redbad[1] | redbad[2] | redbad[3];
     uint64_t* p = partial + ((bh * S + chunk) * D + t) * 4;
     p[0] = s.w0;
     p[1] = s.w1;
@@ -150,6 +182,10 @@ __device__ __forceinline__ float block_max_256(float v, float* sh) {
 
 // grid (nblocks, B*H), 256 threads.  One work-group per block of `block` rows.
 // mean == nullptr: plain Q.  Otherwise x = fl32(K - mean[c]) (IEEE subtract).
+// Blocks of at most QCACHE * RPP rows (128 at D = 128, 256 at D = 64) are
+// read once and kept in registers between the absmax and the coding pass;
+// larger blocks are read twice.
+constexpr int QCACHE = 8;
 template <int D, bool NORM>
 __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, Lay lx, int N, int block,
                                                        const float* __restrict__ mean,
@@ -176,11 +212,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   float gw[8];
   if constexpr (NORM) norm_weights(nm, bh, lx.H, D, cg * 8, gw);
   const float* rr = NORM ? nm.r + (bh / lx.H) * N : nullptr;
-  float amax = 0.0f;
-#pragma unroll 4
-  for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
-    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+  auto chunk_max = [&](v4i w, float m) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
@@ -189,7 +221,33 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
         a = a - mu[2 * j];
         b = b - mu[2 * j + 1];
       }
-      amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
+      m = fmaxf(m, fmaxf(fabsf(a), fabsf(b)));
+    }
+    return m;
+  };
+  const bool resident = r1 - r0 <= QCACHE * RPP;  // uniform over the work-group
+  v4i cache[QCACHE];
+  float amax = 0.0f;
+  if (resident) {
+#pragma unroll
+    for (int i = 0; i < QCACHE; ++i) {
+      const int r = r0 + rg + i * RPP;
+      cache[i] = r < r1 ? *(const v4i*)(xh + (long long)r * lx.sn + cg * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < QCACHE; ++i) {
+      const int r = r0 + rg + i * RPP;
+      if (r < r1) {
+        if constexpr (NORM) cache[i] = norm_chunk(cache[i], rr[r], gw);
+        amax = chunk_max(cache[i], amax);
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int r = r0 + rg; r < r1; r += RPP) {
+      v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
+      if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+      amax = chunk_max(w, amax);
     }
   }
   // a NaN mean (K out of range) poisons the whole block's scale
@@ -201,10 +259,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   const bool fast = s >= 0x1p-125f;  // 1/s finite
   const float y = 1.0f / s;          // correctly rounded
 
-#pragma unroll 2
-  for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
-    if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+  auto code_chunk = [&](v4i w, int r) {
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -220,6 +275,20 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
       packed[j >> 2] |= ((uint32_t)(c & 0xFF)) << ((j & 3) * 8);
     }
     *(uint2*)(ch + (long long)r * D + cg * 8) = make_uint2(packed[0], packed[1]);
+  };
+  if (resident) {
+#pragma unroll
+    for (int i = 0; i < QCACHE; ++i) {
+      const int r = r0 + rg + i * RPP;
+      if (r < r1) code_chunk(cache[i], r);
+    }
+  } else {
+#pragma unroll 2
+    for (int r = r0 + rg; r < r1; r += RPP) {
+      v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
+      if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+      code_chunk(w, r);
+    }
   }
 }
 
@@ -433,9 +502,9 @@ __global__ __launch_bounds__(256) void v_tiles_fp8_kernel(const uint8_t* __restr
   } while (0)
 
 int kmean_chunks(int BH, int N) {
-  // enough work-groups to cover the chip a few times, each at least 256 rows;
-  // at most 2^18 rows per chunk so that each thread adds at most 2^14 values
-  // (< 2^48 each) into its 64-bit window accumulator
+  // enough work-groups to cover the chip a few times, each at least 256 rows
+  // and at most 2^18 (the binary64 windows are flushed every
+  // KMEAN_F64_ADDS rows of a thread, whatever the chunk length)
   int s = (2048 + BH - 1) / BH;
   int maxs = (N + 255) / 256;
   if (s > maxs) s = maxs;

@@ -29,18 +29,27 @@ using namespace sqattn;
 int main(int argc, char** argv) {
   char mode[16];
   if (scanf("%15s", mode) != 1) return 2;
-  if (!strcmp(mode, "mean")) {
+  if (!strcmp(mode, "mean") || !strcmp(mode, "meanf")) {
+    const bool f64 = mode[4] == 'f';
     int cols; if (scanf("%d", &cols) != 1) return 2;
     for (int c = 0; c < cols; ++c) {
       int n; if (scanf("%d", &n) != 1) return 2;
-      Acc192 acc; acc192_zero(acc); int64_t win = 0; bool bad = false;
+      Acc192 acc; acc192_zero(acc); int64_t win = 0; double wf = 0.0; bool bad = false;
       for (int i = 0; i < n; ++i) { unsigned b; if (scanf("%u", &b) != 1) return 2;
-        bad |= kmean_accumulate(acc, win, b);
-        if ((i & 1023) == 1023) kmean_flush_window(acc, win); }
+        if (f64) {  // the GPU kernel's order: binary64 window, the rest outside it
+          wf += kmean_window_value(b);
+          if (!kmean_in_window(b)) bad |= kmean_add_outside(acc, b);
+          if (i % KMEAN_F64_ADDS == KMEAN_F64_ADDS - 1) kmean_flush_f64(acc, wf);
+        } else {
+          bad |= kmean_accumulate(acc, win, b);
+          if ((i & 1023) == 1023) kmean_flush_window(acc, win);
+        } }
       kmean_flush_window(acc, win);
+      kmean_flush_f64(acc, wf);
       float m = acc192_mean_f32(acc, (uint32_t)n);
       uint32_t u; memcpy(&u, &m, 4);
-      printf("%d %u\n", bad ? 1 : 0, u);
+      printf("%d %u %llu %llu %llu\n", bad ? 1 : 0, u, (unsigned long long)acc.w0, (unsigned long long)acc.w1,
+             (unsigned long long)acc.w2);
     }
   } else {
     int n; if (scanf("%d", &n) != 1) return 2;
@@ -85,24 +94,46 @@ def _columns():
     return cols
 
 
-def test_kmean_host_build_matches_oracle(driver):
-    cols = _columns()
-    text = "mean %d\n" % len(cols) + "".join(
+def _window_edge_columns():
+    """Columns at the edges of the binary64 window: 64 in-window values of the
+    largest magnitude (16320 = 255 * 2^6) beside the smallest (2^-26), so a
+    flushed sum needs all 53 bits; values one binade either side of the
+    window; long columns of mixed signs."""
+    big, small = np.float32(16320.0), np.float32(129 * 2.0 ** -33)   # 129 * 2^-33: the window's unit is 2^-33
+    cols = [np.tile(np.float32([big, small]), 64), np.float32(([big] * 63 + [small]) * 9),
+            np.tile(np.float32([big, -small, -big, small, big]), 51),
+            np.float32([2.0 ** 14, 2.0 ** -27, 16320.0, 2.0 ** -26, -(2.0 ** 14) * 1.5, 1.0] * 40)]
+    rng = np.random.default_rng(5)
+    x = np.where(rng.random(20000) < 0.5, -1.0, 1.0) * np.exp2(rng.integers(-26, 14, 20000)) * rng.integers(128, 256, 20000) / 128
+    cols.append(x.astype(np.float32))
+    return [W.f32_to_bf16_bits(c) for c in cols]
+
+
+@pytest.mark.parametrize("mode", ["mean", "meanf"])
+def test_kmean_host_build_matches_oracle(driver, mode):
+    """mean: the 64-bit integer window; meanf: the binary64 window the GPU
+    kernel adds into (flushed every KMEAN_F64_ADDS values)."""
+    cols = _columns() + _window_edge_columns()
+    text = "%s %d\n" % (mode, len(cols)) + "".join(
         "%d %s\n" % (c.size, " ".join(str(int(v)) for v in c)) for c in cols)
     out = _run(driver, text)
     for i, c in enumerate(cols):
-        bad, bits = int(out[2 * i]), int(out[2 * i + 1])
+        bad, bits, w0, w1, w2 = (int(v) for v in out[5 * i: 5 * i + 5])
         assert bad == 0
         ref = quant.kmean_exact(c.reshape(-1, 1))[0]
         assert bits == int(np.float32(ref).view(np.uint32)), (i, bits, ref)
+        # the accumulator holds the exact sum in units of 2^-133 (two's complement)
+        units = sum(int(np.ldexp(float(v), 133)) for v in W.bf16_bits_to_f32(c).astype(np.float64))
+        assert (w0 | (w1 << 64) | (w2 << 128)) == units % (1 << 192), i
 
 
-def test_kmean_host_build_flags_out_of_range(driver):
+@pytest.mark.parametrize("mode", ["mean", "meanf"])
+def test_kmean_host_build_flags_out_of_range(driver, mode):
     cols = [W.f32_to_bf16_bits(np.float32([1.0, 2.0 ** 33])), W.f32_to_bf16_bits(np.float32([2.0 ** 32, -1.0])),
             np.uint16([0x7F80, 0x3F80])]
-    text = "mean 3\n" + "".join("%d %s\n" % (c.size, " ".join(str(int(v)) for v in c)) for c in cols)
+    text = "%s 3\n" % mode + "".join("%d %s\n" % (c.size, " ".join(str(int(v)) for v in c)) for c in cols)
     out = _run(driver, text)
-    assert [int(out[0]), int(out[2]), int(out[4])] == [1, 0, 1]
+    assert [int(out[0]), int(out[5]), int(out[10])] == [1, 0, 1]
 
 
 def test_e4m3_host_build_matches_oracle(driver):
