@@ -396,12 +396,22 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
   const int cg = t % CPR, rg = t / CPR;
   const uint16_t* vh = v + lay_row(lv, bh, 0);
   const int r0 = tt * KT, r1 = min(N, r0 + KT);
+  // the tile's KT / RPP chunks of this thread, read once and kept in
+  // registers for the coding pass (rows past N read as zeros, unused)
+  constexpr int NCH = KT / RPP;
+  static_assert(KT % RPP == 0, "whole passes per tile");
+  v4i w[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int r = r0 + rg + i * RPP;
+    w[i] = r < r1 ? *(const v4i*)(vh + (long long)r * lv.sn + cg * 8) : v4i{0, 0, 0, 0};
+  }
   float amax = 0.0f;
-  for (int r = r0 + rg; r < r1; r += RPP) {
-    v4i w = *(const v4i*)(vh + (long long)r * lv.sn + cg * 8);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t u = (uint32_t)w[j];
+      uint32_t u = (uint32_t)w[i][j];
       amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(u & 0xFFFFu)), fabsf(bf16_bits_to_f32(u >> 16))));
     }
   }
@@ -409,13 +419,14 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
   const float s = amax / 448.0f;
   if (t == 0) scales[bh * nt + tt] = s;
   const bool zero = !(s > 0.0f);
-  for (int r = r0 + rg; r < r0 + KT; r += RPP) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int r = r0 + rg + i * RPP;
     uint32_t packed[2] = {0u, 0u};
     if (r < r1) {
-      v4i w = *(const v4i*)(vh + (long long)r * lv.sn + cg * 8);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t u = (uint32_t)w[j >> 1];
+        uint32_t u = (uint32_t)w[i][j >> 1];
         float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
         uint32_t c = zero ? 0u : e4m3_encode_f32(a / s);
         packed[j >> 2] |= c << ((j & 3) * 8);
