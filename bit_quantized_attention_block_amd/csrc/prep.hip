@@ -85,24 +85,39 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t* __re
   // values in the fast window add into the doubles (exact for up to
   // KMEAN_F64_ADDS rows, then flushed); a chunk holding any other value
   // sends those into the 192-bit accumulators
+  // Rows are loaded KB at a time before any is added, so that the loads are
+  // in flight together; rows past the group's end read as zeros, which add
+  // nothing (a zero is exact in the window and outside it alike).
+  constexpr int KB = 4;
+  static_assert(KMEAN_F64_ADDS % KB == 0, "whole batches per window");
   for (int rb = r0 + rg; rb < r1; rb += KMEAN_F64_ADDS * RPP) {
     const int re = min(r1, rb + KMEAN_F64_ADDS * RPP);
-#pragma unroll 4
-    for (int r = rb; r < re; r += RPP) {
-      v4i w = *(const v4i*)(kh + (long long)r * lk.sn + cg * 8);
-      if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
-      bool inside = true;
+    for (int r = rb; r < re; r += KB * RPP) {
+      v4i w[KB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        inside &= kmean_in_window(b);
-        win[j] += kmean_window_value(b);
+      for (int u = 0; u < KB; ++u) {
+        const int ru = r + u * RPP;
+        w[u] = ru < re ? *(const v4i*)(kh + (long long)ru * lk.sn + cg * 8) : v4i{0, 0, 0, 0};
       }
-      if (!inside) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        if constexpr (NORM) {
+          const int ru = r + u * RPP;
+          if (ru < re) w[u] = norm_chunk(w[u], rr[ru], gw);
+        }
+        bool inside = true;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t b = ((uint32_t)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-          if (!kmean_in_window(b)) bad |= kmean_add_outside(acc[j], b);
+          const uint32_t b = ((uint32_t)w[u][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          inside &= kmean_in_window(b) || (b & 0x7FFFu) == 0;
+          win[j] += kmean_window_value(b);
+        }
+        if (!inside) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t b = ((uint32_t)w[u][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            if (!kmean_in_window(b)) bad |= kmean_add_outside(acc[j], b);
+          }
         }
       }
     }
