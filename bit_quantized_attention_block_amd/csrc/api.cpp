@@ -126,6 +126,21 @@ int hip_check(const char* what) {
   return SQATTN_OK;
 }
 
+// The attention kernel of the P.V type.  A work item is (head, 256-row query
+// block); work-group w runs on XCD w % 8 (round-robin dispatch) and takes item
+// (w % 8) * per_xcd + w / 8, so each XCD walks consecutive query blocks of the
+// same head, which share K/V tiles through that XCD's L2.
+int launch_attention(sqattn::AttnParams p, int d, int pv, hipStream_t st, const char* what) {
+  p.qtiles = (p.N + sqattn::ATT_QWG - 1) / sqattn::ATT_QWG;
+  const long long W = (long long)p.BH * p.qtiles;
+  p.per_xcd = (int)((W + 7) / 8);
+  const hipError_t e = pv == SQATTN_PV_BF16 ? sqattn::launch_attention_bf16(p, d, st)
+                                            : sqattn::launch_attention_fp8(p, d, st);
+  if (e != hipSuccess)
+    return fail(SQATTN_ERR_HIP, std::string(what) + ": setting the kernel's LDS size: " + hipGetErrorString(e));
+  return hip_check(what);
+}
+
 // Provides workspace: the caller's, or a stream-ordered allocation freed by
 // the destructor (also stream-ordered).
 struct Workspace {
@@ -370,9 +385,9 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   p.mask = mask;
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   p.lo = lay[3];
-  sqattn::launch_attention(p, d, pv_dtype, st);
-  return hip_check(qkn ? "sqattn_forward_qknorm launch"
-                       : mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
+  return launch_attention(p, d, pv_dtype, st,
+                          qkn ? "sqattn_forward_qknorm launch"
+                              : mask ? "sqattn_forward_sparse launch" : "sqattn_forward launch");
 }
 
 int sqattn_forward_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, float scale,
@@ -499,8 +514,8 @@ static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k
   p.mask = mask;
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   p.lo = sqattn::contiguous_lay(H, N, d);
-  sqattn::launch_attention(p, d, pv_dtype, (hipStream_t)stream);
-  return hip_check(mask ? "sqattn_attend_quantized_sparse launch" : "sqattn_attend_quantized launch");
+  return launch_attention(p, d, pv_dtype, (hipStream_t)stream,
+                          mask ? "sqattn_attend_quantized_sparse launch" : "sqattn_attend_quantized launch");
 }
 
 int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,

@@ -39,6 +39,8 @@
 // * Keys past N: the K tile reads row N-1 there (a real score of the same
 //   tile, so the tile max is unchanged), y is zeroed for them in the last
 //   tile, and the packed V tile is zero past N.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -452,23 +454,24 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
 }
 
 template <int D, bool SP>
-static void launch_d(const AttnParams& q, hipStream_t st) {
+static hipError_t launch_d(const AttnParams& q, hipStream_t st) {
   constexpr int lds = Geo<D>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
-  static bool configured = false;  // the attribute is per kernel, set once per process
-  if (!configured) {
-    (void)hipFuncSetAttribute((const void*)attn_fp8_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              lds);
-    configured = true;
-  }
+  // the attribute is per kernel: set once per process (the first status is kept)
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)attn_fp8_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               lds);
+  });
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((attn_fp8_kernel<D, SP>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
+  return hipSuccess;
 }
 
-void launch_attention_fp8(const AttnParams& q, int d, hipStream_t st) {
+hipError_t launch_attention_fp8(const AttnParams& q, int d, hipStream_t st) {
   const bool sp = q.mask != nullptr;
-  if (d == 128)
-    sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
-  else
-    sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
+  if (d == 128) return sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
+  return sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
 }
 
 }  // namespace sqattn

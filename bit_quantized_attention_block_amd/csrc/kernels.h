@@ -54,11 +54,12 @@ struct AttnParams {
   float scale_log2e;
 };
 
-void launch_attention(const AttnParams& p, int d, int pv, hipStream_t st);
-// 16-bit P.V kernel (software-pipelined); p.qtiles and p.per_xcd must be set.
-void launch_attention_bf16(const AttnParams& p, int d, hipStream_t st);
-// FP8 P.V kernel (software-pipelined, running max per tile); same requirements.
-void launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
+// 16-bit P.V kernel; p.qtiles and p.per_xcd must be set.  Returns the status
+// of the one-time kernel attribute setup (launch errors surface through
+// hipGetLastError as usual).
+hipError_t launch_attention_bf16(const AttnParams& p, int d, hipStream_t st);
+// FP8 P.V kernel (running max per tile); same requirements.
+hipError_t launch_attention_fp8(const AttnParams& p, int d, hipStream_t st);
 
 // W8A8 linear layer: 128x128 block quantizer and the block-scaled INT8 GEMM.
 // RMSNorm: inv_rms[r] = fl32(1 / fl32(sqrt(fl32(mean_k x[r,k]^2 + eps)))), the mean
