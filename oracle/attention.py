@@ -26,14 +26,23 @@ Readings where the pages are silent:
     of ``kv_tile`` in ascending order with running max m_t; P~_j =
     exp(s_j - m_t(j)) in (0, 1]; the FP8 operand is E4M3(448 * P~_j); the row
     sum accumulates the unrounded P~; V enters as s_v * decode(code_v).
-    Elements whose 448*P~ lies within ``eps_rel`` of an E4M3 rounding midpoint
-    may legitimately round either way in the kernel's binary32 arithmetic; the
-    possible effect of each is summed into a per-element envelope E.  The
-    default width is per row, eps_r = 2^-20 * (1 + M_r) with M_r the row's
-    largest |logit| in log2 units: the kernel's logit factor
-    sQ*sK*scale*log2(e) carries up to four binary32 roundings (2^-22
-    relative), so x - m is off by at most 2^-21 * M_r, and exp2 adds about
-    2^-22; the default doubles that bound.
+    Elements whose 448*P~ lies within ``eps_rel`` (relative) of an E4M3
+    rounding midpoint may legitimately round either way in the kernel's
+    binary32 arithmetic; the possible effect of each is summed into a
+    per-element envelope E.  The default width is per row,
+    eps_r = 2^-21 * (M_r + 3), M_r the row's largest |logit| in log2 units,
+    a bound on the relative error of 448*P~ computed in binary32 as
+      c  = fl32(fl32(sQ * fl32(scale * fl32(log2 e))) * sK)   (per tile)
+      mn = running max of fl32(Dmax_tile * c),  mp = fl32(mn - fl32(log2 448))
+      y  = exp2(fl32(D * c - mp))          (one fused multiply-add, D exact)
+    Only elements with y >= 2^-11 can round to a nonzero E4M3 value, so
+    |arg| <= 11 there.  With u = 2^-24: c is off by <= 4u relative (|D c| <=
+    M_r: 4u M_r), the running max by <= 5u M_r, mp's rounding adds
+    u (M_r + 9), fl32(log2 448) 8u, the FMA 11u, so the exponent argument is
+    off by <= u (10 M_r + 28); times ln 2, plus 2u for v_exp_f32 (1 ulp),
+    the relative error of y is <= u (6.94 M_r + 21.4) < 2^-21 (M_r + 3).
+    tests/test_oracle_fp8_envelope.py checks this bound against an exact
+    evaluation of that binary32 chain on heavy-tailed data.
 """
 from __future__ import annotations
 
@@ -42,7 +51,7 @@ import numpy as np
 from . import fp
 
 __all__ = ["int_scores", "logits", "softmax_pv", "attention_fp64", "attend_bf16",
-           "attend_fp8", "e4m3_round_f64", "MASK_Q", "MASK_K", "key_mask"]
+           "attend_fp8", "e4m3_round_f64", "envelope_width", "MASK_Q", "MASK_K", "key_mask"]
 
 MASK_Q = 128   # query rows per block-mask row
 MASK_K = 64    # keys per block-mask column
@@ -112,6 +121,12 @@ def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_blo
     return out
 
 
+def envelope_width(max_abs_logit_log2):
+    """Relative width eps_r = 2^-21 (M_r + 3) of the FP8 ambiguity band for a
+    row whose largest |logit| is M_r (log2 units); see the module docstring."""
+    return 2.0 ** -21 * (3.0 + np.asarray(max_abs_logit_log2, np.float64))
+
+
 def e4m3_round_f64(y: np.ndarray):
     """Nearest-even E4M3FN rounding of non-negative float64 values.
 
@@ -174,7 +189,7 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
         if round_p is None:
             if eps_rel is None:
                 # the largest |logit| among the keys the kernel evaluates (kept keys)
-                eps = 2.0 ** -20 * (1.0 + np.where(keep, np.abs(S), 0.0).max(axis=1, keepdims=True) / np.log(2.0))
+                eps = envelope_width(np.where(keep, np.abs(S), 0.0).max(axis=1, keepdims=True) / np.log(2.0))
             else:
                 eps = eps_rel
             frac = c - np.floor(c)

@@ -11,7 +11,7 @@ import torch
 
 import bit_quantized_attention_block_amd as sq
 import workloads as W
-from gpu_util import MAX_ABS, MIN_COS, dev_bf16, host, out_metrics
+from gpu_util import MAX_ABS, MIN_COS, check_fp8, dev_bf16, host, out_metrics
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +29,7 @@ def _masked_case(w, mask, N=None, d=None, B=None, H=None, pv=None, heads=None):
     out_h = host(out)
     idx = list(range(B_ * H_)) if heads is None else list(heads)
     g_rows, r_rows, e_rows = [], [], []
+    hits = elements = 0
     for i in idx:
         b, h = divmod(i, H_)
         r = oracle.forward_head(q[b, h], k[b, h], v[b, h], rows[i], w.q_block, 64, w.scale, pv=pv,
@@ -39,10 +40,15 @@ def _masked_case(w, mask, N=None, d=None, B=None, H=None, pv=None, heads=None):
         g_rows.append(g)
         r_rows.append(r["out"])
         e_rows.append(r["envelope"])
+        if pv == "fp8":
+            hits += r["envelope_hits"]
+            elements += len(rows[i]) * N_
     mt = out_metrics(g_rows, r_rows, e_rows if pv == "fp8" else None)
     print(f"  max_abs {mt['max_abs']:.3g} excess {mt['max_excess']:.3g} cos {mt['cos']:.7f}", flush=True)
     assert mt["max_excess"] <= MAX_ABS, mt
     assert mt["cos"] >= MIN_COS, mt
+    if pv == "fp8":
+        check_fp8(mt, hits, elements)
     return out
 
 
