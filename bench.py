@@ -449,7 +449,7 @@ def main(argv=None):
         vp = sq.pack_v(V, "bf16")
 
     def kern():
-        sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out,
+        sq.attend_packed(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out,
                             block_mask=M)
 
     reps = a.kernel_reps or a.steps

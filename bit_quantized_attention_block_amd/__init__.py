@@ -16,7 +16,7 @@ import math
 import os
 
 __all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "forward",
-           "attend_quantized", "pack_v", "workspace_bytes", "packed_v_bytes",
+           "attend_quantized", "attend_packed", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
            "w8a8_linear_rmsnorm", "w8a8_rmsnorm_workspace_bytes", "forward_qknorm",
@@ -48,6 +48,7 @@ EXPORTS = {
     "sqattn_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_attend_quantized": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                      _vp]),
+    "sqattn_attend_packed": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp]),
     "sqattn_forward_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "sqattn_forward_strided": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _i, _vp, _vp, _vp, _sz, _vp,
                                     _vp]),
@@ -56,6 +57,8 @@ EXPORTS = {
                                    _sz, _vp, _vp]),
     "sqattn_attend_quantized_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                             _vp, _vp]),
+    "sqattn_attend_packed_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp,
+                                         _vp]),
     "sqattn_w8a8_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "sqattn_w8a8_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "sqattn_w8a8_workspace_bytes": (_sz, [_i, _i]),
@@ -276,6 +279,11 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
         _check(lib().sqattn_forward_sparse(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(m),
                                            _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
         return out
+    if q_block == 128 and od == OUT_FP32:
+        # the default options: the plain entry point (q_block 128, k/v blocks 64, fp32 out)
+        _check(lib().sqattn_forward(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
+                                    _ptr(w), wb, _stream(q)))
+        return out
     _check(lib().sqattn_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                    _ptr(w), wb, _stream(q), ctypes.byref(o)))
     return out
@@ -353,35 +361,55 @@ def pack_v(v, pv="bf16"):
     return packed
 
 
-def attend_quantized(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
-                     pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
-    """The attention kernel alone, on quantized Q/K and packed V (see pack_v);
-    block_mask as in forward."""
+def _attend(packed, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block, out, out_dtype, block_mask):
     torch = _torch()
     _dev(q_i8, "q_i8", torch.int8)
     _dev(k_i8, "k_i8", torch.int8)
     _dev(q_scale, "q_scale", torch.float32)
     _dev(k_scale, "k_scale", torch.float32)
-    _dev(v_packed, "v_packed", torch.uint8)
     B, H, N, d = _shape(q_i8)
-    if v_packed.numel() < packed_v_bytes(B, H, N, d, pv):
-        raise ValueError("v_packed is too small")
+    if packed:
+        _dev(v, "v_packed", torch.uint8)
+        if v.numel() < packed_v_bytes(B, H, N, d, pv):
+            raise ValueError("v_packed is too small")
+    else:
+        _dev(v, "v", torch.bfloat16 if _PV[pv] == PV_BF16 else torch.uint8)
+        if _shape(v) != (B, H, N, d):
+            raise ValueError("v must have the shape of q_i8")
     if _PV[pv] == PV_FP8:
         _dev(v_scale, "v_scale", torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, od = _out(out, (B, H, N, d), q_i8.device, out_dtype)
     o = _opts(q_block, od)
+    L = lib()
+    args = (_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v), _ptr(v_scale), B, H, N, d,
+            float(scale), _PV[pv])
     if block_mask is not None:
         m = _mask(block_mask, B, H, N)
-        _check(lib().sqattn_attend_quantized_sparse(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
-                                                    _ptr(v_packed), _ptr(v_scale), B, H, N, d, float(scale),
-                                                    _PV[pv], _ptr(m), ctypes.byref(o), _ptr(out), _stream(q_i8)))
+        fn = L.sqattn_attend_packed_sparse if packed else L.sqattn_attend_quantized_sparse
+        _check(fn(*args, _ptr(m), ctypes.byref(o), _ptr(out), _stream(q_i8)))
         return out
-    _check(lib().sqattn_attend_quantized(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_packed),
-                                         _ptr(v_scale), B, H, N, d, float(scale), _PV[pv], ctypes.byref(o),
-                                         _ptr(out), _stream(q_i8)))
+    fn = L.sqattn_attend_packed if packed else L.sqattn_attend_quantized
+    _check(fn(*args, ctypes.byref(o), _ptr(out), _stream(q_i8)))
     return out
+
+
+def attend_quantized(q_i8, q_scale, k_i8, k_scale, v, v_scale=None, scale: float | None = None,
+                     pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
+    """Attention on quantized Q/K (from quantize_qk) and V: bf16 [B,H,N,d] for
+    pv="bf16", E4M3 codes (from quantize_v_fp8) with their scales for
+    pv="fp8"; block_mask as in forward."""
+    return _attend(False, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block, out, out_dtype,
+                   block_mask)
+
+
+def attend_packed(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
+                  pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
+    """The attention kernel alone, on quantized Q/K and V already in the
+    kernel's tile layout (see pack_v)."""
+    return _attend(True, q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, scale, pv, q_block, out, out_dtype,
+                   block_mask)
 
 
 # --------------------------------------------------------------------------- W8A8 linear

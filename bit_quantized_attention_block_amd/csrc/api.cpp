@@ -515,26 +515,83 @@ static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k
   p.mq = (N + sqattn::SP_MQ - 1) / sqattn::SP_MQ;
   p.lo = sqattn::contiguous_lay(H, N, d);
   return launch_attention(p, d, pv_dtype, (hipStream_t)stream,
-                          mask ? "sqattn_attend_quantized_sparse launch" : "sqattn_attend_quantized launch");
+                          mask ? "sqattn_attend_packed_sparse launch" : "sqattn_attend_packed launch");
 }
 
-int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
-                            const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
-                            int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
+int sqattn_attend_packed(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                         const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
+                         int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
   return attend_impl(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, B, H, N, d, scale, pv_dtype, nullptr, opts,
                      out, stream);
 }
 
-int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                                   const float* k_scale, const void* v_packed, const float* v_scale, int B, int H,
-                                   int N, int d, float scale, int pv_dtype, const uint8_t* block_mask,
-                                   const sqattn_opts* opts, void* out, void* stream) {
+int sqattn_attend_packed_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                const void* v_packed, const float* v_scale, int B, int H, int N, int d, float scale,
+                                int pv_dtype, const uint8_t* block_mask, const sqattn_opts* opts, void* out,
+                                void* stream) {
   if (!block_mask) {
     g_err.clear();
     return fail(SQATTN_ERR_INVALID_ARG, "block_mask is NULL");
   }
   return attend_impl(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, B, H, N, d, scale, pv_dtype, block_mask,
                      opts, out, stream);
+}
+
+// Raw V (bf16, or E4M3 codes for FP8) into a stream-ordered temporary in the
+// kernel's tile layout, then the kernel.  The temporary is freed
+// stream-ordered after the launch.
+static int attend_raw(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                      const void* v, const float* v_scale, int B, int H, int N, int d, float scale, int pv_dtype,
+                      const uint8_t* mask, const sqattn_opts* opts, void* out, void* stream) {
+  g_err.clear();
+  int s;
+  Sizes z;
+  if ((s = check_ptr(v, "v", 16))) return s;
+  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if (pv_dtype != SQATTN_PV_BF16 && pv_dtype != SQATTN_PV_FP8_E4M3)
+    return fail(SQATTN_ERR_INVALID_ARG, "unknown pv_dtype");
+  // everything the kernel call checks, before anything is allocated or enqueued
+  if ((s = check_ptr(q_i8, "q_i8", 16)) || (s = check_ptr(k_i8, "k_i8", 16)) ||
+      (s = check_ptr(q_scale, "q_scale", 4)) || (s = check_ptr(k_scale, "k_scale", 4)) ||
+      (s = check_ptr(out, "out", 16)))
+    return s;
+  if (pv_dtype == SQATTN_PV_FP8_E4M3 && (s = check_ptr(v_scale, "v_scale", 4))) return s;
+  if (!std::isfinite(scale) || scale < 0.0f) return fail(SQATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  Opts o;
+  if ((s = resolve_opts(opts, &o))) return s;
+  if (mask && (s = check_sparse(N))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  const size_t bytes = (size_t)(z.BH * z.nt * z.d * sqattn::KT) * (pv_dtype == SQATTN_PV_BF16 ? 2 : 1);
+  if ((s = ws.acquire(nullptr, 0, bytes, st))) return s;
+  if (pv_dtype == SQATTN_PV_BF16)
+    sqattn::launch_v_tiles_bf16((const uint16_t*)v, sqattn::contiguous_lay(H, N, d), (int)z.BH, N, d,
+                                ws.at<uint16_t>(0), st);
+  else
+    sqattn::launch_v_tiles_fp8((const uint8_t*)v, (int)z.BH, N, d, ws.at<uint8_t>(0), st);
+  if ((s = hip_check("V packing launch"))) return s;
+  s = attend_impl(q_i8, q_scale, k_i8, k_scale, ws.at<void>(0), v_scale, B, H, N, d, scale, pv_dtype, mask, opts,
+                  out, stream);
+  return s;
+}
+
+int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                            const void* v, const float* v_scale, int B, int H, int N, int d, float scale,
+                            int pv_dtype, const sqattn_opts* opts, void* out, void* stream) {
+  return attend_raw(q_i8, q_scale, k_i8, k_scale, v, v_scale, B, H, N, d, scale, pv_dtype, nullptr, opts, out,
+                    stream);
+}
+
+int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                   const float* k_scale, const void* v, const float* v_scale, int B, int H, int N,
+                                   int d, float scale, int pv_dtype, const uint8_t* block_mask,
+                                   const sqattn_opts* opts, void* out, void* stream) {
+  if (!block_mask) {
+    g_err.clear();
+    return fail(SQATTN_ERR_INVALID_ARG, "block_mask is NULL");
+  }
+  return attend_raw(q_i8, q_scale, k_i8, k_scale, v, v_scale, B, H, N, d, scale, pv_dtype, block_mask, opts, out,
+                    stream);
 }
 
 int sqattn_w8a8_quantize(const void* x, int rows, int cols, int8_t* codes, float* scales, void* stream) {

@@ -119,7 +119,7 @@ def run_target(workload: str, reps: int) -> None:
                 vp = sq.pack_v(vc, "fp8")
             else:
                 vs, vp = None, sq.pack_v(V, "bf16")
-            sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+            sq.attend_packed(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
             torch.cuda.synchronize()
             print(f"[target] {w.name}: rep done", flush=True)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -111,7 +111,11 @@ const char* sqattn_last_error(void);
 size_t sqattn_quantize_qk_workspace_bytes(int B, int H, int N, int d);
 
 /*
- * Quantize Q and K (smoothing K by its per-channel mean first).
+ * Quantize Q and K (smoothing K by its per-channel mean first): the low-bit
+ * Q/K of the method (jefxiong.cn "AIGC weekend special 5.10", section 1.2
+ * item (1): Q and K to low bit so that QK^T runs on integer matrix units) with
+ * the outlier smoothing of K (GVCLab Video-Generation-101 systems survey,
+ * reference [3] title); per-block INT8 with absmax/127 scales as read above.
  *   q, k      : bf16 [B,H,N,d] inputs.
  *   q_i8      : int8 [B,H,N,d] codes of Q;  q_scale : float [B,H,ceil(N/q_block)].
  *   k_i8      : int8 [B,H,N,d] codes of K'; k_scale : float [B,H,ceil(N/k_block)].
@@ -146,7 +150,11 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
 /*
  * Full forward: out = softmax(Q K^T * scale) V computed on quantized
  * operands (the steps above), out [B,H,N,d] fp32 (bf16 with
- * opts->out_dtype = SQATTN_OUT_BF16 in sqattn_forward_ex).
+ * opts->out_dtype = SQATTN_OUT_BF16 in sqattn_forward_ex) -- the quantized
+ * attention step of the DiT denoiser (digipub.cc TurboDiffusion article,
+ * attention-acceleration paragraph: SageAttention2++; jefxiong.cn "AIGC
+ * weekend special 5.10", section 1.2 item (1); GVCLab research log
+ * 2026-09-02, section 5.5 table: 16-bit or FP8 P.V).
  *   scale     : softmax scale applied to the logits (commonly 1/sqrt(d)),
  *               finite and >= 0.
  *   pv_dtype  : SQATTN_PV_BF16 or SQATTN_PV_FP8_E4M3.
@@ -181,18 +189,36 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
                   void* stream);
 
 /*
- * Attention on prepared operands: a single kernel launch (the hot kernel
- * alone, for parity and kernel timing).
+ * Attention on quantized operands: the logits from the INT8 codes of Q and
+ * smoothed K on the integer matrix units, softmax, P.V in bf16 or FP8
+ * (jefxiong.cn "AIGC weekend special 5.10", section 1.2 item (1); GVCLab
+ * research log 2026-09-02, section 5.5 table, SageAttention2 row), i.e. the
+ * forward without its quantization steps.
  *   q_i8/q_scale/k_i8/k_scale : as written by sqattn_quantize_qk with
  *              k_block = 64 and q_block = opts->q_block (default 128).
- *   v_packed : from sqattn_pack_v with the same pv_dtype.
+ *   v        : [B,H,N,d] bf16 for SQATTN_PV_BF16; E4M3 codes (uint8) as
+ *              written by sqattn_quantize_v_fp8 for SQATTN_PV_FP8_E4M3.
  *   v_scale  : [B,H,ceil(N/64)] from sqattn_quantize_v_fp8 for FP8; NULL for bf16.
  *   out      : [B,H,N,d], fp32 or bf16 as opts->out_dtype says.
+ * V is first laid out in the kernel's tile layout (as sqattn_pack_v) in a
+ * temporary of sqattn_packed_v_bytes() allocated and freed stream-ordered on
+ * `stream`; arguments are validated before anything is allocated.
  */
 int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                            const float* k_scale, const void* v_packed, const float* v_scale,
+                            const float* k_scale, const void* v, const float* v_scale,
                             int B, int H, int N, int d, float scale, int pv_dtype,
                             const sqattn_opts* opts, void* out, void* stream);
+
+/*
+ * sqattn_attend_quantized on V already in the kernel's tile layout: a single
+ * kernel launch (the hot kernel alone, for kernel timing).
+ *   v_packed : from sqattn_pack_v with the same pv_dtype.
+ * Everything else as sqattn_attend_quantized.
+ */
+int sqattn_attend_packed(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                         const float* k_scale, const void* v_packed, const float* v_scale, int B,
+                         int H, int N, int d, float scale, int pv_dtype, const sqattn_opts* opts,
+                         void* out, void* stream);
 
 /*
  * Block-sparse attention: the same step computed only on the (query block,
@@ -213,17 +239,22 @@ int sqattn_attend_quantized(const int8_t* q_i8, const float* q_scale, const int8
  * dropped tile's V can reach rows of the other query block of the same
  * work-group through 0 * NaN).  N <= 262144 (4096 key tiles), else
  * SQATTN_ERR_UNSUPPORTED.  Everything else as sqattn_forward_ex /
- * sqattn_attend_quantized.
+ * sqattn_attend_quantized (raw V) / sqattn_attend_packed (packed V).
  */
 int sqattn_forward_sparse(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                           float scale, int pv_dtype, const uint8_t* block_mask, void* out,
                           void* workspace, size_t workspace_bytes, void* stream,
                           const sqattn_opts* opts);
 int sqattn_attend_quantized_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                                   const float* k_scale, const void* v_packed,
-                                   const float* v_scale, int B, int H, int N, int d, float scale,
-                                   int pv_dtype, const uint8_t* block_mask,
-                                   const sqattn_opts* opts, void* out, void* stream);
+                                   const float* k_scale, const void* v, const float* v_scale,
+                                   int B, int H, int N, int d, float scale, int pv_dtype,
+                                   const uint8_t* block_mask, const sqattn_opts* opts, void* out,
+                                   void* stream);
+int sqattn_attend_packed_sparse(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                const float* k_scale, const void* v_packed, const float* v_scale,
+                                int B, int H, int N, int d, float scale, int pv_dtype,
+                                const uint8_t* block_mask, const sqattn_opts* opts, void* out,
+                                void* stream);
 
 /*
  * sqattn_forward_ex / sqattn_forward_sparse on strided operands, so that a

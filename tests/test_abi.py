@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 27
+    assert len(names) == 29
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
@@ -86,6 +86,27 @@ def test_forward_validation(kw, code, needle):
     assert needle in _err()
 
 
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(out=FAKE + 4), INVALID, "aligned"),
+    (dict(d=96), UNSUPPORTED, "64 or 128"),
+    (dict(N=1 << 24), RANGE, "2^24"),
+    (dict(pv=2), INVALID, "pv_dtype"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(wsb=1), WORKSPACE, "needed"),
+])
+def test_plain_forward_validation(kw, code, needle):
+    # sqattn_forward (q, k, v, B, H, N, d, scale, pv_dtype, out, workspace, bytes, stream):
+    # the same checks as the _ex form with default options, before anything is enqueued
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, H=1, N=256, d=64, scale=0.125, pv=0, out=FAKE, ws=FAKE, wsb=1)
+    a.update(kw)
+    L = sq.lib()
+    rc = L.sqattn_forward(a["q"], a["k"], a["v"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["pv"], a["out"],
+                          a["ws"], a["wsb"], None)
+    assert rc == code
+    assert needle in _err()
+
+
 def test_quantize_validation():
     L = sq.lib()
     args = [FAKE, FAKE, 1, 1, 256, 128, 128, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None]
@@ -108,20 +129,29 @@ def test_quantize_validation():
 
 
 def test_attend_and_pack_validation():
+    # the raw-V entry point validates everything before it allocates its V
+    # temporary (so these calls enqueue and allocate nothing), like the packed one
     L = sq.lib()
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 300, 128, 0.1, 1, None, FAKE, None]
-    a = list(base)
-    a[5] = None                                           # fp8 needs v_scale
-    assert L.sqattn_attend_quantized(*a) == INVALID and "v_scale" in _err()
-    a = list(base)
-    a[11] = 7
-    assert L.sqattn_attend_quantized(*a) == INVALID
-    a = list(base)
-    a[4] = FAKE + 1
-    assert L.sqattn_attend_quantized(*a) == INVALID and "v_packed" in _err()
-    a = list(base)
-    a[9] = 32
-    assert L.sqattn_attend_quantized(*a) == UNSUPPORTED
+    for fn, vname in ((L.sqattn_attend_quantized, "v"), (L.sqattn_attend_packed, "v_packed")):
+        a = list(base)
+        a[5] = None                                           # fp8 needs v_scale
+        assert fn(*a) == INVALID and "v_scale" in _err()
+        a = list(base)
+        a[11] = 7
+        assert fn(*a) == INVALID
+        a = list(base)
+        a[4] = FAKE + 1
+        assert fn(*a) == INVALID and vname in _err()
+        a = list(base)
+        a[9] = 32
+        assert fn(*a) == UNSUPPORTED
+        a = list(base)
+        a[13] = None
+        assert fn(*a) == INVALID and "out" in _err()
+        a = list(base)
+        a[10] = float("inf")
+        assert fn(*a) == INVALID and "scale" in _err()
     assert L.sqattn_pack_v(FAKE, 1, 1, 100, 128, 3, FAKE, None) == INVALID
     assert L.sqattn_pack_v(FAKE, 1, 1, 100, 128, 0, None, None) == INVALID
     assert L.sqattn_pack_v(FAKE, 1, 1, 0, 128, 0, FAKE, None) == INVALID
@@ -234,12 +264,13 @@ def test_sparse_validation():
     a[12] = BIG
     assert L.sqattn_forward_sparse(*a) == UNSUPPORTED and "262144" in _err()
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 2, 300, 128, 0.1, 0, FAKE, None, FAKE, None]
-    a = list(base)
-    a[12] = None
-    assert L.sqattn_attend_quantized_sparse(*a) == INVALID and "block_mask" in _err()
-    a = list(base)
-    a[8] = 262144 + 64
-    assert L.sqattn_attend_quantized_sparse(*a) == UNSUPPORTED
+    for fn in (L.sqattn_attend_quantized_sparse, L.sqattn_attend_packed_sparse):
+        a = list(base)
+        a[12] = None
+        assert fn(*a) == INVALID and "block_mask" in _err()
+        a = list(base)
+        a[8] = 262144 + 64
+        assert fn(*a) == UNSUPPORTED
 
 
 def test_per_row_q_block_accepted():

@@ -144,6 +144,8 @@ def test_degenerate_inputs(kind, pv):
 
 
 def test_attend_quantized_matches_forward():
+    # sqattn_attend_quantized (raw V or E4M3 codes) and sqattn_attend_packed
+    # (V in the kernel's tile layout) give the forward's bytes
     w = W.get(2)
     q, k, v, rows = W.gen_inputs(w, N=1500, d=128, B=1, H=3)
     Q, K, V = dev_bf16(q), dev_bf16(k), dev_bf16(v)
@@ -152,11 +154,61 @@ def test_attend_quantized_matches_forward():
         qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, 128, 64)
         if pv == "fp8":
             vc, vs = sq.quantize_v_fp8(V)
-            out2 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(vc, pv), vs, scale=w.scale, pv=pv)
+            out2 = sq.attend_quantized(qi, qs, ki, ks, vc, vs, scale=w.scale, pv=pv)
+            out3 = sq.attend_packed(qi, qs, ki, ks, sq.pack_v(vc, pv), vs, scale=w.scale, pv=pv)
         else:
-            out2 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(V, pv), scale=w.scale, pv=pv)
+            out2 = sq.attend_quantized(qi, qs, ki, ks, V, scale=w.scale, pv=pv)
+            out3 = sq.attend_packed(qi, qs, ki, ks, sq.pack_v(V, pv), scale=w.scale, pv=pv)
         torch.cuda.synchronize()
-        assert torch.equal(out, out2), pv
+        assert torch.equal(out, out2) and torch.equal(out, out3), pv
+
+
+@pytest.mark.parametrize("pv", ["bf16", "fp8"])
+def test_plain_forward_entry_point(pv):
+    # sqattn_forward(q, k, v, B, H, N, d, scale, pv_dtype, out, ...) called through
+    # the C symbol itself (default blocks: q 128, k/v 64; fp32 out): every row of
+    # a ragged 300-token case against the oracle, and equal to sqattn_forward_ex
+    import ctypes
+    w = W.get(0)
+    q, k, v, rows = W.gen_inputs(w, N=300, d=64, B=1, H=2)
+    Q, K, V = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    B, H, N, d = q.shape
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    L = sq.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    code = {"bf16": sq.PV_BF16, "fp8": sq.PV_FP8}[pv]
+    rc = L.sqattn_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), B, H, N, d, ctypes.c_float(w.scale), code,
+                          out.data_ptr(), None, 0, st)
+    assert rc == 0, sq.lib().sqattn_last_error()
+    ex = torch.empty_like(out)
+    rc = L.sqattn_forward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), B, H, N, d, ctypes.c_float(w.scale), code,
+                             ex.data_ptr(), None, 0, st, None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, ex)
+    ref = oracle_heads(q, k, v, rows, 128, w.scale, pv)
+    got = host(out)
+    m = out_metrics([got[0, i][rows[i]] for i in range(H)], [ref[i]["out"] for i in range(H)],
+                    [ref[i]["envelope"] for i in range(H)] if pv == "fp8" else None)
+    assert m["max_abs"] <= MAX_ABS and m["cos"] >= MIN_COS, m
+
+
+def test_k_out_of_accumulator_range_gives_nan_mean():
+    # a head holding |K| >= 2^33 is outside the exact K-mean accumulator: its
+    # mean is NaN (a finite value elsewhere in the batch is unaffected)
+    w = W.get(0)
+    q, k, v, rows = W.gen_inputs(w, N=200, d=64, B=1, H=2)
+    k = k.copy()
+    k[0, 0, 17, 5] = W.f32_to_bf16_bits(np.array([2.0 ** 34], np.float32))[0]
+    Q, K = dev_bf16(q), dev_bf16(k)
+    qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, 64, 64)
+    torch.cuda.synchronize()
+    mu_h, ks_h, ki_h = host(mu), host(ks), host(ki)
+    assert np.isnan(mu_h[0, 0]).all()
+    ref = oracle_heads(q, k, v, rows, 64, w.scale, "bf16", heads=[1])[1]
+    assert np.array_equal(mu_h[0, 1].view(np.uint32), ref["k_mean"].view(np.uint32))
+    assert np.array_equal(ks_h[0, 1].view(np.uint32), ref["k_scale"].view(np.uint32))
+    assert np.array_equal(ki_h[0, 1], ref["k_codes"])
 
 
 def test_deterministic_and_caller_workspace():
@@ -201,11 +253,9 @@ def test_bf16_output(pv, d):
     qi, qs, ki, ks, mu = sq.quantize_qk(Q, K, w.q_block, 64)
     if pv == "fp8":
         vc, vs = sq.quantize_v_fp8(V)
-        a16 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(vc, pv), vs, scale=w.scale, pv=pv,
-                                  out=torch.empty_like(o16))
+        a16 = sq.attend_quantized(qi, qs, ki, ks, vc, vs, scale=w.scale, pv=pv, out=torch.empty_like(o16))
     else:
-        a16 = sq.attend_quantized(qi, qs, ki, ks, sq.pack_v(V, pv), scale=w.scale, pv=pv,
-                                  out_dtype=torch.bfloat16)
+        a16 = sq.attend_quantized(qi, qs, ki, ks, V, scale=w.scale, pv=pv, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert o16.dtype == torch.bfloat16 and a16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16))

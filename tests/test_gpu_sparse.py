@@ -101,12 +101,13 @@ def test_sparse_deterministic_and_kernel_entry():
         qi, qs, ki, ks, _ = sq.quantize_qk(Q, K)
         if pv == "fp8":
             vc, vs = sq.quantize_v_fp8(V)
-            vp = sq.pack_v(vc, "fp8")
+            vr, vp = vc, sq.pack_v(vc, "fp8")
         else:
-            vs, vp = None, sq.pack_v(V, "bf16")
-        c = sq.attend_quantized(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=pv, block_mask=M)
+            vs, vr, vp = None, V, sq.pack_v(V, "bf16")
+        c = sq.attend_packed(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=pv, block_mask=M)
+        e = sq.attend_quantized(qi, qs, ki, ks, vr, vs, scale=w.scale, pv=pv, block_mask=M)
         torch.cuda.synchronize()
-        assert torch.equal(a, b) and torch.equal(a, c), pv
+        assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, e), pv
 
 
 @pytest.mark.parametrize("name,density", [("wan14b-480p", 0.15), ("wan14b-480p-fp8", 0.15)])
