@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_v_fp8", "forward",
+__all__ = ["lib", "lib_path", "SqattnError", "quantize_qk", "quantize_qk_noalloc", "quantize_v_fp8", "forward",
            "attend_quantized", "attend_packed", "pack_v", "workspace_bytes", "packed_v_bytes",
            "quantize_qk_workspace_bytes", "PV_BF16", "PV_FP8", "version", "EXPORTS",
            "w8a8_quantize", "w8a8_gemm", "w8a8_linear", "w8a8_workspace_bytes", "w8a8_rmsnorm_quantize",
@@ -40,6 +40,7 @@ EXPORTS = {
     "sqattn_last_error": (_c.c_char_p, []),
     "sqattn_quantize_qk_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "sqattn_quantize_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sqattn_quantize_qk_noalloc": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "sqattn_quantize_v_fp8": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "sqattn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _vp]),
     "sqattn_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]),
@@ -181,6 +182,37 @@ def quantize_qk(q, k, q_block: int = 128, k_block: int = 64, workspace=None):
     w, wb = _ws(quantize_qk_workspace_bytes(B, H, N, d), dev, workspace)
     _check(lib().sqattn_quantize_qk(_ptr(q), _ptr(k), B, H, N, d, q_block, k_block, _ptr(qi), _ptr(qs),
                                     _ptr(ki), _ptr(ks), _ptr(mu), _ptr(w), wb, _stream(q)))
+    return qi, qs, ki, ks, mu
+
+
+def quantize_qk_noalloc(q, k, q_block: int = 128, k_block: int = 64, outs=None):
+    """quantize_qk through sqattn_quantize_qk_noalloc: the library allocates
+    nothing (the K-mean partial sums live in its static device scratch).
+    outs: the caller's (q_i8, q_scale, k_i8, k_scale, k_mean) tensors, or None
+    to have them allocated here by torch."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if tuple(k.shape) != (B, H, N, d):
+        raise ValueError("q and k shapes differ")
+    dev = q.device
+    if outs is None:
+        outs = (torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+                torch.empty((B, H, -(-N // q_block)), dtype=torch.float32, device=dev),
+                torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+                torch.empty((B, H, -(-N // k_block)), dtype=torch.float32, device=dev),
+                torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    qi, qs, ki, ks, mu = outs
+    for t, n, dt, shape in ((qi, "q_i8", torch.int8, (B, H, N, d)), (ki, "k_i8", torch.int8, (B, H, N, d)),
+                            (qs, "q_scale", torch.float32, (B, H, -(-N // q_block))),
+                            (ks, "k_scale", torch.float32, (B, H, -(-N // k_block))),
+                            (mu, "k_mean", torch.float32, (B, H, d))):
+        _dev(t, n, dt)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} must have shape {shape}")
+    _check(lib().sqattn_quantize_qk_noalloc(_ptr(q), _ptr(k), B, H, N, d, q_block, k_block, _ptr(qi), _ptr(qs),
+                                            _ptr(ki), _ptr(ks), _ptr(mu), _stream(q)))
     return qi, qs, ki, ks, mu
 
 

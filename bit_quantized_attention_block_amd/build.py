@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsqattn.so")
-SOURCES = ["api.cpp", "prep.hip", "attn_bf16.hip", "attn_fp8.hip", "w8a8.hip", "norm.hip"]
+SOURCES = ["api.cpp", "prep.hip", "attn_bf16.hip", "attn_fp8.hip", "w8a8.hip", "norm.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

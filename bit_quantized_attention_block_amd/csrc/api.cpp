@@ -249,27 +249,66 @@ size_t sqattn_quantize_qk_workspace_bytes(int B, int H, int N, int d) {
   return align_up((size_t)(z.BH * z.S * z.d) * 32);
 }
 
-int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int q_block, int k_block,
-                       int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+static int quantize_qk_check(const void* q, const void* k, int B, int H, int N, int d, int q_block, int k_block,
+                             const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                             const float* k_mean, Sizes* z) {
   g_err.clear();
   int s;
-  Sizes z;
   if ((s = check_ptr(q, "q", 16)) || (s = check_ptr(k, "k", 16)) || (s = check_ptr(q_i8, "q_i8", 16)) ||
       (s = check_ptr(k_i8, "k_i8", 16)) || (s = check_ptr(q_scale, "q_scale", 4)) ||
       (s = check_ptr(k_scale, "k_scale", 4)) || (s = check_ptr(k_mean, "k_mean", 4)))
     return s;
-  if ((s = check_shape(B, H, N, d, &z))) return s;
+  if ((s = check_shape(B, H, N, d, z))) return s;
   if ((s = check_q_block(q_block)) || (s = check_block(k_block, "k_block"))) return s;
-  hipStream_t st = (hipStream_t)stream;
-  Workspace ws;
-  const size_t need = align_up((size_t)(z.BH * z.S * z.d) * 32);
-  if ((s = ws.acquire(workspace, workspace_bytes, need, st))) return s;
+  return SQATTN_OK;
+}
+
+// The three passes on validated arguments; partial: the K-mean partial sums,
+// kmean_partial_bytes() of device memory (every entry is written before it is read).
+static size_t kmean_partial_bytes(const Sizes& z) { return align_up((size_t)(z.BH * z.S * z.d) * 32); }
+static void quantize_qk_launch(const void* q, const void* k, int H, int N, int d, int q_block, int k_block,
+                               int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                               uint64_t* partial, const Sizes& z, hipStream_t st) {
   const sqattn::Lay lc = sqattn::contiguous_lay(H, N, d);
   sqattn::launch_quant_i8((const uint16_t*)q, lc, (int)z.BH, N, d, q_block, nullptr, q_i8, q_scale, st);
-  sqattn::launch_kmean((const uint16_t*)k, lc, (int)z.BH, N, d, ws.at<uint64_t>(0), k_mean, st);
+  sqattn::launch_kmean((const uint16_t*)k, lc, (int)z.BH, N, d, partial, k_mean, st);
   sqattn::launch_quant_i8((const uint16_t*)k, lc, (int)z.BH, N, d, k_block, k_mean, k_i8, k_scale, st);
+}
+
+int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d, int q_block, int k_block,
+                       int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int s;
+  Sizes z;
+  if ((s = quantize_qk_check(q, k, B, H, N, d, q_block, k_block, q_i8, q_scale, k_i8, k_scale, k_mean, &z)))
+    return s;
+  hipStream_t st = (hipStream_t)stream;
+  Workspace ws;
+  if ((s = ws.acquire(workspace, workspace_bytes, kmean_partial_bytes(z), st))) return s;
+  quantize_qk_launch(q, k, H, N, d, q_block, k_block, q_i8, q_scale, k_i8, k_scale, k_mean, ws.at<uint64_t>(0), z,
+                     st);
   return hip_check("sqattn_quantize_qk launch");
+}
+
+int sqattn_quantize_qk_noalloc(const void* q, const void* k, int B, int H, int N, int d, int q_block, int k_block,
+                               int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                               void* stream) {
+  int s;
+  Sizes z;
+  if ((s = quantize_qk_check(q, k, B, H, N, d, q_block, k_block, q_i8, q_scale, k_i8, k_scale, k_mean, &z)))
+    return s;
+  const size_t need = kmean_partial_bytes(z);
+  if (need > sqattn::kStaticScratchBytes)
+    return fail(SQATTN_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
+                                          " bytes of scratch; the library's static scratch holds " +
+                                          std::to_string(sqattn::kStaticScratchBytes));
+  void* scratch = nullptr;
+  const hipError_t e = sqattn::static_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(SQATTN_ERR_HIP, std::string("device address of the static scratch: ") + hipGetErrorString(e));
+  quantize_qk_launch(q, k, H, N, d, q_block, k_block, q_i8, q_scale, k_i8, k_scale, k_mean, (uint64_t*)scratch, z,
+                     (hipStream_t)stream);
+  return hip_check("sqattn_quantize_qk_noalloc launch");
 }
 
 int sqattn_quantize_v_fp8(const void* v, int B, int H, int N, int d, int v_block, uint8_t* v_fp8,

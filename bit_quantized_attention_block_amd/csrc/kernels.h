@@ -29,6 +29,12 @@ struct RowNorm {
 };
 
 int kmean_chunks(int BH, int N);
+
+// The library's own device scratch for the allocation-free entry points
+// (static_scratch.hip): its size, and its device address on the current
+// device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st, const RowNorm& nm = RowNorm{});
 void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,

@@ -132,6 +132,24 @@ int sqattn_quantize_qk(const void* q, const void* k, int B, int H, int N, int d,
                        float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sqattn_quantize_qk for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same passes and results, with the K-mean partial sums in a scratch array
+ * the library holds in device memory (16 MiB per GPU it runs on, kept until
+ * the process ends) instead of a workspace.  Nothing is allocated.
+ * Returns SQATTN_ERR_WORKSPACE when the sizes need more scratch than that
+ * (sqattn_quantize_qk_workspace_bytes() > 16 MiB, i.e. roughly B*H*S*d > 2^19
+ * with S the K-mean chunks per head; every workload of up to 2048 heads at
+ * d = 128 fits).  Every entry of the scratch is written before it is read,
+ * so the previous call's contents do not matter; calls that overlap in time
+ * on one GPU (different streams, or host threads without ordering) share the
+ * array and race.
+ */
+int sqattn_quantize_qk_noalloc(const void* q, const void* k, int B, int H, int N, int d,
+                               int q_block, int k_block, int8_t* q_i8, float* q_scale,
+                               int8_t* k_i8, float* k_scale, float* k_mean, void* stream);
+
+/*
  * Quantize V to OCP E4M3 per block of v_block (= 64) rows.
  *   v       : bf16 [B,H,N,d];  v_fp8 : uint8 [B,H,N,d] codes;
  *   v_scale : float [B,H,ceil(N/v_block)].

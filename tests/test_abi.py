@@ -28,7 +28,7 @@ def declared():
 def test_library_loads_and_exports_every_declared_function():
     L = sq.lib()
     names = declared()
-    assert len(names) == 29
+    assert len(names) == 30
     assert set(names) == set(sq.EXPORTS), "binding and header disagree"
     for n in names:
         assert hasattr(L, n), n
