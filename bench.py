@@ -17,25 +17,37 @@ MI355X dense INT8 matrix peak (5.0 POPS).
 
 Printed: one JSON line with the contract fields plus
   roofline     - the attention kernel alone (its average launch duration from
-                 HIP events on the launch stream), against the INT8 MFMA peak;
-                 `traffic` comes from the rocprofv3 counter summary in
-                 profiles/ when it was taken on the current kernel source;
+                 HIP events on the launch stream), against the INT8 MFMA peak
+                 (`frac`) and against the mixed ceiling of its two products
+                 (`frac_mixed`: Q K^T on INT8 at 5.0 POPS, P V on bf16 at 2.5
+                 or on FP8 at 5.0 PFLOP/s); `traffic` comes from the rocprofv3
+                 counter summary in profiles/ when it was taken on the current
+                 kernel source and headers;
   cpu_baseline - the CPU oracle timed on a bounded sample of the same workload
-                 (ten heads), scaled to the whole workload.
+                 (ten heads), scaled to the whole workload;
+  numerics     - the error of the GPU output on that sample's rows against the
+                 oracle and against unquantized float64 attention;
+  fallback     - how many work items took the 16-bit path's exact-max second
+                 pass (opts.second_pass_count) in one forward;
+  system       - GPU, ROCm, hipcc, driver and torch versions and the shader and
+                 memory clocks sampled while the timed steps ran.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0         # dense FP8 MFMA
 METRIC = "quantized-attention TOPS (4·B·H·N²·d/s) + % of MI355X INT8 MFMA peak"
 W8A8_METRIC = "W8A8 linear INT8 TOPS (2·M·N·K/s) + % of MI355X INT8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic.json")
@@ -47,23 +59,139 @@ W8A8_SRC = os.path.join(CSRC, "w8a8.hip")
 W8A8_KERNEL = "w8a8_gemm_kernel"
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def _traffic(name, src):
     """Per-launch HBM bytes of the workload's profiled kernel from the
     committed counter summary, or None if absent or taken on another version
-    of the kernel source."""
+    of the kernel source or of a header it includes."""
+    from bit_quantized_attention_block_amd.rocprof_harness import source_key
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f).get(name)
     except (OSError, ValueError, AttributeError):
         return None
-    if not t or t.get("src_sha256") != _sha(src):
+    if not t or t.get("src_key") != source_key(src):
         return None
     return t.get("bytes_per_launch")
+
+
+def mixed_peak(pv):
+    """The MFMA ceiling of attention in ops/s units (TOPS): half the work
+    (Q K^T) on INT8 at 5.0 POPS, half (P V) on bf16 at 2.5 or FP8 at 5.0
+    PFLOP/s, so 4 / (2/5.0 + 2/peak_pv) POPS."""
+    pv_peak = BF16_PEAK_TFLOPS if pv == "bf16" else FP8_PEAK_TFLOPS
+    return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
+
+
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def _cmd(*args):
+    try:
+        r = subprocess.run(list(args), capture_output=True, text=True, timeout=20)
+        return r.stdout if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _card(torch):
+    """sysfs device directory of cuda:0 (matched by PCI bus id when several
+    cards are listed), or None."""
+    import glob
+    cards = sorted(c for c in glob.glob("/sys/class/drm/card[0-9]*/device") if os.path.exists(c + "/pp_dpm_sclk"))
+    if len(cards) == 1:
+        return cards[0]
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bus = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+    except Exception:
+        return None
+    for c in cards:
+        if bus in os.path.realpath(c):
+            return c
+    return None
+
+
+def _dpm_mhz(text):
+    """The current level (marked '*') of a pp_dpm_* listing, in MHz."""
+    for line in (text or "").splitlines():
+        if line.rstrip().endswith("*"):
+            v = line.split(":", 1)[-1].strip().rstrip("*").strip().lower()
+            try:
+                return float(v.replace("mhz", ""))
+            except ValueError:
+                return None
+    return None
+
+
+class ClockSampler:
+    """Samples the current shader and memory clock levels from sysfs every
+    interval seconds on a thread while the timed steps run."""
+
+    def __init__(self, card, interval=0.02):
+        self.card, self.interval = card, interval
+        self.sclk, self.mclk = [], []
+        self._stop = threading.Event()
+        self._t = None
+
+    def __enter__(self):
+        if self.card:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            s = _dpm_mhz(_read(self.card + "/pp_dpm_sclk"))
+            m = _dpm_mhz(_read(self.card + "/pp_dpm_mclk"))
+            if s:
+                self.sclk.append(s)
+            if m:
+                self.mclk.append(m)
+            self._stop.wait(self.interval)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t:
+            self._t.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.sclk:
+            return {"source": "sysfs pp_dpm_sclk / pp_dpm_mclk", "samples": 0,
+                    "note": "not readable on this machine" if self.card is None else "no samples"}
+        s = np.array(self.sclk)
+        return {"source": f"sysfs pp_dpm_sclk / pp_dpm_mclk current level every {self.interval * 1e3:.0f} ms "
+                          "during the timed forward steps",
+                "samples": int(s.size), "sclk_mhz_median": float(np.median(s)), "sclk_mhz_min": float(s.min()),
+                "sclk_mhz_max": float(s.max()),
+                "mclk_mhz_median": float(np.median(self.mclk)) if self.mclk else None}
+
+
+def system_info(torch):
+    """GPU name and architecture, ROCm / HIP runtime / hipcc / driver / torch
+    versions."""
+    info = {"torch": torch.__version__, "hip_runtime": torch.version.hip,
+            "rocm": _read("/opt/rocm/.info/version"),
+            "driver": _read("/sys/module/amdgpu/version")}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info["gpu"] = p.name
+        info["arch"] = getattr(p, "gcnArchName", None)
+        info["compute_units"] = p.multi_processor_count
+    except Exception:  # pragma: no cover
+        pass
+    hv = _cmd("/opt/rocm/bin/hipcc", "--version") or ""
+    info["hipcc"] = "; ".join(l.strip() for l in hv.splitlines() if "version" in l.lower())[:200] or None
+    if not info["driver"]:
+        dv = _cmd("/opt/rocm/bin/rocm-smi", "--showdriverversion") or ""
+        info["driver"] = next((l.split(":", 1)[-1].strip() for l in dv.splitlines() if "version" in l.lower()),
+                              None)
+    return info
 
 
 def _timed(torch, np, dev, stream, fn, n):
@@ -83,12 +211,21 @@ def _timed(torch, np, dev, stream, fn, n):
     return ev[0].elapsed_time(ev[n]) / n, float(np.median(per)), min(per), wall
 
 
-def _cores():
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
         return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         return 1
+
+
+def _cores():
+    """(CPU cores this process may run on, BLAS threads of numpy)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        n = os.cpu_count() or 1
+    return n, _blas_threads()
 
 
 def cpu_baseline_w8a8(w, x, wt, b, row_blocks=64, w_rows=8192):
@@ -108,7 +245,9 @@ def cpu_baseline_w8a8(w, x, wt, b, row_blocks=64, w_rows=8192):
     oracle.w8a8.linear(cx, sx, cw, sw, None if b is None else b[:wr])
     t2 = time.perf_counter()
     t_full = (t1 - t0) / rows * w.M + (t2 - t1) / (rows * wr) * (w.M * w.N)
-    return {"value": round(w.ops / t_full / 1e12, 6), "unit": "TOPS", "cores": int(_cores()), "kind": "oracle",
+    cores, blas = _cores()
+    return {"value": round(w.ops / t_full / 1e12, 6), "unit": "TOPS", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
             "sample": f"{rows} rows of x quantized ({t1 - t0:.1f} s) and multiplied with {wr} of the {w.N} rows "
                       f"of W ({t2 - t1:.1f} s); scaled to {w.M} x {w.N} outputs",
             "sample_seconds": round(t2 - t0, 2)}
@@ -155,7 +294,8 @@ def bench_w8a8(a):
 
     for _ in range(a.warmup):
         step()
-    ms, ms_med, ms_min, t_wall = _timed(torch, np, dev, stream, step, a.steps)
+    with ClockSampler(_card(torch)) as clocks:
+        ms, ms_med, ms_min, t_wall = _timed(torch, np, dev, stream, step, a.steps)
     print(f"[bench] linear {ms:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f}; wall "
           f"{t_wall / a.steps * 1e3:.3f}); torch {torch.__version__}, HIP {torch.version.hip}",
           file=sys.stderr, flush=True)
@@ -196,7 +336,8 @@ def bench_w8a8(a):
                                  "rmsnorm_quantize_x": round(n_ms, 4), "layernorm_quantize_x": round(l_ms, 4)},
                    "rmsnorm": bool(a.rmsnorm), "layernorm": bool(a.layernorm)},
         "roofline": {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "peak_mixed": INT8_PEAK_TOPS, "frac_mixed": round(k_tops / INT8_PEAK_TOPS, 4),
                      "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
                      "ops_per_launch": w.ops},
     }
@@ -205,6 +346,8 @@ def bench_w8a8(a):
         res["cpu_baseline"] = cpu_baseline_w8a8(w, x, wt, b)
     else:
         res["cpu_baseline"] = None
+    res["system"] = system_info(torch)
+    res["system"]["clocks"] = clocks.summary()
     print(json.dumps(res), flush=True)
     return 0
 
@@ -229,13 +372,15 @@ def sparse_ops(w, mask):
     return int(kept), int(processed)
 
 
-def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
+def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None, outs=None):
     """Time the oracle on `heads` heads (full quantization of each head plus
     its checked rows against all N keys) and scale to the whole workload
-    (with a block mask: the masked oracle, rated on the kept work `ops`)."""
+    (with a block mask: the masked oracle, rated on the kept work `ops`).
+    The oracle's output rows go into `outs` ({(b, h): (rows, O, E)}, E the
+    FP8 path's per-element ambiguity bound, else None)."""
     import numpy as np
     import oracle
-    cores = _cores()
+    cores, blas = _cores()
     t_quant = t_attn = 0.0
     nrows = 0
     for i in range(heads):
@@ -249,17 +394,22 @@ def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
         r = rows[i]
         bm = None if mask is None else mask[b, h]
         if w.pv == "fp8":
-            oracle.attention.attend_fp8(qc, qs, kc, ks, vc, vs, r, w.q_block, w.k_block, w.scale, block_mask=bm)
+            O, E, _ = oracle.attention.attend_fp8(qc, qs, kc, ks, vc, vs, r, w.q_block, w.k_block, w.scale,
+                                                  block_mask=bm)
         else:
-            oracle.attention.attend_bf16(qc, qs, kc, ks, v[b, h], r, w.q_block, w.k_block, w.scale, block_mask=bm)
+            O = oracle.attention.attend_bf16(qc, qs, kc, ks, v[b, h], r, w.q_block, w.k_block, w.scale,
+                                             block_mask=bm)
+            E = None
         t2 = time.perf_counter()
+        if outs is not None:
+            outs[(b, h)] = (r, O, E)
         t_quant += t1 - t0
         t_attn += t2 - t1
         nrows += len(r)
     BH = w.B * w.H
     t_full = t_quant / heads * BH + t_attn / nrows * (w.N * BH)
     return {"value": round((w.ops if ops is None else ops) / t_full / 1e12, 6), "unit": "TOPS",
-            "cores": int(cores), "kind": "oracle",
+            "cores": cores, "blas_threads": blas, "kind": "oracle",
             "sample": f"{heads} heads of {w.name}: full quantization ({t_quant:.1f} s) + {nrows} query rows "
                       f"against all {w.N} keys ({t_attn:.1f} s); scaled to {BH} heads x {w.N} rows"
                       + ("" if mask is None else " (block mask applied)"),
@@ -268,6 +418,45 @@ def cpu_baseline(w, q, k, v, rows, heads=10, mask=None, ops=None):
             # as scaled above) and of the attention alone on the sample
             "rows_per_s": round(w.N * BH / t_full, 3),
             "attention_rows_per_s": round(nrows / t_attn, 3)}
+
+
+def numerics(w, q, k, v, out, outs, mask=None):
+    """Error of the GPU output on the oracle's sampled rows: against the
+    oracle (the parity measure; for FP8 also beyond its per-element ambiguity
+    bound) and against unquantized float64 attention on the same bf16 inputs
+    (the method's own error)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+    worst = dict(oracle_max_abs=0.0, oracle_max_excess=0.0, fp64_max_abs=0.0, fp64_mean_abs=0.0)
+    cos_min, n, s_abs = 1.0, 0, 0.0
+    for (b, h), (r, O, E) in outs.items():
+        g = out[b, h][torch.as_tensor(r, device=out.device)].float().cpu().numpy().astype(np.float64)
+        e = np.abs(g - O)
+        worst["oracle_max_abs"] = max(worst["oracle_max_abs"], float(e.max()))
+        if E is not None:
+            worst["oracle_max_excess"] = max(worst["oracle_max_excess"], float(np.maximum(e - E, 0).max()))
+        if mask is not None:
+            continue
+        f = W.bf16_bits_to_f32
+        ref = oracle.attention.attention_fp64(f(q[b, h, r]).astype(np.float64), f(k[b, h]).astype(np.float64),
+                                              f(v[b, h]).astype(np.float64), w.scale)
+        d = np.abs(g - ref)
+        worst["fp64_max_abs"] = max(worst["fp64_max_abs"], float(d.max()))
+        s_abs += float(d.sum())
+        n += d.size
+        cos = (g * ref).sum(1) / np.maximum(np.linalg.norm(g, axis=1) * np.linalg.norm(ref, axis=1), 1e-300)
+        cos_min = min(cos_min, float(cos.min()))
+    res = {"rows": int(sum(len(r) for r, _, _ in outs.values())),
+           "vs_oracle_max_abs": worst["oracle_max_abs"]}
+    if w.pv == "fp8":
+        res["vs_oracle_max_abs_beyond_fp8_ambiguity"] = worst["oracle_max_excess"]
+    if mask is None:
+        res.update({"vs_fp64_unquantized_max_abs": worst["fp64_max_abs"],
+                    "vs_fp64_unquantized_mean_abs": s_abs / max(n, 1), "vs_fp64_unquantized_cos_min": cos_min})
+    return res
 
 
 def bench_dit_block(a):
@@ -322,7 +511,8 @@ def bench_dit_block(a):
 
     for _ in range(a.warmup):
         step()
-    ms, ms_med, ms_min, _ = _timed(torch, np, dev, stream, step, a.steps)
+    with ClockSampler(_card(torch)) as clocks:
+        ms, ms_med, ms_min, _ = _timed(torch, np, dev, stream, step, a.steps)
     t1, t2, t3 = (_timed(torch, np, dev, stream, f, a.steps)[0] for f in (s1, s2, s3))
     ops_qkv, ops_att, ops_out = 2 * B * N * 3 * C * C, w.ops, 2 * B * N * C * C
     ops = ops_qkv + ops_att + ops_out
@@ -339,6 +529,7 @@ def bench_dit_block(a):
                                  "layernorm_qkv_projection": round(t1, 4), "qknorm_attention": round(t2, 4),
                                  "out_projection": round(t3, 4)}},
         "roofline": None, "cpu_baseline": None,
+        "system": dict(system_info(torch), clocks=clocks.summary()),
     }
     print(json.dumps(res), flush=True)
     return 0
@@ -434,7 +625,8 @@ def main(argv=None):
 
     for _ in range(a.warmup):
         step()
-    ms, ms_med, ms_min, t_wall = timed(step, a.steps)
+    with ClockSampler(_card(torch)) as clocks:
+        ms, ms_med, ms_min, t_wall = timed(step, a.steps)
     print(f"[bench] forward {ms:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f}; wall "
           f"{t_wall / a.steps * 1e3:.3f}); torch {torch.__version__}, HIP {torch.version.hip}",
           file=sys.stderr, flush=True)
@@ -467,6 +659,19 @@ def main(argv=None):
 
     p_ms = timed(prep, reps)[0]
 
+    # fallback ratio: work items that took the exact-max second pass in one
+    # forward (the FP8 path rebases every tile and has no such pass)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M,
+               second_pass_count=cnt)
+    torch.cuda.synchronize(dev)
+    items = w.B * w.H * -(-w.N // 256)
+    fallback = {"second_pass_work_items": int(cnt.item()), "work_items": items,
+                "ratio": round(int(cnt.item()) / items, 6),
+                "what": "work items (one head's 256 query rows) whose row sum reached 2^64 in the one-pass "
+                        "softmax and were recomputed with the exact row max" if w.pv == "bf16" else
+                        "none by construction: the FP8 path rebases its running max every tile"}
+
     tops = ops / (ms * 1e-3) / 1e12
     k_tops = ops / (k_ms * 1e-3) / 1e12
     res = {
@@ -489,7 +694,9 @@ def main(argv=None):
                                  "attention_kernel": round(k_ms, 4), "attention_kernel_median": round(k_med, 4),
                                  "attention_kernel_min": round(k_min, 4), "quantize_and_pack": round(p_ms, 4)}},
         "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+                     "peak_mixed": round(mixed_peak(w.pv), 2),
+                     "frac_mixed": round(k_tops / mixed_peak(w.pv), 4),
                      "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
                      "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
     }
@@ -507,11 +714,23 @@ def main(argv=None):
             "processed_fraction": round(processed / w.ops, 4),
             "dense_equivalent_tops": round(w.ops / (ms * 1e-3) / 1e12, 3)}
         res["roofline"]["processed_ops_per_launch"] = processed
+    res["fallback"] = fallback
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows, mask=mask_h, ops=ops)
+        outs = {}
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows, mask=mask_h, ops=ops, outs=outs)
+        if a.qk_norm:
+            res["numerics"] = None  # the oracle sample is of the plain forward
+        else:
+            print("[bench] comparing the sampled rows", file=sys.stderr, flush=True)
+            step()
+            torch.cuda.synchronize(dev)
+            res["numerics"] = numerics(w, q, k, v, out, outs, mask=mask_h)
     else:
         res["cpu_baseline"] = None
+        res["numerics"] = None
+    res["system"] = system_info(torch)
+    res["system"]["clocks"] = clocks.summary()
     print(json.dumps(res), flush=True)
     return 0
 

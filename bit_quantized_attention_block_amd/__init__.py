@@ -74,7 +74,8 @@ EXPORTS = {
 
 
 class Opts(ctypes.Structure):
-    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("out_dtype", _i)]
+    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("out_dtype", _i),
+                ("second_pass_count", ctypes.c_void_p)]
 
 
 class SqattnError(RuntimeError):
@@ -230,8 +231,18 @@ def quantize_v_fp8(v, v_block: int = 64):
 OUT_FP32, OUT_BF16 = 0, 1
 
 
-def _opts(q_block, out_dtype=OUT_FP32):
-    return Opts(q_block=int(q_block), k_block=64, v_block=64, out_dtype=out_dtype)
+def _opts(q_block, out_dtype=OUT_FP32, second_pass_count=None):
+    """sqattn_opts; second_pass_count: None or a one-element int32 device
+    tensor the 16-bit P.V kernel increments per (head, 256-row block) that
+    took the exact-max second pass (the caller zeroes it)."""
+    c = None
+    if second_pass_count is not None:
+        torch = _torch()
+        _dev(second_pass_count, "second_pass_count", torch.int32)
+        if second_pass_count.numel() < 1:
+            raise ValueError("second_pass_count must hold one element")
+        c = second_pass_count.data_ptr()
+    return Opts(q_block=int(q_block), k_block=64, v_block=64, out_dtype=out_dtype, second_pass_count=c)
 
 
 def _out(out, shape, dev, out_dtype):
@@ -284,18 +295,19 @@ def _row_strides(t, name, dtype):
 
 
 def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
-            workspace=None, out_dtype=None, block_mask=None):
+            workspace=None, out_dtype=None, block_mask=None, second_pass_count=None):
     """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> out [B,H,N,d],
     fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16.  block_mask
     (uint8/bool [B,H,ceil(N/128),ceil(N/64)]): block-sparse attention over
     the kept (128-row query block, 64-key tile) pairs.  q, k, v and out may be
     strided views with contiguous rows (e.g. q = qkv[:, :, 0].transpose(1, 2)
     of a [B,N,3,H,d] projection output); they go through
-    sqattn_forward_strided."""
+    sqattn_forward_strided.  second_pass_count: see _opts."""
     torch = _torch()
     strided = any(isinstance(t, torch.Tensor) and not t.is_contiguous() for t in (q, k, v, out))
     if strided:
-        return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask)
+        return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask,
+                                second_pass_count=second_pass_count)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, torch.bfloat16)
     B, H, N, d = _shape(q)
@@ -305,13 +317,13 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
         scale = 1.0 / math.sqrt(d)
     out, od = _out(out, (B, H, N, d), q.device, out_dtype)
     w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
-    o = _opts(q_block, od)
+    o = _opts(q_block, od, second_pass_count)
     if block_mask is not None:
         m = _mask(block_mask, B, H, N)
         _check(lib().sqattn_forward_sparse(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(m),
                                            _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
         return out
-    if q_block == 128 and od == OUT_FP32:
+    if q_block == 128 and od == OUT_FP32 and second_pass_count is None:
         # the default options: the plain entry point (q_block 128, k/v blocks 64, fp32 out)
         _check(lib().sqattn_forward(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                     _ptr(w), wb, _stream(q)))
@@ -327,7 +339,8 @@ def forward_qknorm_workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) ->
 
 
 def forward_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps: float = 1e-6, scale: float | None = None, pv="bf16",
-                   q_block: int = 128, out=None, workspace=None, out_dtype=None, block_mask=None):
+                   q_block: int = 128, out=None, workspace=None, out_dtype=None, block_mask=None,
+                   second_pass_count=None):
     """Attention with the per-token RMSNorm of q and k (over each token's H*d
     features, weights gamma_q / gamma_k fp32 [H*d] or None) fused into their
     quantization; sqattn_forward_qknorm.  q, k, v: bf16 [B,H,N,d] views whose
@@ -340,10 +353,11 @@ def forward_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps: float = 1e-6, scale
             if g.numel() != q.shape[1] * q.shape[3]:
                 raise ValueError(f"{n} has {g.numel()} elements, expected H*d = {q.shape[1] * q.shape[3]}")
     return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask,
-                            qkn=(gamma_q, gamma_k, float(eps)))
+                            qkn=(gamma_q, gamma_k, float(eps)), second_pass_count=second_pass_count)
 
 
-def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask, qkn=None):
+def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask, qkn=None,
+                     second_pass_count=None):
     torch = _torch()
     st = []
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -361,7 +375,7 @@ def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, blo
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, d)}")
     ost = _row_strides(out, "out", out_dtype)
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32
-    o = _opts(q_block, od)
+    o = _opts(q_block, od, second_pass_count)
     m = _mask(block_mask, B, H, N) if block_mask is not None else None
     ins = (ctypes.c_int64 * 9)(*st)
     outs = (ctypes.c_int64 * 3)(*ost)
@@ -393,7 +407,8 @@ def pack_v(v, pv="bf16"):
     return packed
 
 
-def _attend(packed, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block, out, out_dtype, block_mask):
+def _attend(packed, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block, out, out_dtype, block_mask,
+            second_pass_count=None):
     torch = _torch()
     _dev(q_i8, "q_i8", torch.int8)
     _dev(k_i8, "k_i8", torch.int8)
@@ -413,7 +428,7 @@ def _attend(packed, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, od = _out(out, (B, H, N, d), q_i8.device, out_dtype)
-    o = _opts(q_block, od)
+    o = _opts(q_block, od, second_pass_count)
     L = lib()
     args = (_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v), _ptr(v_scale), B, H, N, d,
             float(scale), _PV[pv])
@@ -428,20 +443,22 @@ def _attend(packed, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block
 
 
 def attend_quantized(q_i8, q_scale, k_i8, k_scale, v, v_scale=None, scale: float | None = None,
-                     pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
+                     pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None,
+                     second_pass_count=None):
     """Attention on quantized Q/K (from quantize_qk) and V: bf16 [B,H,N,d] for
     pv="bf16", E4M3 codes (from quantize_v_fp8) with their scales for
     pv="fp8"; block_mask as in forward."""
     return _attend(False, q_i8, q_scale, k_i8, k_scale, v, v_scale, scale, pv, q_block, out, out_dtype,
-                   block_mask)
+                   block_mask, second_pass_count)
 
 
 def attend_packed(q_i8, q_scale, k_i8, k_scale, v_packed, v_scale=None, scale: float | None = None,
-                  pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None):
+                  pv="bf16", q_block: int = 128, out=None, out_dtype=None, block_mask=None,
+                  second_pass_count=None):
     """The attention kernel alone, on quantized Q/K and V already in the
     kernel's tile layout (see pack_v)."""
     return _attend(True, q_i8, q_scale, k_i8, k_scale, v_packed, v_scale, scale, pv, q_block, out, out_dtype,
-                   block_mask)
+                   block_mask, second_pass_count)
 
 
 # --------------------------------------------------------------------------- W8A8 linear

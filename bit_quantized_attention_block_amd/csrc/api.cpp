@@ -9,7 +9,6 @@
 #include <cstdio>
 #include <string>
 
-#include "common.h"
 #include "kernels.h"
 
 namespace {
@@ -69,6 +68,7 @@ int check_ptr(const void* p, const char* name, size_t align) {
 
 struct Opts {
   int q_block, k_block, v_block, out_bf16;
+  uint32_t* second_pass;
 };
 
 int resolve_opts(const sqattn_opts* o, Opts* r) {
@@ -76,6 +76,7 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   r->k_block = 64;
   r->v_block = 64;
   r->out_bf16 = 0;
+  r->second_pass = nullptr;
   if (!o) return SQATTN_OK;
   if (o->out_dtype != SQATTN_OUT_FP32 && o->out_dtype != SQATTN_OUT_BF16)
     return fail(SQATTN_ERR_INVALID_ARG, "opts.out_dtype must be SQATTN_OUT_FP32 or SQATTN_OUT_BF16");
@@ -83,6 +84,9 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   if (o->q_block) r->q_block = o->q_block;
   if (o->k_block) r->k_block = o->k_block;
   if (o->v_block) r->v_block = o->v_block;
+  if (o->second_pass_count && !aligned(o->second_pass_count, 4))
+    return fail(SQATTN_ERR_INVALID_ARG, "opts.second_pass_count is not 4-byte aligned");
+  r->second_pass = o->second_pass_count;
   int s;
   if ((s = check_q_block(r->q_block))) return s;
   if (r->k_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "k_block must be 64 (the attention tile)");
@@ -415,6 +419,7 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   p.sv = vs;
   p.out = out;
   p.out_bf16 = o.out_bf16;
+  p.second_pass = o.second_pass;
   p.N = N;
   p.nq = (int)z.nq;
   p.q_block = o.q_block;
@@ -543,6 +548,7 @@ static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k
   p.sv = v_scale;
   p.out = out;
   p.out_bf16 = o.out_bf16;
+  p.second_pass = o.second_pass;
   p.N = N;
   p.nq = (int)((N + o.q_block - 1) / o.q_block);
   p.q_block = o.q_block;

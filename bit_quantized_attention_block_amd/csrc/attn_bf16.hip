@@ -475,6 +475,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     if (pass == 1) {
       // Rare path: some row's sum reached 2^HEADROOM.  Take the exact row max
       // over all keys as the reference, so that every P <= 1.
+      if (p.second_pass && threadIdx.x == 0) atomicAdd(p.second_pass, 1u);
       C.m = C.exact_max(npos);
       if constexpr (SP) C.has_m = true;
     }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace sqattn {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -37,19 +39,6 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 //     needed; V^T (rows = channels) is the A operand read from LDS, where
 //     each lane-half's 8 (bf16) or 32 (FP8) keys are contiguous.  Row max and
 //     row sum therefore need only one exchange between lanes l and l^32.
-
-// Attention tile: 64 keys.  K blocks must coincide with these tiles.
-constexpr int KT = 64;
-// Attention work-group: 8 waves, 32 query rows each.
-constexpr int ATT_WAVES = 8;
-constexpr int ATT_QW = 32;
-constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
-// Block-sparse attention: one mask row per 128 query rows (waves 0-3 of a
-// work-group read mask row 2 qt, waves 4-7 row 2 qt + 1); at most SP_MAXT key
-// tiles per head (the work-group's list of tiles lives in LDS).
-constexpr int SP_MQ = 128;
-constexpr int SP_MAXT = 4096;
-constexpr int SP_LIST_BYTES = 4 * SP_MAXT + 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

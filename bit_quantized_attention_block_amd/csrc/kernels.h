@@ -1,10 +1,25 @@
-// Host-side launchers of the sqattn kernels (all enqueue on the given stream).
+// Host-side launchers of the sqattn kernels (all enqueue on the given stream)
+// and the kernel geometry host code sizes buffers by.  Plain C++ besides the
+// HIP runtime types: api.cpp includes only this header of the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace sqattn {
+
+// Attention tile: 64 keys.  K blocks must coincide with these tiles.
+constexpr int KT = 64;
+// Attention work-group: 8 waves, 32 query rows each.
+constexpr int ATT_WAVES = 8;
+constexpr int ATT_QW = 32;
+constexpr int ATT_QWG = ATT_WAVES * ATT_QW;
+// Block-sparse attention: one mask row per 128 query rows (waves 0-3 of a
+// work-group read mask row 2 qt, waves 4-7 row 2 qt + 1); at most SP_MAXT key
+// tiles per head (the work-group's list of tiles lives in LDS).
+constexpr int SP_MQ = 128;
+constexpr int SP_MAXT = 4096;
+constexpr int SP_LIST_BYTES = 4 * SP_MAXT + 64;
 
 // Element strides of a [B, H, N, d] operand with d contiguous: row r of head
 // (b, h) starts at b*sb + h*sh + r*sn.  Contiguous: {H*N*d, N*d, d, H}.
@@ -28,7 +43,19 @@ struct RowNorm {
   const float* gamma = nullptr;
 };
 
-int kmean_chunks(int BH, int N);
+// Chunks per head of the K-mean pass: enough work-groups to cover the chip a
+// few times, each at least 256 rows and at most 2^18 (the binary64 windows
+// are flushed every KMEAN_F64_ADDS rows of a thread, whatever the chunk
+// length).
+inline int kmean_chunks(int BH, int N) {
+  int s = (2048 + BH - 1) / BH;
+  int maxs = (N + 255) / 256;
+  if (s > maxs) s = maxs;
+  int mins = (N + (1 << 18) - 1) >> 18;
+  if (s < mins) s = mins;
+  if (s < 1) s = 1;
+  return s;
+}
 
 // The library's own device scratch for the allocation-free entry points
 // (static_scratch.hip): its size, and its device address on the current
@@ -58,6 +85,7 @@ struct AttnParams {
   Lay lo;               // element strides of the output rows
   int N, nq, q_block, nt, BH, qtiles, per_xcd;
   float scale_log2e;
+  uint32_t* second_pass;  // null, or a counter of work items that took the exact-max second pass
 };
 
 // 16-bit P.V kernel; p.qtiles and p.per_xcd must be set.  Returns the status

@@ -527,19 +527,6 @@ __global__ __launch_bounds__(256) void v_tiles_fp8_kernel(const uint8_t* __restr
       hipLaunchKernelGGL((KERNEL<64, false>), GRID, BLOCK, 0, STREAM, __VA_ARGS__); \
   } while (0)
 
-int kmean_chunks(int BH, int N) {
-  // enough work-groups to cover the chip a few times, each at least 256 rows
-  // and at most 2^18 (the binary64 windows are flushed every
-  // KMEAN_F64_ADDS rows of a thread, whatever the chunk length)
-  int s = (2048 + BH - 1) / BH;
-  int maxs = (N + 255) / 256;
-  if (s > maxs) s = maxs;
-  int mins = (N + (1 << 18) - 1) >> 18;
-  if (s < mins) s = mins;
-  if (s < 1) s = 1;
-  return s;
-}
-
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st, const RowNorm& nm) {
   int S = kmean_chunks(BH, N);

@@ -28,9 +28,9 @@ only counters that fit one run).
   profiles/<kernel>_<workload>_profile.md  kernel durations (rocprofv3 --stats),
                                            HBM bytes and MFMA busy per launch
   profiles/kernel_traffic.json             per-launch HBM bytes of the profiled
-                                           kernel, keyed by workload, with the
-                                           sha256 of the kernel source it was
-                                           measured on.
+                                           kernel, keyed by workload, with a
+                                           sha256 over the kernel source and
+                                           the headers it includes, as measured.
 
 HBM bytes come from the TCC counters FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch), each scaled by the factor that maps the same counter to the known
@@ -209,9 +209,33 @@ def _shown(name: str) -> str:
     return n[:n.index(">") + 1] if "<" in n.split("(")[0] else n.split("(")[0]
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _includes(path):
+    """The sources a kernel file compiles: the file and, recursively, the
+    headers it includes by a quoted name from its own directory, sorted."""
+    seen, todo = set(), [os.path.abspath(path)]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        with open(f) as fh:
+            for line in fh:
+                t = line.strip()
+                if t.startswith("#include \""):
+                    todo.append(os.path.join(os.path.dirname(f), t.split('"')[1]))
+    return sorted(seen)
+
+
+def source_key(path):
+    """sha256 over the kernel file and every header it includes (name and
+    bytes of each, in sorted order): a counter summary is only valid for the
+    code it was taken on."""
+    h = hashlib.sha256()
+    for f in _includes(path):
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def summarize(workload: str, outdir: str, profiles: str) -> int:
@@ -306,7 +330,9 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
             allt = json.load(f)
     except (OSError, ValueError):
         allt = {}
-    allt[w.name] = {"kernel": kname, "src_sha256": _sha(sp["src"]), "bytes_per_launch": round(traffic),
+    allt[w.name] = {"kernel": kname, "src_key": source_key(sp["src"]),
+                    "src_files": [os.path.basename(f) for f in _includes(sp["src"])],
+                    "bytes_per_launch": round(traffic),
                     "read_bytes": round(read_b), "write_bytes": round(write_b),
                     "fetch_kib": f_attn, "write_kib": w_attn, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
                     "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns}

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SQATTN_VERSION 10000 /* 1.0.0 */
+#define SQATTN_VERSION 10100 /* 1.1.0 */
 
 typedef enum {
   SQATTN_OK = 0,
@@ -86,12 +86,20 @@ typedef enum { SQATTN_OUT_FP32 = 0, SQATTN_OUT_BF16 = 1 } sqattn_out_dtype;
  * granularity of the kernel's Q operand, where each lane holds one row; it
  * costs the attention kernel nothing and helps heavy-tailed Q most).  k_block: 64 (the attention tile;
  * default).  v_block: 64 (FP8 only; default).  out_dtype: SQATTN_OUT_FP32
- * (default) or SQATTN_OUT_BF16, the fp32 result rounded to nearest even. */
+ * (default) or SQATTN_OUT_BF16, the fp32 result rounded to nearest even.
+ * second_pass_count: NULL (default), or a device pointer to one uint32 that
+ * the attention kernel increments (atomically, on the call's stream) once for
+ * every work item -- one head's 256 query rows -- that took the rare exact-max
+ * second pass of the 16-bit P.V path (a row sum of the one-pass schedule
+ * reached its headroom); the caller zeroes it and reads it after the stream
+ * has run.  The FP8 path rebases every tile and never takes that pass.
+ * Divided by B * H * ceil(N / 256) it is the fallback ratio of the call. */
 typedef struct sqattn_opts {
   int q_block;
   int k_block;
   int v_block;
   int out_dtype;
+  uint32_t* second_pass_count;
 } sqattn_opts;
 
 /* SQATTN_VERSION of the loaded library. */

@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_function():
     syms = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
         assert n in syms, f"{n} is not an exported C symbol"
-    assert sq.version() == 10000
+    assert sq.version() == 10100
 
 
 def test_status_strings():
@@ -80,6 +80,7 @@ def _err():
     (dict(opts=sq.Opts(24, 64, 64, 0)), INVALID, "q_block"),
     (dict(opts=sq.Opts(128, 64, 64, 2)), INVALID, "out_dtype"),
     (dict(opts=sq.Opts(128, 64, 64, -1)), INVALID, "out_dtype"),
+    (dict(opts=sq.Opts(128, 64, 64, 0, FAKE + 2)), INVALID, "second_pass_count"),
 ])
 def test_forward_validation(kw, code, needle):
     assert _fwd(**kw) == code

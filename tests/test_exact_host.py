@@ -61,18 +61,28 @@ int main(int argc, char** argv) {
 """
 
 
-@pytest.fixture(scope="module")
-def driver(tmp_path_factory):
+# the driver is built twice: optimised, and for the host sanitizers
+# (AddressSanitizer + UndefinedBehaviorSanitizer, any report fatal), so that
+# every case below also runs the helpers under both
+SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+SAN_ENV = dict(os.environ, ASAN_OPTIONS="verify_asan_link_order=0:detect_leaks=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+
+
+@pytest.fixture(scope="module", params=["O2", "sanitize"])
+def driver(request, tmp_path_factory):
     d = tmp_path_factory.mktemp("exact")
     src = d / "drv.cpp"
     src.write_text(DRIVER)
     exe = d / "drv"
-    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    flags = ["-O2"] if request.param == "O2" else SANITIZE
+    subprocess.run(["g++", *flags, "-std=c++17", "-I", CSRC, str(src), "-o", str(exe)], check=True)
     return str(exe)
 
 
 def _run(exe, text):
-    r = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
+    r = subprocess.run([exe], input=text, capture_output=True, text=True, env=SAN_ENV)
+    assert r.returncode == 0 and "runtime error" not in r.stderr, r.stderr[-2000:]
     return r.stdout.split()
 
 

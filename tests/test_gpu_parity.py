@@ -143,6 +143,34 @@ def test_degenerate_inputs(kind, pv):
               bound_hits=False)
 
 
+def test_second_pass_counter():
+    # opts.second_pass_count counts the work items (head, 256-row block) that
+    # took the exact-max second pass.  far_max: every row's score at key 100
+    # exceeds its first 32 keys' by about 290 in log2 units, so every one of
+    # the 2 heads x 2 blocks does; workload-shaped data never does.  The
+    # counter leaves the output unchanged and accumulates over calls.
+    q, k, v, _ = _degenerate("far_max")
+    Q, K, V = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ref = sq.forward(Q, K, V, pv="bf16")
+    out = sq.forward(Q, K, V, pv="bf16", second_pass_count=cnt)
+    out = sq.forward(Q, K, V, pv="bf16", second_pass_count=cnt, out=out)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 2 * 4 and torch.equal(out, ref)
+    qi, qs, ki, ks, _ = sq.quantize_qk(Q, K, 128, 64)
+    cnt.zero_()
+    sq.attend_quantized(qi, qs, ki, ks, V, pv="bf16", second_pass_count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 4
+    w = W.get(2)
+    q, k, v, _ = W.gen_inputs(w, N=1500, d=128, B=1, H=3)
+    cnt.zero_()
+    for pv in ("bf16", "fp8"):
+        sq.forward(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=w.scale, pv=pv, second_pass_count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0
+
+
 def test_attend_quantized_matches_forward():
     # sqattn_attend_quantized (raw V or E4M3 codes) and sqattn_attend_packed
     # (V in the kernel's tile layout) give the forward's bytes
