@@ -189,8 +189,8 @@ def system_info(torch):
     info["hipcc"] = "; ".join(l.strip() for l in hv.splitlines() if "version" in l.lower())[:200] or None
     if not info["driver"]:
         dv = _cmd("/opt/rocm/bin/rocm-smi", "--showdriverversion") or ""
-        info["driver"] = next((l.split(":", 1)[-1].strip() for l in dv.splitlines() if "version" in l.lower()),
-                              None)
+        info["driver"] = next((l.split(":", 1)[-1].strip() for l in dv.splitlines()
+                               if "driver version" in l.lower() and ":" in l), None)
     return info
 
 
@@ -555,6 +555,8 @@ def main(argv=None):
     ap.add_argument("--qk-norm", action="store_true",
                     help="attention workloads: Q, K, V as views of a fused [B, N, 3, H, d] projection output and "
                          "the step is attention with the per-token q/k RMSNorm fused into the quantization")
+    ap.add_argument("--smooth-q", action="store_true",
+                    help="attention workloads: Q smoothing per Q block (opts.smooth_q) in the timed forward")
     ap.add_argument("--block-density", type=float, default=None,
                     help="block-sparse attention: fraction of the non-local blocks kept")
     a = ap.parse_args(argv)
@@ -591,11 +593,13 @@ def main(argv=None):
     if mask_h is not None:
         M = torch.from_numpy(mask_h).to(dev)
     out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(sq.workspace_bytes(w.B, w.H, w.N, w.d, w.pv, w.q_block), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sq.workspace_bytes(w.B, w.H, w.N, w.d, w.pv, w.q_block, a.smooth_q), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M)
+        sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M,
+                   smooth_q=a.smooth_q)
 
     plain_ms = None
     if a.qk_norm:
@@ -663,14 +667,15 @@ def main(argv=None):
     # forward (the FP8 path rebases every tile and has no such pass)
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     sq.forward(Q, K, V, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out, workspace=ws, block_mask=M,
-               second_pass_count=cnt)
+               second_pass_count=cnt, smooth_q=a.smooth_q)
     torch.cuda.synchronize(dev)
     items = w.B * w.H * -(-w.N // 256)
     fallback = {"second_pass_work_items": int(cnt.item()), "work_items": items,
                 "ratio": round(int(cnt.item()) / items, 6),
                 "what": "work items (one head's 256 query rows) whose row sum reached 2^64 in the one-pass "
                         "softmax and were recomputed with the exact row max" if w.pv == "bf16" else
-                        "none by construction: the FP8 path rebases its running max every tile"}
+                        "none by construction: the FP8 path keeps P, O and the row sum relative to the exact "
+                        "running max of every tile"}
 
     tops = ops / (ms * 1e-3) / 1e12
     k_tops = ops / (k_ms * 1e-3) / 1e12
@@ -700,6 +705,10 @@ def main(argv=None):
                      "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
                      "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
     }
+    if a.smooth_q:
+        res["config"]["smooth_q"] = {
+            "step": "Q smoothing per Q block: exact block mean removed before INT8 quantization, returned as a "
+                    "logit bias (mean . K', binary32 per block and key) added to the scores"}
     if a.qk_norm:
         res["config"]["qk_norm"] = {
             "layout": "q, k, v as views of a fused [B, N, 3, H, d] projection output",
@@ -719,7 +728,7 @@ def main(argv=None):
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         outs = {}
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, rows, mask=mask_h, ops=ops, outs=outs)
-        if a.qk_norm:
+        if a.qk_norm or a.smooth_q:
             res["numerics"] = None  # the oracle sample is of the plain forward
         else:
             print("[bench] comparing the sampled rows", file=sys.stderr, flush=True)

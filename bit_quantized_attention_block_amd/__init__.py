@@ -74,7 +74,7 @@ EXPORTS = {
 
 
 class Opts(ctypes.Structure):
-    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("out_dtype", _i),
+    _fields_ = [("q_block", _i), ("k_block", _i), ("v_block", _i), ("out_dtype", _i), ("smooth_q", _i),
                 ("second_pass_count", ctypes.c_void_p)]
 
 
@@ -231,10 +231,11 @@ def quantize_v_fp8(v, v_block: int = 64):
 OUT_FP32, OUT_BF16 = 0, 1
 
 
-def _opts(q_block, out_dtype=OUT_FP32, second_pass_count=None):
+def _opts(q_block, out_dtype=OUT_FP32, second_pass_count=None, smooth_q=False):
     """sqattn_opts; second_pass_count: None or a one-element int32 device
     tensor the 16-bit P.V kernel increments per (head, 256-row block) that
-    took the exact-max second pass (the caller zeroes it)."""
+    took the exact-max second pass (the caller zeroes it); smooth_q: Q
+    smoothing per Q block (forward only)."""
     c = None
     if second_pass_count is not None:
         torch = _torch()
@@ -242,7 +243,8 @@ def _opts(q_block, out_dtype=OUT_FP32, second_pass_count=None):
         if second_pass_count.numel() < 1:
             raise ValueError("second_pass_count must hold one element")
         c = second_pass_count.data_ptr()
-    return Opts(q_block=int(q_block), k_block=64, v_block=64, out_dtype=out_dtype, second_pass_count=c)
+    return Opts(q_block=int(q_block), k_block=64, v_block=64, out_dtype=out_dtype, smooth_q=int(bool(smooth_q)),
+                second_pass_count=c)
 
 
 def _out(out, shape, dev, out_dtype):
@@ -262,8 +264,8 @@ def _out(out, shape, dev, out_dtype):
     return out, (OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32)
 
 
-def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128) -> int:
-    o = _opts(q_block)
+def workspace_bytes(B, H, N, d, pv="bf16", q_block: int = 128, smooth_q: bool = False) -> int:
+    o = _opts(q_block, smooth_q=smooth_q)
     return int(lib().sqattn_workspace_bytes(B, H, N, d, _PV[pv], ctypes.byref(o)))
 
 
@@ -295,19 +297,20 @@ def _row_strides(t, name, dtype):
 
 
 def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, out=None,
-            workspace=None, out_dtype=None, block_mask=None, second_pass_count=None):
+            workspace=None, out_dtype=None, block_mask=None, second_pass_count=None, smooth_q: bool = False):
     """Quantized attention forward: bf16 q, k, v [B,H,N,d] -> out [B,H,N,d],
     fp32 or (out_dtype=torch.bfloat16, or a bf16 `out`) bf16.  block_mask
     (uint8/bool [B,H,ceil(N/128),ceil(N/64)]): block-sparse attention over
     the kept (128-row query block, 64-key tile) pairs.  q, k, v and out may be
     strided views with contiguous rows (e.g. q = qkv[:, :, 0].transpose(1, 2)
     of a [B,N,3,H,d] projection output); they go through
-    sqattn_forward_strided.  second_pass_count: see _opts."""
+    sqattn_forward_strided.  second_pass_count, smooth_q (Q smoothing per Q
+    block, q_block 64, 128 or 256, dense): see _opts."""
     torch = _torch()
     strided = any(isinstance(t, torch.Tensor) and not t.is_contiguous() for t in (q, k, v, out))
     if strided:
         return _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask,
-                                second_pass_count=second_pass_count)
+                                second_pass_count=second_pass_count, smooth_q=smooth_q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, torch.bfloat16)
     B, H, N, d = _shape(q)
@@ -316,14 +319,14 @@ def forward(q, k, v, scale: float | None = None, pv="bf16", q_block: int = 128, 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, od = _out(out, (B, H, N, d), q.device, out_dtype)
-    w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
-    o = _opts(q_block, od, second_pass_count)
+    w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block, smooth_q), q.device, workspace)
+    o = _opts(q_block, od, second_pass_count, smooth_q)
     if block_mask is not None:
         m = _mask(block_mask, B, H, N)
         _check(lib().sqattn_forward_sparse(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(m),
                                            _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
         return out
-    if q_block == 128 and od == OUT_FP32 and second_pass_count is None:
+    if q_block == 128 and od == OUT_FP32 and second_pass_count is None and not smooth_q:
         # the default options: the plain entry point (q_block 128, k/v blocks 64, fp32 out)
         _check(lib().sqattn_forward(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), _PV[pv], _ptr(out),
                                     _ptr(w), wb, _stream(q)))
@@ -357,7 +360,7 @@ def forward_qknorm(q, k, v, gamma_q=None, gamma_k=None, eps: float = 1e-6, scale
 
 
 def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, block_mask, qkn=None,
-                     second_pass_count=None):
+                     second_pass_count=None, smooth_q=False):
     torch = _torch()
     st = []
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -375,12 +378,12 @@ def _forward_strided(q, k, v, scale, pv, q_block, out, workspace, out_dtype, blo
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, d)}")
     ost = _row_strides(out, "out", out_dtype)
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_FP32
-    o = _opts(q_block, od, second_pass_count)
+    o = _opts(q_block, od, second_pass_count, smooth_q)
     m = _mask(block_mask, B, H, N) if block_mask is not None else None
     ins = (ctypes.c_int64 * 9)(*st)
     outs = (ctypes.c_int64 * 3)(*ost)
     if qkn is None:
-        w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block), q.device, workspace)
+        w, wb = _ws(workspace_bytes(B, H, N, d, pv, q_block, smooth_q), q.device, workspace)
         _check(lib().sqattn_forward_strided(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, ins, outs, float(scale),
                                             _PV[pv], _ptr(m), _ptr(out), _ptr(w), wb, _stream(q), ctypes.byref(o)))
     else:

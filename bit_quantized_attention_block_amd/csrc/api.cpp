@@ -67,7 +67,7 @@ int check_ptr(const void* p, const char* name, size_t align) {
 }
 
 struct Opts {
-  int q_block, k_block, v_block, out_bf16;
+  int q_block, k_block, v_block, out_bf16, smooth_q;
   uint32_t* second_pass;
 };
 
@@ -76,6 +76,7 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   r->k_block = 64;
   r->v_block = 64;
   r->out_bf16 = 0;
+  r->smooth_q = 0;
   r->second_pass = nullptr;
   if (!o) return SQATTN_OK;
   if (o->out_dtype != SQATTN_OUT_FP32 && o->out_dtype != SQATTN_OUT_BF16)
@@ -84,6 +85,8 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   if (o->q_block) r->q_block = o->q_block;
   if (o->k_block) r->k_block = o->k_block;
   if (o->v_block) r->v_block = o->v_block;
+  if (o->smooth_q != 0 && o->smooth_q != 1) return fail(SQATTN_ERR_INVALID_ARG, "opts.smooth_q must be 0 or 1");
+  r->smooth_q = o->smooth_q;
   if (o->second_pass_count && !aligned(o->second_pass_count, 4))
     return fail(SQATTN_ERR_INVALID_ARG, "opts.second_pass_count is not 4-byte aligned");
   r->second_pass = o->second_pass_count;
@@ -91,6 +94,8 @@ int resolve_opts(const sqattn_opts* o, Opts* r) {
   if ((s = check_q_block(r->q_block))) return s;
   if (r->k_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "k_block must be 64 (the attention tile)");
   if (r->v_block != sqattn::KT) return fail(SQATTN_ERR_UNSUPPORTED, "v_block must be 64");
+  if (r->smooth_q && r->q_block != 64 && r->q_block != 128 && r->q_block != 256)
+    return fail(SQATTN_ERR_UNSUPPORTED, "Q smoothing needs q_block 64, 128 or 256");
   return SQATTN_OK;
 }
 
@@ -105,10 +110,12 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t q_i8, k_i8, q_scale, k_scale, k_mean, partial, vt, v_scale, total;
+  size_t q_i8, k_i8, q_scale, k_scale, k_mean, partial, vt, v_scale, q_mean, q_bias, total;
 };
 
-FwdLayout forward_layout(const Sizes& z, int pv, int q_block) {
+// smooth: Q smoothing (the block means and the bias; the partial sums serve
+// the Q means first, then the K mean)
+FwdLayout forward_layout(const Sizes& z, int pv, int q_block, bool smooth = false) {
   FwdLayout L;
   Carve c;
   const long long nq = (z.N + q_block - 1) / q_block;
@@ -117,9 +124,11 @@ FwdLayout forward_layout(const Sizes& z, int pv, int q_block) {
   L.q_scale = c.take((size_t)(z.BH * nq) * 4);
   L.k_scale = c.take((size_t)(z.BH * z.nt) * 4);
   L.k_mean = c.take((size_t)(z.BH * z.d) * 4);
-  L.partial = c.take((size_t)(z.BH * z.S * z.d) * 32);
+  L.partial = c.take((size_t)(z.BH * (smooth && nq > z.S ? nq : z.S) * z.d) * 32);
   L.vt = c.take((size_t)(z.BH * z.nt * z.d * sqattn::KT) * (pv == SQATTN_PV_BF16 ? 2 : 1));
   L.v_scale = c.take(pv == SQATTN_PV_BF16 ? 0 : (size_t)(z.BH * z.nt) * 4);
+  L.q_mean = c.take(smooth ? (size_t)(z.BH * nq * z.d) * 4 : 0);
+  L.q_bias = c.take(smooth ? (size_t)(z.BH * nq * z.nt * sqattn::KT) * 4 : 0);
   L.total = c.off;
   return L;
 }
@@ -338,7 +347,7 @@ size_t sqattn_workspace_bytes(int B, int H, int N, int d, int pv_dtype, const sq
     g_err = keep;
     return 0;
   }
-  return forward_layout(z, pv_dtype, o.q_block).total;
+  return forward_layout(z, pv_dtype, o.q_block, o.smooth_q != 0).total;
 }
 
 // q/k RMSNorm fused into the quantization: the per-token factors of q and
@@ -360,6 +369,8 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   Opts o;
   if ((s = validate_forward(q, k, v, B, H, N, d, scale, pv_dtype, out, opts, &z, &o))) return s;
   if (mask && (s = check_sparse(N))) return s;
+  if (o.smooth_q && (mask || qkn))
+    return fail(SQATTN_ERR_UNSUPPORTED, "Q smoothing runs on dense attention without the q/k RMSNorm");
   sqattn::Lay lay[4];
   for (int i = 0; i < 4; ++i) lay[i] = sqattn::contiguous_lay(H, N, d);
   for (int i = 0; i < 4; ++i) {
@@ -381,7 +392,8 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
       return fail(SQATTN_ERR_INVALID_ARG,
                   "q/k RMSNorm needs each token's H*d values of q and k contiguous (head stride d)");
   }
-  const FwdLayout L = forward_layout(z, pv_dtype, o.q_block);
+  const bool smooth = o.smooth_q != 0;
+  const FwdLayout L = forward_layout(z, pv_dtype, o.q_block, smooth);
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;
   if ((s = ws.acquire(workspace, workspace_bytes, L.total + (qkn ? qknorm_extra(z, B) : 0), st))) return s;
@@ -400,9 +412,15 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
     nq = sqattn::RowNorm{rq, qkn->gamma_q};
     nk = sqattn::RowNorm{rk, qkn->gamma_k};
   }
-  sqattn::launch_quant_i8((const uint16_t*)q, lay[0], BH, N, d, o.q_block, nullptr, qi, qs, st, nq);
+  float* qm = smooth ? ws.at<float>(L.q_mean) : nullptr;
+  if (smooth)
+    sqattn::launch_qmean((const uint16_t*)q, lay[0], BH, N, d, o.q_block, ws.at<uint64_t>(L.partial), qm, st);
+  sqattn::launch_quant_i8((const uint16_t*)q, lay[0], BH, N, d, o.q_block, qm, qi, qs, st, nq, smooth);
   sqattn::launch_kmean((const uint16_t*)k, lay[1], BH, N, d, ws.at<uint64_t>(L.partial), km, st, nk);
   sqattn::launch_quant_i8((const uint16_t*)k, lay[1], BH, N, d, o.k_block, km, ki, ks, st, nk);
+  if (smooth)
+    sqattn::launch_qbias((const uint16_t*)k, lay[1], BH, N, d, km, qm, qs, ks, o.q_block,
+                         ws.at<float>(L.q_bias), st);
   float* vs = nullptr;
   if (pv_dtype == SQATTN_PV_BF16) {
     sqattn::launch_v_tiles_bf16((const uint16_t*)v, lay[2], BH, N, d, ws.at<uint16_t>(L.vt), st);
@@ -420,6 +438,7 @@ static int forward_impl(const void* q, const void* k, const void* v, int B, int 
   p.out = out;
   p.out_bf16 = o.out_bf16;
   p.second_pass = o.second_pass;
+  p.qbias = smooth ? ws.at<float>(L.q_bias) : nullptr;
   p.N = N;
   p.nq = (int)z.nq;
   p.q_block = o.q_block;
@@ -539,6 +558,7 @@ static int attend_impl(const int8_t* q_i8, const float* q_scale, const int8_t* k
   if (pv_dtype == SQATTN_PV_FP8_E4M3 && (s = check_ptr(v_scale, "v_scale", 4))) return s;
   if (!std::isfinite(scale) || scale < 0.0f) return fail(SQATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if ((s = resolve_opts(opts, &o))) return s;
+  if (o.smooth_q) return fail(SQATTN_ERR_UNSUPPORTED, "Q smoothing is a step of the forward (Q is quantized here)");
   sqattn::AttnParams p{};
   p.q = q_i8;
   p.sq = q_scale;
@@ -604,6 +624,7 @@ static int attend_raw(const int8_t* q_i8, const float* q_scale, const int8_t* k_
   if (!std::isfinite(scale) || scale < 0.0f) return fail(SQATTN_ERR_INVALID_ARG, "scale must be finite and >= 0");
   Opts o;
   if ((s = resolve_opts(opts, &o))) return s;
+  if (o.smooth_q) return fail(SQATTN_ERR_UNSUPPORTED, "Q smoothing is a step of the forward (Q is quantized here)");
   if (mask && (s = check_sparse(N))) return s;
   hipStream_t st = (hipStream_t)stream;
   Workspace ws;

@@ -47,6 +47,13 @@
 //     tiles (positions index entries, list entries name tiles); a listed tile
 //     this wave's mask row drops gets the exponent offset +inf (P = 0), and
 //     the reference is taken from the first kept tile.
+//   * Q smoothing (SM, dense): the logit bias of the wave's Q block for the K
+//     tile's 64 keys (binary32, units of sQ sK) rides in the ring entry with
+//     the tile (1 KB, up to four blocks); the vector phase adds it to the
+//     float-bits scores before the exponent (the first tile's from global
+//     memory), one float add per score rounded at the scores' unit (a c / 2
+//     logit error at most where |S + bias| < 2^22, inside the 16-bit path's
+//     tolerance); maxima are then taken as floats.
 #include <mutex>
 
 #include "common.h"
@@ -92,7 +99,7 @@ __host__ __device__ __forceinline__ int swz(int r, int c) {
   return r * U + (c ^ ((r / (16 / U)) & (U - 1)));
 }
 
-template <int D>
+template <int D, bool SM = false>
 struct Geo {
   static constexpr int NCH = D / 32;            // INT8 k-steps (32 channels each)
   static constexpr int NCB = D / 32;            // 32-channel blocks of O^T
@@ -101,7 +108,8 @@ struct Geo {
   static constexpr int VU = 8;                  // 16-byte units of a V^T row (64 keys * 2 B)
   static constexpr int VTB = D * 128;           // V^T tile in LDS
   static constexpr int KSC = KBYTES + VTB;      // the K tile's scale (64 copies, one per lane)
-  static constexpr int ES = KSC + 256;          // ring entry: K tile, V^T tile, K scale
+  static constexpr int BOFF = KSC + 256;        // the Q-smoothing bias of the K tile (SM)
+  static constexpr int ES = BOFF + (SM ? 1024 : 0);  // ring entry: K tile, V^T tile, K scale, bias
   static constexpr int LDS_BYTES = NSLOT * ES;
   static constexpr int KCH = KBYTES / 1024;     // 1 KB direct loads per K tile
   static constexpr int VCH = VTB / 1024;        // ... per V^T tile
@@ -109,13 +117,17 @@ struct Geo {
   static constexpr int VBYTES = D * KT * 2;     // packed V tile in HBM
 };
 
-template <int D, bool SP>
+template <int D, bool SP, bool SM = false>
 struct Ctx {
-  using G = Geo<D>;
+  using G = Geo<D, SM>;
   uint8_t* lds;
   const uint8_t* kh;
   const uint8_t* vth;
   const float* skh;
+  const uint8_t* qbh;     // SM: the bias rows of the work-group's first Q block
+  uint32_t qboff;         // SM: this lane's byte offset in them (block lane / 16, 4 keys)
+  uint32_t qbw;           // SM: byte offset of this wave's block in an entry's bias area
+  long long qbg;          // SM: byte offset of this wave's block row from qbh (global)
   int N, nt, lane, wave, g, lr;
   uint32_t kad[G::NCH];   // per-lane LDS byte offsets of the K operands (k-step ch, half 0)
   uint32_t vad[4];        // ... of the V^T operands (16-key k-step ks, channel block 0)
@@ -176,19 +188,23 @@ struct Ctx {
     const uint8_t* kt;
     const uint8_t* vt;
     const float* ks;
+    const uint8_t* qb;
     uint32_t klim;
     int entry;
   };
   __device__ __forceinline__ Refill refill(int j) const {
     const int tk = tile_at(j + 1), tv = tile_at(j);
     return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, skh + tk,
-                  (uint32_t)(min(N - 1 - tk * KT, KT) * D), j % NSLOT};
+                  SM ? qbh + (long long)tk * KT * 4 : nullptr, (uint32_t)(min(N - 1 - tk * KT, KT) * D),
+                  j % NSLOT};
   }
-  // chunk slot i of a pair (i == PER: the K scale, wave 0 only).  K rows past
-  // the tile's last valid row read that row (same permuted column).
+  // chunk slot i of a pair (i == PER: the K scale, wave 0 only, and with SM
+  // the tile's bias, wave 1 only).  K rows past the tile's last valid row
+  // read that row (same permuted column).
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (i == G::PER) {
       if (wave == 0) lds_dma4(r.ks, 0u, lds_addr(lds + r.entry * G::ES + G::KSC));
+      if (SM && wave == 1) lds_dma16(r.qb, qboff, lds_addr(lds + r.entry * G::ES + G::BOFF));
       return;
     }
     const bool isk = is_k(i);  // wave-uniform
@@ -212,7 +228,7 @@ struct Ctx {
   // touches before both wave groups have passed that phase.
   __device__ __forceinline__ void phase_bar() const {
     __builtin_amdgcn_sched_barrier(0);
-    if (wave == 0)
+    if (wave == 0 || (SM && wave == 1))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (G::PER + 1)));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::PER));
@@ -233,6 +249,15 @@ struct Ctx {
     }
   }
 
+  // SM: the same over scores held as binary32 bit patterns of any sign, less off
+  __device__ __forceinline__ float rowmax_f(const v16i& x, float c, float off) const {
+    float d = __builtin_fmaxf(__int_as_float(x[0]), __int_as_float(x[1]));
+#pragma unroll
+    for (int i = 2; i < 16; ++i) d = __builtin_fmaxf(d, __int_as_float(x[i]));
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(d), __float_as_int(d), false, false);
+    return (__builtin_fmaxf(__int_as_float(r[0]), __int_as_float(r[1])) - off) * c;  // c >= 0
+  }
+
   // max over the 32 keys of half kb of S (lanes l and l^32 share a query), in log2 units
   __device__ __forceinline__ float rowmax(const v16i& x, float c, int bias) const {
     int d = max(max(x[0], x[1]), x[2]);
@@ -242,13 +267,40 @@ struct Ctx {
     return (float)(pair_max_i(d) - bias) * c;  // c >= 0
   }
 
+  // ---- SM: add the bias of the tile's keys (64 binary32 values of the
+  // wave's block at p, LDS or global) to the scores held as float bits
+  // (ints: converted first): register i of half kb is key
+  // 32 kb + 16 (i / 8) + 8 g + i % 8
+  template <bool FROM_INT = false, class P>
+  __device__ __forceinline__ void add_bias(const P* p) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4f b0 = *(const v4f*)((const uint8_t*)p + (32 * kb + 16 * h + 8 * g) * 4);
+        const v4f b1 = *(const v4f*)((const uint8_t*)p + (32 * kb + 16 * h + 8 * g) * 4 + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i0 = 8 * h + r, i1 = 8 * h + 4 + r;
+          const float x0 = FROM_INT ? (float)s[kb][i0] : __int_as_float(s[kb][i0]);
+          const float x1 = FROM_INT ? (float)s[kb][i1] : __int_as_float(s[kb][i1]);
+          s[kb][i0] = __float_as_int(x0 + b0[r]);
+          s[kb][i1] = __float_as_int(x1 + b1[r]);
+        }
+      }
+  }
+
   // ---- V(t): P = 2^(S c - k) with k = 1.5 * 2^23 c + ref, packed to bf16 as
   // the P^T operands, and the row sum.  Register i of half kb holds key
   // 32 kb + 16 (i / 8) + 8 g + i % 8 (perm_key order), which is element
   // i % 8 of lane-half g of 16-key k-step 2 kb + i / 8.  MASK: keys >= kvalid
-  // get P = 0.
+  // get P = 0.  SM: bias_e is the entry holding the tile's bias (< 0: the
+  // bias is in the scores already).
   template <bool MASK>
-  __device__ __forceinline__ void vphase(float c, float k, int kvalid, const Refill& rf) {
+  __device__ __forceinline__ void vphase(float c, float k, int kvalid, const Refill& rf, int bias_e = -1) {
+    if constexpr (SM) {
+      if (bias_e >= 0) add_bias(lds + bias_e * G::ES + G::BOFF + qbw);
+    }
     float part[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -355,8 +407,10 @@ struct Ctx {
 #pragma unroll
     for (int j = 0; j < NSLOT - 1; ++j) issue(refill(j));
     qk_global(tile_at(0));
+    if constexpr (SM) add_bias(qbh + qbg + (long long)tile_at(0) * KT * 4);
     float c = cq * ld_uniform(skh + tile_at(0));
-    if (!SP && set_ref) m = rowmax(s[0], c, SQ_MAGIC);  // reference: max of the first 32 keys
+    if (!SP && set_ref)  // reference: max of the first 32 keys
+      m = SM ? rowmax_f(s[0], c, SQ_MAGIC_F) : rowmax(s[0], c, SQ_MAGIC);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     if (wave >= 4) phase_bar();  // waves 4-7 run one phase behind
@@ -364,7 +418,8 @@ struct Ctx {
     for (int t = 0; t < npos - 1; ++t) {
       // V(t) refills the entry of pair t - 2 with pair t + 3, then reads the
       // first operands of M(t)
-      vphase<false>(c, SP ? k_sparse(t, c) : __builtin_fmaf(SQ_MAGIC_F, c, m), KT, refill(t + NSLOT - 2));
+      vphase<false>(c, SP ? k_sparse(t, c) : __builtin_fmaf(SQ_MAGIC_F, c, m), KT, refill(t + NSLOT - 2),
+                    t > 0 ? (t - 1) % NSLOT : -1);
       prefetch<true>(t);
       phase_bar();
       const float ksc = mphase<true>(t);
@@ -373,7 +428,7 @@ struct Ctx {
     }
     const int t = npos - 1;
     vphase<true>(c, SP ? k_sparse(t, c) : __builtin_fmaf(SQ_MAGIC_F, c, m), N - tile_at(t) * KT,
-                 refill(t + NSLOT - 2));
+                 refill(t + NSLOT - 2), t > 0 ? (t - 1) % NSLOT : -1);
     prefetch<false>(t);
     phase_bar();
     mphase<false>(t);
@@ -409,7 +464,13 @@ struct Ctx {
           const v4i a = *(const v4i*)(lds + kad[ch] + kb * 32 * D);
           s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], ch == 0 ? z : s[kb], 0, 0, 0);
         }
-      const float r = __builtin_fmaxf(rowmax(s[0], c, 0), rowmax(s[1], c, 0));
+      float r;
+      if constexpr (SM) {
+        add_bias<true>(qbh + qbg + (long long)t * KT * 4);
+        r = __builtin_fmaxf(rowmax_f(s[0], c, 0.0f), rowmax_f(s[1], c, 0.0f));
+      } else {
+        r = __builtin_fmaxf(rowmax(s[0], c, 0), rowmax(s[1], c, 0));
+      }
       if (!SP || keeps(list[j])) mx = __builtin_fmaxf(mx, r);
     }
     __syncthreads();
@@ -419,10 +480,10 @@ struct Ctx {
 
 }  // namespace
 
-template <int D, bool SP>
+template <int D, bool SP, bool SM>
 __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
-  using Cx = Ctx<D, SP>;
-  using G = Geo<D>;
+  using Cx = Ctx<D, SP, SM>;
+  using G = Geo<D, SM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int w = blockIdx.x;
@@ -447,6 +508,19 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   C.kh = (const uint8_t*)p.k + hoff;
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
+  if constexpr (SM) {
+    // blocks of q_block (64, 128 or 256) rows: the work-group's first block
+    // and this wave's (a wave whose rows all lie past N takes the last
+    // existing block); lane l of the bias load reads block b0 + l / 16 (the
+    // last existing one past the end), keys 4 (l % 16) .. + 3
+    const int b0 = qt * ATT_QWG / p.q_block, nbw = min(ATT_QWG / p.q_block, p.nq - b0);
+    const long long rowb = (long long)p.nt * KT * 4;
+    C.qbh = (const uint8_t*)p.qbias + ((long long)bh * p.nq + b0) * rowb;
+    C.qboff = (uint32_t)(min(C.lane / 16, nbw - 1) * rowb + (C.lane % 16) * 16);
+    const int wb = min(C.wave * ATT_QW / p.q_block, nbw - 1);
+    C.qbw = (uint32_t)(wb * 256);
+    C.qbg = (long long)wb * rowb;
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) C.magic[r] = SQ_MAGIC;
   asm volatile("" : "+v"(C.magic));  // keep the accumulator start in vector registers
@@ -506,25 +580,30 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, inv, C.g);
 }
 
-template <int D, bool SP>
+template <int D, bool SP, bool SM>
 static hipError_t launch_d(const AttnParams& q, hipStream_t st) {
-  constexpr int lds = Geo<D>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
+  constexpr int lds = Geo<D, SM>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   // the attribute is per kernel: set once per process (the first status is kept)
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               lds);
+    attr = hipFuncSetAttribute((const void*)attn_bf16_kernel<D, SP, SM>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, SP>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, SP, SM>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
   return hipSuccess;
 }
 
+// Q smoothing (q.qbias) runs on the dense kernels only (the caller checks)
 hipError_t launch_attention_bf16(const AttnParams& q, int d, hipStream_t st) {
-  const bool sp = q.mask != nullptr;
-  if (d == 128) return sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
-  return sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
+  const bool sp = q.mask != nullptr, sm = q.qbias != nullptr;
+  if (d == 128) {
+    if (sm) return launch_d<128, false, true>(q, st);
+    return sp ? launch_d<128, true, false>(q, st) : launch_d<128, false, false>(q, st);
+  }
+  if (sm) return launch_d<64, false, true>(q, st);
+  return sp ? launch_d<64, true, false>(q, st) : launch_d<64, false, false>(q, st);
 }
 
 }  // namespace sqattn

@@ -3,29 +3,37 @@
 // Same integer logits and register layouts as the 16-bit kernel (INT8
 // S^T = K Q^T with K rows in the perm_key order, lane-local softmax, O^T =
 // V^T P^T with P^T built in the lane), with the P.V product on
-// v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation).  What the FP8
-// path adds is the online rounding the result depends on: P is rounded to
-// E4M3 relative to the running row max of the tiles seen so far, so this
-// kernel keeps an exact running max per 64-key tile and rescales O when it
-// moves.
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation, E8M0
+// block scales).  What the FP8 path adds is the online rounding the result
+// depends on: P is rounded to E4M3 relative to the running row max of the
+// tiles seen so far, so this kernel keeps an exact running max per 64-key
+// tile and rescales O when it moves.
 //
 // Work-group: 8 waves (two per SIMD), 32 query rows each.  The unit of the
 // pipeline is a 64-key tile:
 //
-//   iteration t:   MFMA  T    = V(t-1)^T P(t-1)^T     (D/32 x fp8 32x32x64)
-//                  MFMA  S(t+1) = K(t+1) Q^T          (2 D/32 x i8 32x32x32)
-//                  VALU  tile max of S(t) -> m(t)
-//                        O += sV(t-1) 2^(m(t-1) - mr) T
+//   iteration t:   MFMA  O^T += sV(t-1) V(t-1)^T P(t-1)^T (D/32 x fp8 32x32x64)
+//                  MFMA  S(t+1) = K(t+1) Q^T             (2 D/32 x i8 32x32x32)
+//                  VALU  tile max of S(t) -> m(t); if it moved for some
+//                        row of the wave, O and the row sum *= 2^(m(t-1) - m(t))
 //                        P(t) = E4M3(448 * 2^(S(t) c(t) - m(t))), row sum
 //
-// * Tile t's P is relative to m(t), the exact max over tiles 0..t.  O and
-//   the row sum are kept relative to a reference mr <= m that moves up only
-//   when some row's max outgrew it by 2^16 (one exp per row and tile, and a
-//   vector rescale of O rarely after the first tile).
-// * The per-block V scale is applied as O += sV * T with T from an MFMA that
-//   starts at zero, so O is held in absolute units (no ratio of scales that
-//   could overflow when neighbouring V blocks differ by many orders of
-//   magnitude).
+// * Tile t's P is relative to m(t), the exact max over tiles 0..t, and so
+//   are O and the row sum: the matrix instruction accumulates straight into
+//   O.  The rescale is a branch taken by the whole wave when some row's max
+//   moved (often on the first tiles, rarely later: a new maximum among t
+//   tiles of random scores comes with probability about 1/t per row).
+// * The V block scale is a power of two (see the V quantizer) and rides in
+//   the instruction as the E8M0 scale of the V operand, so O is held in
+//   absolute units with no vector work per tile, also when neighbouring V
+//   blocks differ by many orders of magnitude.
+// * Scores: the INT8 accumulation starts from the bits of 1.5 * 2^23, so the
+//   int32 result read as a float is exactly 1.5 * 2^23 + S (|S| < 2^22) and S
+//   is one exact full-rate subtraction away (not the half-rate int-to-float
+//   conversion); the tile max is taken on the biased integers.  The bf16
+//   kernel's one-FMA form, which folds 1.5 * 2^23 c into the exponent offset,
+//   rounds that offset: up to 0.75 c in the exponent, outside the E4M3
+//   envelope.
 // * 448 is folded into the exponent: y = 2^(x c - (m - log2 448)) = 448 P~,
 //   the E4M3 operand is the rounded y and the row sum adds the unrounded y, so
 //   O = sum(sV y^ code) / sum(y).
@@ -39,6 +47,14 @@
 // * Keys past N: the K tile reads row N-1 there (a real score of the same
 //   tile, so the tile max is unchanged), y is zeroed for them in the last
 //   tile, and the packed V tile is zero past N.
+// * Q smoothing (SM): the logit bias of the wave's Q block for the tile's 64
+//   keys, a binary32 value in units of sQ sK, rides in the V slot of the
+//   previous tile (1 KB: up to four blocks of the work-group), which has
+//   landed by iteration t and stays put through it; the first tile's comes
+//   from global memory.  The scores are converted first and the
+//   bias added (fl32(S + bias), one rounding); the tile max and P are taken on
+//   those values.  One vector add per score; a rounded integer bias would
+//   move logits by up to c / 2, too coarse for the E4M3 rounding of P.
 #include <mutex>
 
 #include "common.h"
@@ -54,7 +70,9 @@ constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
 constexpr int NSLOT = 4;                          // LDS ring depth (tiles)
 constexpr float LOG2_448 = 8.80735492205760410f;  // log2(448)
-constexpr float REBASE = 16.0f;                   // lazy reference of O: at most 2^16 below the max
+constexpr int E8M0_ONE = 127;                     // E8M0 scale 2^0
+constexpr int SQ_MAGIC = 0x4B400000;              // bits of 1.5 * 2^23
+constexpr float SQ_MAGIC_F = 12582912.0f;
 
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 field layout:
@@ -75,7 +93,7 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
   return *(const __attribute__((address_space(4))) float*)p;
 }
 
-template <int D>
+template <int D, bool SM = false>
 struct Geo {
   static constexpr int NCH = D / 32;            // QK k-steps per 32-key half
   static constexpr int NCB = D / 32;            // 32-channel blocks of O^T
@@ -87,33 +105,37 @@ struct Geo {
   static constexpr int VROWC = 5;               // V^T row: 64 keys * 1 B = 4 chunks + pad
   static constexpr int VROW = 16 * VROWC;
   static constexpr int VSC = D * VROW;          // offset of the V scale in a V slot
-  static constexpr int VS = VSC + 256;          // V slot bytes
+  static constexpr int VQB = VSC + 256;         // offset of the Q-smoothing bias (SM)
+  static constexpr int VS = VQB + (SM ? 1024 : 0);  // V slot bytes
   static constexpr int VBASE = NSLOT * KS;      // V ring offset in LDS
   static constexpr int LDS_BYTES = NSLOT * (KS + VS);
   static constexpr int KINST = (KT * KROWC + 63) / 64;   // 1 KB direct loads per K tile
   static constexpr int VINST = (D * VROWC + 63) / 64;     // ... per V tile
   static constexpr int PER = (KINST + VINST + WAVES - 1) / WAVES;  // K+V loads per wave
-  static constexpr int LPB = PER + 2;           // direct loads per wave per boundary (+ 2 scales)
+  static constexpr int LPB = PER + 2 + (SM ? 1 : 0);  // direct loads per wave per boundary (+ 2 scales, bias)
   static constexpr int VBYTES = D * KT;         // packed V tile in HBM
 };
 
-template <int D, bool SP = false>
+template <int D, bool SP = false, bool SM = false>
 struct Ctx {
-  using G = Geo<D>;
+  using G = Geo<D, SM>;
   uint8_t* lds;
   const uint8_t* kh;
   const uint8_t* vth;
   const float* skh;
   const float* svh;
+  const uint8_t* qbh;     // SM: the bias rows of the work-group's first Q block
+  uint32_t qboff;         // SM: this lane's byte offset in them (block lane / 16, 4 keys)
+  uint32_t qbw;           // SM: byte offset of this wave's block in a slot's bias area
+  long long qbg;          // SM: byte offset of this wave's block row from qbh (global)
   int N, nt, lane, wave, g, lr;
   uint32_t kbase, vbase;  // per-lane LDS operand offsets (slot 0)
   float cq;               // sQ(row) * scale * log2(e)
   v4i qreg[G::NCH];       // Q operands
+  v16i magic;             // SQ_MAGIC in every element: start of the INT8 accumulation
   v16f o[G::NCB];         // O^T accumulators (absolute units, relative to m)
-  float m;               // running max (log2 units): P of tile t is relative to m(t)
-  float mr;              // reference of O and l (mr <= m, lazily moved up)
-  float ep;              // 2^(m - mr) of the latest tile
-  float l;               // running sum of 448 P~, relative to mr
+  float m;               // running max (log2 units): P, O and l of tile t are relative to m(t)
+  float l;               // running sum of 448 P~
 
   // ---- global -> LDS (direct); see the 16-bit kernel for the scheme.  Chunk
   // slot i < PER of a wave is one 1 KB chunk of the K or V slot; PER and
@@ -149,6 +171,12 @@ struct Ctx {
                   (uint32_t)(min(N - 1 - tk * KT, KT) * D)};
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
+    if (SM && i == G::PER + 2) {
+      // the bias of the tile after V's (dense: tile tv + 1), clamped
+      lds_dma16(qbh + (long long)min(r.tv + 1, nt - 1) * KT * 4, qboff,
+                lds_addr(lds + G::VBASE + r.vs * G::VS + G::VQB));
+      return;
+    }
     if (i == G::PER) {
       lds_dma4(skh + r.tk, 0u, lds_addr(lds + r.ks * G::KS + G::KSC));
       return;
@@ -172,8 +200,29 @@ struct Ctx {
   __device__ __forceinline__ float k_scale(int slot) const {
     return *(const float*)(lds + slot * G::KS + G::KSC + 4 * lane);
   }
-  __device__ __forceinline__ float v_scale(int slot) const {
-    return *(const float*)(lds + G::VBASE + slot * G::VS + G::VSC + 4 * lane);
+  // the V block scale (a power of two) as the E8M0 scale of the instruction:
+  // its binary exponent field (2^-127, stored as a subnormal, and 0 give 0)
+  __device__ __forceinline__ int v_scale_e8(int slot) const {
+    return (int)((*(const uint32_t*)(lds + G::VBASE + slot * G::VS + G::VSC + 4 * lane) >> 23) & 0xFF);
+  }
+
+  // ---- SM: the scores of tile t as binary32 values fl32(S + bias), in place
+  // (bit patterns in the integer registers); the bias of the 16 keys
+  // 32 kb + 16 h + 8 g + j (h < 2, j < 8) of the lane's rows is read from the
+  // tile's 64 values of the wave's block at p
+  __device__ __forceinline__ void add_bias(v16i (&s)[2], const uint8_t* p) const {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4f b0 = *(const v4f*)(p + (32 * kb + 16 * h + 8 * g) * 4);
+        const v4f b1 = *(const v4f*)(p + (32 * kb + 16 * h + 8 * g) * 4 + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][8 * h + r] = __float_as_int((__int_as_float(s[kb][8 * h + r]) - SQ_MAGIC_F) + b0[r]);
+          s[kb][8 * h + 4 + r] = __float_as_int((__int_as_float(s[kb][8 * h + 4 + r]) - SQ_MAGIC_F) + b1[r]);
+        }
+      }
   }
 
   // ---- S of K tile t0 straight from global memory (rows past N read row N-1)
@@ -185,15 +234,22 @@ struct Ctx {
       for (int ch = 0; ch < G::NCH; ++ch) {
         const v4i a = *(const v4i*)(kh + (long long)key * D + ch * 32 + g * 16);
         if (ch == 0) {
-          v16i z;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z[r] = 0;
-          s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], z, 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], magic, 0, 0, 0);
         } else {
           s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], s[kb], 0, 0, 0);
         }
       }
     }
+  }
+
+  // ---- SM: the same over binary32 scores held as bit patterns
+  __device__ __forceinline__ float tile_max_f(const v16i (&s)[2]) const {
+    float d0 = __builtin_fmaxf(__int_as_float(s[0][0]), __int_as_float(s[1][0]));
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+      d0 = __builtin_fmaxf(d0, __builtin_fmaxf(__int_as_float(s[0][i]), __int_as_float(s[1][i])));
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(d0), __float_as_int(d0), false, false);
+    return __builtin_fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
   }
 
   // ---- row max of S(t) over the tile's 64 keys (lanes l and l^32 share a row)
@@ -209,38 +265,45 @@ struct Ctx {
     return pair_max_i(d0);
   }
 
-  // ---- one tile iteration t.  QK: the next tile's scores into sn (when
-  // QK); PV: V(t-1) (slot vslot, scale svp) times pprev; softmax of sc (tile
-  // t, factor c) into pcur.  MASK: last tile, keys >= N excluded.
-  // Block-sparse: t is the list position (slots), tile the tile number; a
-  // listed tile this wave's mask row drops (act false) leaves the running
-  // max alone, gets P = 0 (mp = +inf) and carries weight ep = 0, which also
-  // keeps the first kept tile's 2^(m - mr) from meeting m = mr = -inf.
-  template <bool QK, bool MASK>
-  __device__ __forceinline__ void iter(const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t,
-                                       float c, float svp, const Refill& rf, int tile = 0, bool act = true) {
-    const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
-    const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
-
-    // running max of tile t
-    float mn = __builtin_fmaxf(m, (float)tile_max(sc) * c);  // c >= 0
-    if constexpr (SP) mn = act ? mn : m;
-    const float w = svp * ep;  // tile t-1 relative to mr
-
-    // P.V of the previous tile from a zero accumulator, O += w T
+  // ---- O^T += sV V^T P^T for the V tile at LDS offset va (per lane), its
+  // scale as E8M0 exponent sve
+  __device__ __forceinline__ void pv(uint32_t va, const v8i& p, int sve, const Refill* rf) {
 #pragma unroll
     for (int cb = 0; cb < G::NCB; ++cb) {
       const v4i a0 = *(const v4i*)(lds + va + cb * 32 * G::VROW);
       const v4i a1 = *(const v4i*)(lds + va + cb * 32 * G::VROW + 16);
       const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      v16f z;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) z[r] = 0.0f;
-      const v16f tv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pprev, z, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(tv[r], w, o[cb][r]);
-      if (cb < G::LPB) load_part(rf, cb);
+      // formats 0/0: E4M3 x E4M3; the V operand scaled by 2^(sve - 127)
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, o[cb], 0, 0, 0, sve, 0, E8M0_ONE);
+      if (rf && cb < G::LPB) load_part(*rf, cb);
     }
+  }
+
+  // ---- one tile iteration t.  QK: the next tile's scores into sn (when
+  // QK); PV: V(t-1) (scale exponent sve) times pprev into O; softmax of sc
+  // (tile t, factor c) into pcur.  MASK: last tile, keys >= N excluded.
+  // Block-sparse: t is the list position (slots), tile the tile number; a
+  // listed tile this wave's mask row drops (act false) leaves the running
+  // max alone and gets P = 0 (mp = +inf).
+  template <bool QK, bool MASK>
+  __device__ __forceinline__ void iter(v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t,
+                                       float c, int sve, const Refill& rf, int tile = 0, bool act = true) {
+    const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
+    const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
+
+    // running max of tile t (SM: of the biased binary32 scores; the bias of
+    // tile t > 0 sits in V slot t - 1, landed at boundary t - 1)
+    float mn;
+    if constexpr (SM) {
+      if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NSLOT - 1)) * G::VS + G::VQB + qbw);
+      mn = __builtin_fmaxf(m, tile_max_f(sc) * c);
+    } else {
+      mn = __builtin_fmaxf(m, (float)(tile_max(sc) - SQ_MAGIC) * c);  // c >= 0
+    }
+    if constexpr (SP) mn = act ? mn : m;
+
+    // P.V of the previous tile (relative to m(t-1) = m) into O
+    pv(va, pprev, sve, &rf);
     // scores of the next tile
     if constexpr (QK) {
 #pragma unroll
@@ -249,10 +312,7 @@ struct Ctx {
         for (int kb = 0; kb < 2; ++kb) {
           const v4i a = *(const v4i*)(lds + ka + kb * 32 * G::KROW + ch * 32);
           if (ch == 0) {
-            v16i z;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = 0;
-            sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], z, 0, 0, 0);
+            sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], magic, 0, 0, 0);
           } else {
             sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], sn[kb], 0, 0, 0);
           }
@@ -261,24 +321,19 @@ struct Ctx {
 #pragma unroll
     for (int i = G::NCB; i < G::LPB; ++i) load_part(rf, i);
 
-    // move the reference of O and l up once some row's max outgrew it by
-    // 2^REBASE (always on the first tile, where mr = -inf)
-    if (__builtin_amdgcn_ballot_w64(mn - mr > REBASE)) {
-      const float f = __builtin_amdgcn_exp2f(mr - mn);  // mr = -inf: 0
+    // O and l follow the max: rescale when it moved for some row of the
+    // wave (always on the first tile, where m = -inf and O = l = 0)
+    if (__builtin_amdgcn_ballot_w64(mn > m)) {
+      const float f = __builtin_amdgcn_exp2f(m - mn);  // 1 where unmoved; m = -inf: 0
 #pragma unroll
       for (int cb = 0; cb < G::NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] *= f;
       l *= f;
-      mr = mn;
     }
     m = mn;
     float mp = mn - LOG2_448;
-    ep = __builtin_amdgcn_exp2f(mn - mr);  // tile t relative to mr, <= 2^REBASE
-    if constexpr (SP) {
-      mp = act ? mp : __builtin_inff();
-      ep = act ? ep : 0.0f;
-    }
+    if constexpr (SP) mp = act ? mp : __builtin_inff();
 
     // P(t) = E4M3(y), y = 448 P~; byte 16 kb + i of the operand is key
     // 32 kb + 16 (i / 8) + 8 g + i % 8, the lane's S(t)[kb][i]
@@ -291,7 +346,9 @@ struct Ctx {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j;
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[kb][i], c, -mp));
+        // exact: 1.5 * 2^23 + S - 1.5 * 2^23 (|S| < 2^22), a full-rate subtract
+        const float sv = SM ? __int_as_float(sc[kb][i]) : __int_as_float(sc[kb][i]) - SQ_MAGIC_F;
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mp));
         if constexpr (MASK) {
           const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
           if (key >= kvalid) e = 0.0f;
@@ -303,34 +360,16 @@ struct Ctx {
       word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
       pcur[r] = word;
     }
-    l = __builtin_fmaf(ep, (part[0] + part[1]) + (part[2] + part[3]), l);
-  }
-
-  // ---- O += sV(last) 2^(m - mr) V(last)^T P(last)^T
-  __device__ __forceinline__ void pv_last(const v8i& p, int slot, float sv) {
-    sv *= ep;
-    const uint32_t va = vbase + slot * G::VS;
-#pragma unroll
-    for (int cb = 0; cb < G::NCB; ++cb) {
-      const v4i a0 = *(const v4i*)(lds + va + cb * 32 * G::VROW);
-      const v4i a1 = *(const v4i*)(lds + va + cb * 32 * G::VROW + 16);
-      const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      v16f z;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) z[r] = 0.0f;
-      const v16f t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, z, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(t[r], sv, o[cb][r]);
-    }
+    l += (part[0] + part[1]) + (part[2] + part[3]);
   }
 };
 
 }  // namespace
 
-template <int D, bool SP>
+template <int D, bool SP, bool SM>
 __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
-  using Cx = Ctx<D, SP>;
-  using G = Geo<D>;
+  using Cx = Ctx<D, SP, SM>;
+  using G = Geo<D, SM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int w = blockIdx.x;
@@ -354,6 +393,19 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
   C.svh = p.sv + (long long)bh * p.nt;
+  if constexpr (SM) {
+    // blocks of q_block (64, 128 or 256) rows: the work-group's first block
+    // and this wave's; lane l of the bias load reads block b0 + l / 16 (the
+    // last existing one past the end), keys 4 (l % 16) .. + 3
+    const int b0 = qt * ATT_QWG / p.q_block, nbw = min(ATT_QWG / p.q_block, p.nq - b0);
+    const long long rowb = (long long)p.nt * KT * 4;
+    C.qbh = (const uint8_t*)p.qbias + ((long long)bh * p.nq + b0) * rowb;
+    C.qboff = (uint32_t)(min(C.lane / 16, nbw - 1) * rowb + (C.lane % 16) * 16);
+    // (a wave whose rows all lie past N takes the last existing block)
+    const int wb = min(C.wave * ATT_QW / p.q_block, nbw - 1);
+    C.qbw = (uint32_t)(wb * 256);
+    C.qbg = (long long)wb * rowb;
+  }
   C.init_loads();
   const int row = qt * ATT_QWG + C.wave * ATT_QW + C.lr;
   const bool rok = row < p.N;
@@ -362,9 +414,10 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     C.qreg[ch] = rok ? *(const v4i*)(p.q + hoff + (long long)row * D + ch * 32 + C.g * 16) : v4i{0, 0, 0, 0};
   C.cq = rok ? p.sq[(long long)bh * p.nq + row / p.q_block] * p.scale_log2e : 0.0f;
   C.m = -__builtin_inff();
-  C.mr = -__builtin_inff();
-  C.ep = 0.0f;
   C.l = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) C.magic[r] = SQ_MAGIC;
+  asm volatile("" : "+v"(C.magic));  // keep the accumulator start in vector registers
 #pragma unroll
   for (int cb = 0; cb < G::NCB; ++cb)
 #pragma unroll
@@ -396,6 +449,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   v16i S0[2], S1[2];
   v8i P0, P1;
   C.qk_first(S0, tile_at(0));
+  if constexpr (SM) C.add_bias(S0, C.qbh + C.qbg + (long long)tile_at(0) * KT * 4);
   float c = C.cq * ld_uniform(C.skh + tile_at(0));
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
@@ -409,12 +463,12 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   // the prologue put there (read no earlier than iterations 3 and 2, after
   // boundaries that wait for it), so every iteration issues the same loads.
   typename Cx::Refill rf = C.refill(tile_at(4), 0, tile_at(2), 2);
-  auto step = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
+  auto step = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
     // K(t+1) and V(t-1) have landed (boundary t-1); their slots are refilled
     // only after this iteration
     const float c_next = C.cq * C.k_scale((t + 1) & (NSLOT - 1));
-    const float svp = C.v_scale((t - 1) & (NSLOT - 1));
-    C.template iter<true, false>(sc, sn, pprev, pcur, t, c, svp, rf, tile_at(t), kept(t));
+    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
+    C.template iter<true, false>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
     // Wait for our own loads of three boundaries ago and all LDS reads, then
     // a plain barrier (the "memory" clobber keeps every memory access on its
     // side).  __syncthreads() would add a fence that waits for every
@@ -424,14 +478,14 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     rf = C.refill(tile_at(t + 5), (t + 1) & (NSLOT - 1), tile_at(t + 3), (t - 1) & (NSLOT - 1));
     c = c_next;
   };
-  auto last = [&](const v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
-    const float svp = C.v_scale((t - 1) & (NSLOT - 1));
-    C.template iter<false, true>(sc, sn, pprev, pcur, t, c, svp, rf, tile_at(t), kept(t));
+  auto last = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
+    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
+    C.template iter<false, true>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
     // V(t) may still be in flight (issued up to two boundaries ago, by any
     // wave): wait for every load, then a barrier
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    C.pv_last(pcur, t & (NSLOT - 1), C.v_scale(t & (NSLOT - 1)));
+    C.pv(C.vbase + (t & (NSLOT - 1)) * G::VS, pcur, C.v_scale_e8(t & (NSLOT - 1)), nullptr);
   };
   // tiles in pairs, so that the score and P registers alternate without copies
   int t = 0;
@@ -453,25 +507,30 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, inv, C.g);
 }
 
-template <int D, bool SP>
+template <int D, bool SP, bool SM>
 static hipError_t launch_d(const AttnParams& q, hipStream_t st) {
-  constexpr int lds = Geo<D>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
+  constexpr int lds = Geo<D, SM>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   // the attribute is per kernel: set once per process (the first status is kept)
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute((const void*)attn_fp8_kernel<D, SP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               lds);
+    attr = hipFuncSetAttribute((const void*)attn_fp8_kernel<D, SP, SM>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_fp8_kernel<D, SP>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
+  hipLaunchKernelGGL((attn_fp8_kernel<D, SP, SM>), dim3(8 * q.per_xcd), dim3(NTHR), lds, st, q);
   return hipSuccess;
 }
 
+// Q smoothing (q.qbias) runs on the dense kernels only (the caller checks)
 hipError_t launch_attention_fp8(const AttnParams& q, int d, hipStream_t st) {
-  const bool sp = q.mask != nullptr;
-  if (d == 128) return sp ? launch_d<128, true>(q, st) : launch_d<128, false>(q, st);
-  return sp ? launch_d<64, true>(q, st) : launch_d<64, false>(q, st);
+  const bool sp = q.mask != nullptr, sm = q.qbias != nullptr;
+  if (d == 128) {
+    if (sm) return launch_d<128, false, true>(q, st);
+    return sp ? launch_d<128, true, false>(q, st) : launch_d<128, false, false>(q, st);
+  }
+  if (sm) return launch_d<64, false, true>(q, st);
+  return sp ? launch_d<64, true, false>(q, st) : launch_d<64, false, false>(q, st);
 }
 
 }  // namespace sqattn

@@ -64,8 +64,18 @@ constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch(void** ptr);
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st, const RowNorm& nm = RowNorm{});
-void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
-                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm = RowNorm{});
+// mean: null (plain), one row per head (K smoothing), or with mean_blocks one
+// row per block (Q smoothing: rows of blocks quantized plainly are set to 0)
+void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, float* mean,
+                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm = RowNorm{},
+                     bool mean_blocks = false);
+// Q smoothing: the exact mean of every block of `block` rows ([BH][nq][d];
+// partial: BH * nq * d * 32 bytes), and the logit bias of every (block, key)
+// in units of sQ sK ([BH][nq][nt * 64], binary32)
+void launch_qmean(const uint16_t* q, const Lay& lq, int BH, int N, int d, int block, uint64_t* partial,
+                  float* mean, hipStream_t st);
+void launch_qbias(const uint16_t* k, const Lay& lk, int BH, int N, int d, const float* kmean, const float* qmean,
+                  const float* q_scale, const float* k_scale, int block, float* bias, hipStream_t st);
 void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st);
 void launch_quant_v_fp8(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint8_t* codes, uint8_t* vt,
                         float* scales, hipStream_t st);
@@ -86,6 +96,9 @@ struct AttnParams {
   int N, nq, q_block, nt, BH, qtiles, per_xcd;
   float scale_log2e;
   uint32_t* second_pass;  // null, or a counter of work items that took the exact-max second pass
+  // Q smoothing: null, or the logit bias [BH][nq][nt * 64] of every (Q block,
+  // key) in units of sQ sK, binary32 (q_block 64, 128 or 256; dense only)
+  const float* qbias;
 };
 
 // 16-bit P.V kernel; p.qtiles and p.per_xcd must be set.  Returns the status

@@ -9,7 +9,8 @@
 //       code = clamp(rne(fl32(x/s)), -127, 127).
 //   v_tiles_bf16 : V into the attention kernel's tile layout ([d][64 keys]).
 //   quant_v_fp8 : per-64-row E4M3 codes of V (GVCLab research log 2026-09-02,
-//       section 5.5 table: FP8 P.V), s_v = fl32(absmax/448).
+//       section 5.5 table: FP8 P.V), s_v the smallest power of two with
+//       absmax <= 448 s_v.
 //
 // All kernels are HBM-bound streaming passes; loads and stores are 16-byte
 // per lane along rows so that each wave touches whole 128-byte lines.
@@ -181,6 +182,22 @@ __global__ __launch_bounds__(D) void kmean_finalize_kernel(const uint64_t* __res
   mean[bh * D + c] = bad ? __builtin_nanf("") : acc192_mean_f32(s, (uint32_t)N);
 }
 
+// grid (nq, B*H), D threads: the mean of each Q block from its partial sum
+// (the partial pass run with one chunk per block): mu = fl32(sum / rows),
+// rounded once; NaN where a value fell outside the exact range.
+template <int D>
+__global__ __launch_bounds__(D) void qmean_finalize_kernel(const uint64_t* __restrict__ partial, int N,
+                                                           int block, float* __restrict__ mean) {
+  const long long bh = blockIdx.y;
+  const int b = blockIdx.x, nq = gridDim.x, c = threadIdx.x;
+  const uint64_t* p = partial + ((bh * nq + b) * D + c) * 4;
+  Acc192 s;
+  acc192_zero(s);
+  acc192_add(s, p[0], p[1], p[2]);
+  const int rows = min(N, (b + 1) * block) - b * block;
+  mean[(bh * nq + b) * D + c] = p[3] ? __builtin_nanf("") : acc192_mean_f32(s, (uint32_t)rows);
+}
+
 // ---------------------------------------------------------------------------
 // per-block INT8 quantization
 // ---------------------------------------------------------------------------
@@ -196,14 +213,19 @@ __device__ __forceinline__ float block_max_256(float v, float* sh) {
 }
 
 // grid (nblocks, B*H), 256 threads.  One work-group per block of `block` rows.
-// mean == nullptr: plain Q.  Otherwise x = fl32(K - mean[c]) (IEEE subtract).
+// mean == nullptr: plain Q.  Otherwise x = fl32(X - mean[c]) (IEEE subtract),
+// with one mean per head (K, mean_blocks = 0) or per block (Q smoothing,
+// mean_blocks = 1).  Q smoothing keeps a block's mean when the smoothed
+// block's scale s > 0 and the mean is finite (a NaN mean comes from values
+// outside the exact range); otherwise the block is quantized plainly and its
+// mean row is set to 0.
 // Blocks of at most QCACHE * RPP rows (128 at D = 128, 256 at D = 64) are
 // read once and kept in registers between the absmax and the coding pass;
 // larger blocks are read twice.
 constexpr int QCACHE = 8;
 template <int D, bool NORM>
 __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restrict__ x, Lay lx, int N, int block,
-                                                       const float* __restrict__ mean,
+                                                       float* __restrict__ mean, int mean_blocks,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales, RowNorm nm) {
   constexpr int CPR = D / 8;
@@ -216,12 +238,14 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   int8_t* ch = codes + bh * (long long)N * D;
   const int r0 = blk * block, r1 = min(N, r0 + block);
 
+  float* mrow = mean ? mean + (mean_blocks ? (bh * nblk + blk) * D : bh * D) : nullptr;
+  bool use_mean = mean != nullptr;  // uniform
   float mu[8];
   bool mean_nan = false;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    mu[j] = mean ? mean[bh * D + cg * 8 + j] : 0.0f;
-    mean_nan |= (mu[j] != mu[j]);
+    mu[j] = mrow ? mrow[cg * 8 + j] : 0.0f;
+    mean_nan |= (mu[j] != mu[j]) && !mean_blocks;
   }
 
   float gw[8];
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
     for (int j = 0; j < 4; ++j) {
       uint32_t u = (uint32_t)w[j];
       float a = bf16_bits_to_f32(u & 0xFFFFu), b = bf16_bits_to_f32(u >> 16);
-      if (mean) {
+      if (use_mean) {
         a = a - mu[2 * j];
         b = b - mu[2 * j + 1];
       }
@@ -268,7 +292,31 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
   // a NaN mean (K out of range) poisons the whole block's scale
   float nanflag = block_max_256(mean_nan ? 1.0f : 0.0f, sh);
   amax = block_max_256(amax, sh);
-  const float s = amax / 127.0f;  // correctly rounded binary32 division
+  float s = amax / 127.0f;  // correctly rounded binary32 division
+  if (mean_blocks) {
+    bool fin = true;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fin &= isfinite(mu[j]);
+    const bool keep = (s > 0.0f) && __syncthreads_and(fin);  // uniform
+    if (!keep) {  // uniform: quantize the block plainly, its mean row 0
+      use_mean = false;
+      amax = 0.0f;
+      if (resident) {
+#pragma unroll
+        for (int i = 0; i < QCACHE; ++i)
+          if (r0 + rg + i * RPP < r1) amax = chunk_max(cache[i], amax);
+      } else {
+        for (int r = r0 + rg; r < r1; r += RPP) {
+          v4i w = *(const v4i*)(xh + (long long)r * lx.sn + cg * 8);
+          if constexpr (NORM) w = norm_chunk(w, rr[r], gw);
+          amax = chunk_max(w, amax);
+        }
+      }
+      amax = block_max_256(amax, sh);
+      s = amax / 127.0f;
+      if (t < D) mrow[t] = 0.0f;
+    }
+  }
   if (t == 0) scales[bh * nblk + blk] = (nanflag > 0.0f) ? __builtin_nanf("") : s;
   const bool zero = !(s > 0.0f) || (nanflag > 0.0f);
   const bool fast = s >= 0x1p-125f;  // 1/s finite
@@ -280,7 +328,7 @@ __global__ __launch_bounds__(256) void quant_i8_kernel(const uint16_t* __restric
     for (int j = 0; j < 8; ++j) {
       uint32_t u = (uint32_t)w[j >> 1];
       float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
-      if (mean) a = a - mu[j];
+      if (use_mean) a = a - mu[j];
       int c = 0;
       if (!zero) {
         float qv = fast ? rne_quotient(a, s, y) : rintf(a / s);  // rne of the correctly rounded quotient
@@ -392,8 +440,19 @@ __global__ __launch_bounds__(256) void v_tiles_bf16_kernel(const uint16_t* __res
   }
 }
 
-// grid (nt, B*H), 256 threads.  One 64-row block of V: s_v = fl32(absmax/448),
-// codes E4M3(fl32(V/s_v)).  Writes the [N][D] codes (if codes != nullptr)
+// Exponent of the FP8 V block scale: the smallest e >= -127 with
+// absmax <= 448 * 2^e, decided on the bits (absmax = f 2^E, 448 = 1.75 2^8:
+// e = E - 8 when f <= 1.75, else E - 7; a subnormal absmax clamps to -127).
+__device__ __forceinline__ int v_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int e = (int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return max(e, -127);
+}
+
+// grid (nt, B*H), 256 threads.  One 64-row block of V: s_v = 2^e (0 for an
+// all-zero block), codes E4M3(V / s_v) (an exact product with 2^-e).  The
+// power of two is the block-scale form the FP8 matrix instruction applies
+// itself, as an E8M0 exponent.  Writes the [N][D] codes (if codes != nullptr)
 // and/or the attention tile layout [nt][D][64] with FP8 key positions
 // (if vt != nullptr, zero for keys >= N), and the scale.
 template <int D>
@@ -431,9 +490,12 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
     }
   }
   amax = block_max_256(amax, sh);
-  const float s = amax / 448.0f;
+  const int e = v_scale_exp(amax);
+  const bool zero = !(amax > 0.0f);
+  // 2^e (2^-127 is the subnormal 0x00400000) and 2^-e (at most 2^127)
+  const float s = zero ? 0.0f : __uint_as_float(e >= -126 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
   if (t == 0) scales[bh * nt + tt] = s;
-  const bool zero = !(s > 0.0f);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int r = r0 + rg + i * RPP;
@@ -443,7 +505,7 @@ __global__ __launch_bounds__(256) void quant_v_fp8_kernel(const uint16_t* __rest
       for (int j = 0; j < 8; ++j) {
         uint32_t u = (uint32_t)w[i][j >> 1];
         float a = bf16_bits_to_f32((j & 1) ? (u >> 16) : (u & 0xFFFFu));
-        uint32_t c = zero ? 0u : e4m3_encode_f32(a / s);
+        uint32_t c = zero ? 0u : e4m3_encode_f32(a * inv);
         packed[j >> 2] |= c << ((j & 3) * 8);
       }
       if (codes)
@@ -504,6 +566,85 @@ __global__ __launch_bounds__(256) void v_tiles_fp8_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Q-smoothing bias
+// ---------------------------------------------------------------------------
+
+// grid (nt, B*H), 256 threads: thread t owns key j = 64 tile + t % 64 and the
+// Q blocks b = t / 64 + 4 i.  For each (b, j) the bias of the logit in units
+// of sQ[b] sK[tile]:
+//   dS   = mu_b . K'_j, K'_j = fl32(K_j - kmean) (binary32): 16 FMA chains of
+//          8 channels each (channel order), summed pairwise
+//   beta = fl32(dS / fl32(sQ[b] sK[tile])), 0 when that product is 0
+// into bias[(bh nq + b) nt 64 + j], binary32 (0 for blocks whose mean row is
+// 0; keys past N repeat key N-1, as the attention kernels' K rows past N do,
+// so that the last tile's max over all 64 positions is a real score).  The
+// attention kernels add it to their scores in floating point.  The error of
+// beta, at most 14 u sum_c |mu_c K'_jc| / (sQ sK) units (u = 2^-24), is part
+// of what the oracle's smoothing width charges.
+template <int D>
+__global__ __launch_bounds__(256) void qbias_kernel(const uint16_t* __restrict__ k, Lay lk, int N,
+                                                    const float* __restrict__ kmean,
+                                                    const float* __restrict__ qmean,
+                                                    const float* __restrict__ sq,
+                                                    const float* __restrict__ sk, int nq,
+                                                    float* __restrict__ bias) {
+  constexpr int NB = 32;  // Q blocks staged in LDS at a time (8 per thread group)
+  __shared__ float mus[NB][D];
+  const long long bh = blockIdx.y;
+  const int tile = blockIdx.x, nt = gridDim.x;
+  const int t = threadIdx.x, jl = t & 63, grp = t >> 6;
+  const int j = tile * KT + jl;
+  float kp[D];
+  {
+    const uint16_t* kr = k + lay_row(lk, bh, min(j, N - 1));
+    const float* km = kmean + bh * D;
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+      const v4i w = *(const v4i*)(kr + c8 * 8);
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const uint32_t u = (uint32_t)w[h >> 1];
+        kp[c8 * 8 + h] = bf16_bits_to_f32((h & 1) ? (u >> 16) : (u & 0xFFFFu)) - km[c8 * 8 + h];
+      }
+    }
+  }
+  // (a key past N takes key N-1's bias, in units of its own tile's scale:
+  // the last tile holds both)
+  const float skt = sk[bh * nt + tile];
+  const long long row = (long long)nt * KT;
+  for (int b0 = 0; b0 < nq; b0 += NB) {
+    __syncthreads();
+    for (int i = t; i < NB * D / 4; i += 256) {
+      const int b = b0 + (4 * i) / D;
+      *(v4f*)&mus[(4 * i) / D][(4 * i) % D] =
+          b < nq ? *(const v4f*)(qmean + (bh * nq + b) * D + (4 * i) % D) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    __syncthreads();
+    for (int bi = grp; bi < NB && b0 + bi < nq; bi += 4) {
+      const int b = b0 + bi;
+      float part[D / 8];
+#pragma unroll
+      for (int g = 0; g < D / 8; ++g) {
+        const v4f m0 = *(const v4f*)&mus[bi][8 * g];
+        const v4f m1 = *(const v4f*)&mus[bi][8 * g + 4];
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = __builtin_fmaf(m0[c], kp[8 * g + c], acc);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = __builtin_fmaf(m1[c], kp[8 * g + 4 + c], acc);
+        part[g] = acc;
+      }
+#pragma unroll
+      for (int w = D / 16; w >= 1; w >>= 1)
+#pragma unroll
+        for (int g = 0; g < w; ++g) part[g] = part[2 * g] + part[2 * g + 1];
+      const float den = sq[bh * nq + b] * skt;
+      bias[(bh * nq + b) * row + j] = den != 0.0f ? part[0] / den : 0.0f;  // correctly rounded
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -539,8 +680,8 @@ void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64
     hipLaunchKernelGGL(kmean_finalize_kernel<64>, dim3(BH), dim3(64), 0, st, partial, S, N, mean);
 }
 
-void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
-                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm) {
+void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, float* mean,
+                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm, bool mean_blocks) {
   const bool norm = nm.r != nullptr;
   if (block == 1 && mean == nullptr) {  // one scale per row
     const int rpw = 256 / (d / 8);
@@ -549,7 +690,22 @@ void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int
     return;
   }
   int nb = (N + block - 1) / block;
-  SQ_DISPATCH_DN(d, norm, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, lx, N, block, mean, codes, scales, nm);
+  SQ_DISPATCH_DN(d, norm, quant_i8_kernel, dim3(nb, BH), dim3(256), st, x, lx, N, block, mean,
+                 mean_blocks ? 1 : 0, codes, scales, nm);
+}
+
+void launch_qmean(const uint16_t* q, const Lay& lq, int BH, int N, int d, int block, uint64_t* partial,
+                  float* mean, hipStream_t st) {
+  const int nq = (N + block - 1) / block;
+  SQ_DISPATCH_DN(d, false, kmean_partial_kernel, dim3(nq, BH), dim3(256), st, q, lq, N, block, partial,
+                 RowNorm{});
+  SQ_DISPATCH_D(d, qmean_finalize_kernel, dim3(nq, BH), dim3(d), st, partial, N, block, mean);
+}
+
+void launch_qbias(const uint16_t* k, const Lay& lk, int BH, int N, int d, const float* kmean, const float* qmean,
+                  const float* q_scale, const float* k_scale, int block, float* bias, hipStream_t st) {
+  const int nt = (N + KT - 1) / KT, nq = (N + block - 1) / block;
+  SQ_DISPATCH_D(d, qbias_kernel, dim3(nt, BH), dim3(256), st, k, lk, N, kmean, qmean, q_scale, k_scale, nq, bias);
 }
 
 void launch_v_tiles_bf16(const uint16_t* v, const Lay& lv, int BH, int N, int d, uint16_t* vt, hipStream_t st) {

@@ -87,6 +87,14 @@ typedef enum { SQATTN_OUT_FP32 = 0, SQATTN_OUT_BF16 = 1 } sqattn_out_dtype;
  * costs the attention kernel nothing and helps heavy-tailed Q most).  k_block: 64 (the attention tile;
  * default).  v_block: 64 (FP8 only; default).  out_dtype: SQATTN_OUT_FP32
  * (default) or SQATTN_OUT_BF16, the fp32 result rounded to nearest even.
+ * smooth_q: 0 (default) or 1, Q smoothing in the forward entry points (dense,
+ * without the q/k RMSNorm; q_block 64, 128 or 256): each Q block's exact
+ * per-channel mean is removed before the block is quantized and returns as an
+ * logit bias mu_b . K'_j in units of sQ sK (binary32), added to the scores
+ * (the outlier smoothing of the SageAttention2 title, GVCLab
+ * Video-Generation-101 systems survey, reference [3], applied to Q).  A block
+ * of equal rows (scale 0) is quantized plainly.  The attend entry points
+ * (already quantized Q) refuse it.
  * second_pass_count: NULL (default), or a device pointer to one uint32 that
  * the attention kernel increments (atomically, on the call's stream) once for
  * every work item -- one head's 256 query rows -- that took the rare exact-max
@@ -99,6 +107,7 @@ typedef struct sqattn_opts {
   int k_block;
   int v_block;
   int out_dtype;
+  int smooth_q;
   uint32_t* second_pass_count;
 } sqattn_opts;
 
@@ -158,7 +167,12 @@ int sqattn_quantize_qk_noalloc(const void* q, const void* k, int B, int H, int N
                                int8_t* k_i8, float* k_scale, float* k_mean, void* stream);
 
 /*
- * Quantize V to OCP E4M3 per block of v_block (= 64) rows.
+ * Quantize V to OCP E4M3 per block of v_block (= 64) rows (GVCLab research
+ * log 2026-09-02, section 5.5 table, SageAttention2 row: FP8 P.V).  The block
+ * scale is a power of two, s = 2^e with e the smallest integer >= -127 such
+ * that max|V| <= 448 s (0 for an all-zero block), and code = E4M3(V / s),
+ * rounded to nearest even: the E8M0 block-scale form the FP8 matrix
+ * instructions apply themselves.
  *   v       : bf16 [B,H,N,d];  v_fp8 : uint8 [B,H,N,d] codes;
  *   v_scale : float [B,H,ceil(N/v_block)].
  */
@@ -225,6 +239,11 @@ int sqattn_pack_v(const void* v, int B, int H, int N, int d, int pv_dtype, void*
  *   v        : [B,H,N,d] bf16 for SQATTN_PV_BF16; E4M3 codes (uint8) as
  *              written by sqattn_quantize_v_fp8 for SQATTN_PV_FP8_E4M3.
  *   v_scale  : [B,H,ceil(N/64)] from sqattn_quantize_v_fp8 for FP8; NULL for bf16.
+ *              The FP8 kernel applies each scale as its binary exponent (an
+ *              E8M0 scale of the matrix instruction): scales must be powers of
+ *              two in [2^-127, 2^127], or 0 with all-zero codes, as
+ *              sqattn_quantize_v_fp8 writes them; other values act as the
+ *              power of two at or below them.
  *   out      : [B,H,N,d], fp32 or bf16 as opts->out_dtype says.
  * V is first laid out in the kernel's tile layout (as sqattn_pack_v) in a
  * temporary of sqattn_packed_v_bytes() allocated and freed stream-ordered on

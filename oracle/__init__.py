@@ -14,6 +14,8 @@ paragraph; GVCLab research log 2026-09-02, section 5.5 table):
 
   quant.kmean_exact      per-channel K mean, exact sum rounded once
   quant.quantize_q       per-block INT8 codes + scales of Q
+  quant.quantize_q_smoothed  the same after removing each block's mean (Q
+                         smoothing, optional; the mean returns as a logit bias)
   quant.quantize_k       K smoothed by its mean, then per-block INT8
   quant.quantize_v_fp8   per-block E4M3 codes + scales of V (FP8 path)
   attention.attend_bf16  logits from the integer codes, exact softmax, P.V
@@ -44,23 +46,32 @@ __all__ = ["attention", "fp", "norm", "quant", "w8a8", "forward_head"]
 
 
 def forward_head(q_bits, k_bits, v_bits, rows, q_block, k_block, scale, pv="bf16",
-                 v_block=64, kv_tile=64, block_mask=None):
+                 v_block=64, kv_tile=64, block_mask=None, smooth_q=False):
     """Run every step for one head; returns a dict of all intermediate results.
 
     q_bits/k_bits/v_bits: uint16 bf16 bits [N, d]; rows: checked query rows;
-    block_mask: optional [ceil(N/128), ceil(N/64)] block-sparse mask."""
-    qc, qs = quant.quantize_q(q_bits, q_block)
+    block_mask: optional [ceil(N/128), ceil(N/64)] block-sparse mask;
+    smooth_q: Q smoothing per Q block (quant.quantize_q_smoothed)."""
+    qm = ks_ = None
+    if smooth_q:
+        qc, qs, qm = quant.quantize_q_smoothed(q_bits, q_block)
+    else:
+        qc, qs = quant.quantize_q(q_bits, q_block)
     kc, ks, mu = quant.quantize_k(k_bits, k_block)
     res = {"q_codes": qc, "q_scale": qs, "k_codes": kc, "k_scale": ks, "k_mean": mu}
+    if smooth_q:
+        ks_ = quant.smooth_k(k_bits, mu)
+        res["q_mean"] = qm
     if pv == "bf16":
         res["out"] = attention.attend_bf16(qc, qs, kc, ks, v_bits, rows, q_block, k_block, scale,
-                                           block_mask=block_mask)
+                                           block_mask=block_mask, q_mean=qm, k_smooth=ks_)
         res["envelope"] = None
     elif pv == "fp8":
         vc, vs = quant.quantize_v_fp8(v_bits, v_block)
         res["v_codes"], res["v_scale"] = vc, vs
         o, e, hits = attention.attend_fp8(qc, qs, kc, ks, vc, vs, rows, q_block, k_block, scale,
-                                          v_block=v_block, kv_tile=kv_tile, block_mask=block_mask)
+                                          v_block=v_block, kv_tile=kv_tile, block_mask=block_mask,
+                                          q_mean=qm, k_smooth=ks_)
         res["out"], res["envelope"], res["envelope_hits"] = o, e, hits
     else:
         raise ValueError(pv)

@@ -43,6 +43,17 @@ Readings where the pages are silent:
     the relative error of y is <= u (6.94 M_r + 21.4) < 2^-21 (M_r + 3).
     tests/test_oracle_fp8_envelope.py checks this bound against an exact
     evaluation of that binary32 chain on heavy-tailed data.
+  * Q smoothing (optional, quant.quantize_q_smoothed): the logits gain the
+    bias mu_b . K'_j of the row's Q block b, exact (float64 products of the
+    binary32 mean and smoothed K), times the softmax scale.  On the FP8 path
+    a kernel that takes the bias in units of sQ sK as a binary32 dot product
+    (16 FMA chains of 8 terms, summed pairwise) divided by fl32(sQ sK)
+    (correctly rounded), and adds it to the converted integer score with one
+    rounding, is off by at most 14 u A_j / (sQ sK) units (A_j =
+    sum_c |mu_c K'_jc|) plus u |S + bias|; times c that is at most
+    u (14 scale log2(e) A_j + M_r) in log2 units, and the envelope widens by
+    ln 2 u (16 scale log2(e) max_j A_j + 2 M_r) relative (smoothing_width).
+    The 16-bit path's tolerance covers a bias rounded to an integer.
 """
 from __future__ import annotations
 
@@ -51,7 +62,8 @@ import numpy as np
 from . import fp
 
 __all__ = ["int_scores", "logits", "softmax_pv", "attention_fp64", "attend_bf16",
-           "attend_fp8", "e4m3_round_f64", "envelope_width", "MASK_Q", "MASK_K", "key_mask"]
+           "attend_fp8", "e4m3_round_f64", "envelope_width", "MASK_Q", "MASK_K", "key_mask",
+           "smoothing_bias", "smoothing_width"]
 
 MASK_Q = 128   # query rows per block-mask row
 MASK_K = 64    # keys per block-mask column
@@ -92,14 +104,35 @@ def attention_fp64(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
     return softmax_pv(S, V)
 
 
+def smoothing_bias(q_mean, k_smooth, rows, q_block) -> np.ndarray:
+    """Delta S [R, N] = mu_b(r) . K'_j in float64: q_mean float32 [nq, d] (zero
+    rows for blocks quantized plainly), k_smooth float32 K' [N, d]."""
+    rows = np.asarray(rows, np.int64)
+    mu = np.asarray(q_mean, np.float32).astype(np.float64)[rows // q_block]
+    return mu @ np.asarray(k_smooth, np.float32).astype(np.float64).T
+
+
+def smoothing_width(q_mean, k_smooth, rows, q_block, scale, max_abs_logit_log2) -> np.ndarray:
+    """Extra relative FP8 envelope width per row [R, 1] for the Q-smoothing
+    bias computed as the module notes describe: ln 2 u (16 scale log2(e)
+    max_j A_j + 2 M_r), A_j = sum_c |mu_c K'_jc| of the row's block."""
+    rows = np.asarray(rows, np.int64)
+    u = 2.0 ** -24
+    mu = np.abs(np.asarray(q_mean, np.float32).astype(np.float64)[rows // q_block])
+    A = (mu @ np.abs(np.asarray(k_smooth, np.float32).astype(np.float64)).T).max(axis=1, keepdims=True)
+    M = np.asarray(max_abs_logit_log2, np.float64)
+    return np.log(2.0) * u * (16.0 * scale * np.log2(np.e) * A + 2.0 * M)
+
+
 def _bf16_to_f64(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_block, scale,
-                chunk: int = 256, block_mask=None) -> np.ndarray:
+                chunk: int = 256, block_mask=None, q_mean=None, k_smooth=None) -> np.ndarray:
     """Output rows O[rows] (float64 [R, d]) of the 16-bit P.V path for one head
-    (block_mask: optional [ceil(N/128), ceil(N/64)], nonzero = computed)."""
+    (block_mask: optional [ceil(N/128), ceil(N/64)], nonzero = computed;
+    q_mean/k_smooth: the Q-smoothing bias, see smoothing_bias)."""
     rows = np.asarray(rows, np.int64)
     N = k_codes.shape[0]
     sk = np.repeat(np.asarray(k_scale, np.float64), k_block)[:N]
@@ -109,6 +142,8 @@ def attend_bf16(q_codes, q_scale, k_codes, k_scale, v_bits, rows, q_block, k_blo
         r = rows[i:i + chunk]
         D = int_scores(q_codes[r], k_codes)
         S = logits(D, np.asarray(q_scale, np.float64)[r // q_block], sk, scale)
+        if q_mean is not None:
+            S = S + smoothing_bias(q_mean, k_smooth, r, q_block) * scale
         if block_mask is None:
             out[i:i + chunk] = softmax_pv(S, V)
             continue
@@ -145,7 +180,7 @@ def e4m3_round_f64(y: np.ndarray):
 
 def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_block, k_block,
                scale, v_block: int = 64, kv_tile: int = 64, eps_rel: float | None = None,
-               round_p=None, chunk: int = 128, block_mask=None):
+               round_p=None, chunk: int = 128, block_mask=None, q_mean=None, k_smooth=None):
     """FP8 P.V path for one head; returns (O [R, d], E [R, d], hits).
 
     ``round_p`` maps 448*P~ to the FP8 operand value (default: E4M3 rounding;
@@ -167,6 +202,8 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
         r = rows[i:i + chunk]
         S = logits(int_scores(q_codes[r], k_codes), np.asarray(q_scale, np.float64)[r // q_block],
                    sk, scale)
+        if q_mean is not None:
+            S = S + smoothing_bias(q_mean, k_smooth, r, q_block) * scale
         keep = np.ones(S.shape, bool) if block_mask is None else key_mask(block_mask, r, N)
         live = keep.any(axis=1, keepdims=True)
         Sk = np.where(keep, S, -np.inf)
@@ -189,7 +226,10 @@ def attend_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, rows, q_blo
         if round_p is None:
             if eps_rel is None:
                 # the largest |logit| among the keys the kernel evaluates (kept keys)
-                eps = envelope_width(np.where(keep, np.abs(S), 0.0).max(axis=1, keepdims=True) / np.log(2.0))
+                M = np.where(keep, np.abs(S), 0.0).max(axis=1, keepdims=True) / np.log(2.0)
+                eps = envelope_width(M)
+                if q_mean is not None:
+                    eps = eps + smoothing_width(q_mean, k_smooth, r, q_block, scale, M)
             else:
                 eps = eps_rel
             frac = c - np.floor(c)

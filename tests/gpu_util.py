@@ -23,7 +23,7 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def oracle_heads(q, k, v, rows, q_block, scale, pv, heads=None, workers=None):
+def oracle_heads(q, k, v, rows, q_block, scale, pv, heads=None, workers=None, smooth_q=False):
     """forward_head over the (b, h) heads; returns a list indexed by b*H + h."""
     B, H = q.shape[:2]
     idx = list(range(B * H)) if heads is None else list(heads)
@@ -31,7 +31,8 @@ def oracle_heads(q, k, v, rows, q_block, scale, pv, heads=None, workers=None):
 
     def one(i):
         b, h = divmod(i, H)
-        return oracle.forward_head(q[b, h], k[b, h], v[b, h], rows[i], q_block, 64, scale, pv=pv)
+        return oracle.forward_head(q[b, h], k[b, h], v[b, h], rows[i], q_block, 64, scale, pv=pv,
+                                   smooth_q=smooth_q)
 
     res = [None] * (B * H)
     with ThreadPoolExecutor(workers) as ex:

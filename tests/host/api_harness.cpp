@@ -10,10 +10,13 @@
 //     allocated (validation precedes every enqueue);
 //   * accepted arguments: every range lies inside one buffer the caller
 //     passed, the workspace, the static scratch or a stream-ordered
-//     allocation; writes never land in an input; writes of different
-//     launches into the workspace never overlap; every workspace or
-//     allocation byte a launch reads was written by an earlier launch of the
-//     same call; every allocation is freed, on the call's stream;
+//     allocation; writes never land in an input; within one launch no write
+//     overlaps a read of another range (an in-place update of the range it
+//     read is declared as such); a write over bytes an earlier launch wrote
+//     comes after some launch in between read them (no lost result); every
+//     workspace or allocation byte a launch reads was written by an earlier
+//     launch of the same call; every allocation is freed, on the call's
+//     stream;
 //   * the *_workspace_bytes functions: exactly that many bytes are accepted,
 //     one 256-byte step less is refused with SQATTN_ERR_WORKSPACE;
 //   * HIP errors forced from here (a failed allocation, a failed launch, a
@@ -26,6 +29,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -54,6 +58,7 @@ struct Access {
   Range r;
   bool write;
   int launch;
+  bool inplace;  // a write of exactly the range this launch read before
 };
 
 std::vector<Buffer> g_buf;
@@ -84,14 +89,14 @@ void failf(const std::string& msg) {
   std::fprintf(stderr, "FAIL [%s] %s\n", g_case.c_str(), msg.c_str());
 }
 
-void record(const char* who, const void* p, long double bytes, bool write) {
+void record(const char* who, const void* p, long double bytes, bool write, bool inplace = false) {
   if (bytes <= 0) return;
   if (!p) {
     failf(std::string(who) + ": null pointer with a nonzero extent");
     return;
   }
   const uintptr_t a = (uintptr_t)p;
-  g_acc.push_back({who, {a, a + (uintptr_t)bytes}, write, g_launches});
+  g_acc.push_back({who, {a, a + (uintptr_t)bytes}, write, g_launches, inplace});
 }
 
 // byte extent of the rows of a [BH, N, d] operand with layout l (element size es)
@@ -130,12 +135,26 @@ void verify() {
       continue;
     }
     if (x.write && b->kind == INPUT) failf(x.who + ": writes into input " + b->name);
+    if (x.write) {
+      // no read of another range in the same launch overlaps the write
+      for (const Access& y : g_acc)
+        if (!y.write && y.launch == x.launch && y.r.a < x.r.b && x.r.a < y.r.b &&
+            !(x.inplace && y.r.a == x.r.a && y.r.b == x.r.b))
+          failf(x.who + " overlaps " + y.who + " in the same launch (" + b->name + ")");
+      // a write over an earlier launch's result only after a launch in between read it
+      for (const Access& y : g_acc) {
+        if (!y.write || y.launch >= x.launch || !(y.r.a < x.r.b && x.r.a < y.r.b)) continue;
+        const uintptr_t ia = std::max(x.r.a, y.r.a), ib = std::min(x.r.b, y.r.b);
+        bool read = false;
+        for (const Access& z : g_acc)
+          if (!z.write && z.r.a < ib && ia < z.r.b &&
+              ((z.launch > y.launch && z.launch < x.launch) || (x.inplace && z.launch == x.launch)))
+            read = true;
+        if (!read) failf(x.who + " overwrites " + y.who + " before any launch read it (" + b->name + ")");
+      }
+    }
     if (b->kind == WORKSPACE || b->kind == ALLOC || b->kind == SCRATCH) {
-      if (x.write) {
-        for (const Access& y : g_acc)
-          if (y.write && y.launch != x.launch && y.r.a < x.r.b && x.r.a < y.r.b && owner(y.r) == b)
-            failf(x.who + " and " + y.who + ": overlapping writes in " + b->name);
-      } else {
+      if (!x.write) {
         // every byte read was written by an earlier launch: sweep the
         // earlier writes' union over [a, b)
         uintptr_t covered = x.r.a;
@@ -246,13 +265,40 @@ void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64
   launched(st);
 }
 
-void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, const float* mean,
-                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm) {
+void launch_quant_i8(const uint16_t* x, const Lay& lx, int BH, int N, int d, int block, float* mean,
+                     int8_t* codes, float* scales, hipStream_t st, const RowNorm& nm, bool mean_blocks) {
+  const long double nb = (N + block - 1) / block;
   record("quant_i8: x", x, lay_extent(lx, BH, N, d, 2), false);
   norm_reads("quant_i8: norm", nm, BH, N, lx.H, d);
-  if (mean) record("quant_i8: mean", mean, (long double)BH * d * 4, false);
+  if (mean) record("quant_i8: mean", mean, (long double)BH * (mean_blocks ? nb : 1) * d * 4, false);
   record("quant_i8: codes", codes, (long double)BH * N * d, true);
-  record("quant_i8: scales", scales, (long double)BH * ((N + block - 1) / block) * 4, true);
+  record("quant_i8: scales", scales, (long double)BH * nb * 4, true);
+  launched(st);
+  // the block means of Q smoothing are rewritten (0 for blocks kept plain):
+  // a write of the same launch, after its read
+  if (mean && mean_blocks) record("quant_i8: mean rows", mean, (long double)BH * nb * d * 4, true, true);
+}
+
+void launch_qmean(const uint16_t* q, const Lay& lq, int BH, int N, int d, int block, uint64_t* partial,
+                  float* mean, hipStream_t st) {
+  const long double nq = (N + block - 1) / block;
+  record("qmean: q", q, lay_extent(lq, BH, N, d, 2), false);
+  record("qmean: partial", partial, (long double)BH * nq * d * 32, true);
+  launched(st);
+  record("qmean finalize: partial", partial, (long double)BH * nq * d * 32, false);
+  record("qmean finalize: mean", mean, (long double)BH * nq * d * 4, true);
+  launched(st);
+}
+
+void launch_qbias(const uint16_t* k, const Lay& lk, int BH, int N, int d, const float* kmean, const float* qmean,
+                  const float* q_scale, const float* k_scale, int block, float* bias, hipStream_t st) {
+  const long double nq = (N + block - 1) / block, nt = (N + KT - 1) / KT;
+  record("qbias: k", k, lay_extent(lk, BH, N, d, 2), false);
+  record("qbias: kmean", kmean, (long double)BH * d * 4, false);
+  record("qbias: qmean", qmean, (long double)BH * nq * d * 4, false);
+  record("qbias: q scales", q_scale, (long double)BH * nq * 4, false);
+  record("qbias: k scales", k_scale, (long double)BH * nt * 4, false);
+  record("qbias: bias", bias, (long double)BH * nq * nt * KT * 4, true);
   launched(st);
 }
 
@@ -302,6 +348,11 @@ static hipError_t attention(const AttnParams& p, int d, bool fp8, hipStream_t st
   }
   record("attention: out", p.out, lay_extent(p.lo, p.BH, p.N, d, p.out_bf16 ? 2 : 4), true);
   if (p.second_pass) record("attention: counter", p.second_pass, 4, true);
+  if (p.qbias) {
+    if (p.mask) failf("attention: Q smoothing with a block mask");
+    if (p.q_block != 64 && p.q_block != 128 && p.q_block != 256) failf("attention: Q smoothing q_block");
+    record("attention: q bias", p.qbias, BH * p.nq * p.nt * KT * 4, false);
+  }
   launched(st);
   return hipSuccess;
 }
@@ -367,12 +418,13 @@ struct Attn {
   int q_block = 128;
   int out_dtype = SQATTN_OUT_FP32;
   bool counter = false;
+  int smooth = 0;
 };
 
 std::string label(const char* f, const Attn& a) {
   char s[160];
-  std::snprintf(s, sizeof s, "%s B=%d H=%d N=%d d=%d pv=%d q_block=%d out=%d", f, a.B, a.H, a.N, a.d, a.pv,
-                a.q_block, a.out_dtype);
+  std::snprintf(s, sizeof s, "%s B=%d H=%d N=%d d=%d pv=%d q_block=%d out=%d smooth=%d", f, a.B, a.H, a.N, a.d,
+                a.pv, a.q_block, a.out_dtype, a.smooth);
   return s;
 }
 
@@ -382,6 +434,7 @@ sqattn_opts opts_of(const Attn& a) {
   sqattn_opts o{};
   o.q_block = a.q_block;
   o.out_dtype = a.out_dtype;
+  o.smooth_q = a.smooth;
   if (a.counter) o.second_pass_count = (uint32_t*)buffer("counter", 4, OUTPUT);
   return o;
 }
@@ -610,6 +663,34 @@ void rejections() {
                     nullptr, "forward_ex opts");
     if (sqattn_workspace_bytes(1, 2, 300, 64, 0, &bad) != 0) failf("workspace_bytes of rejected opts is not 0");
   }
+  // Q smoothing: its q_block set, dense forward only, not on quantized Q
+  for (int qb : {1, 16, 32, 192}) {
+    bad = sqattn_opts{};
+    bad.q_block = qb;
+    bad.smooth_q = 1;
+    reset();
+    expect_rejected(sqattn_forward_ex(p, p, p, 1, 2, 300, 64, 0.1f, 0, p, p, (size_t)1 << 40, g_stream, &bad),
+                    SQATTN_ERR_UNSUPPORTED, "q_block 64, 128 or 256", "forward_ex smoothing q_block");
+  }
+  bad = sqattn_opts{};
+  bad.smooth_q = 2;
+  reset();
+  expect_rejected(sqattn_forward_ex(p, p, p, 1, 2, 300, 64, 0.1f, 0, p, p, (size_t)1 << 40, g_stream, &bad),
+                  SQATTN_ERR_INVALID_ARG, "smooth_q", "forward_ex smooth_q value");
+  bad = sqattn_opts{};
+  bad.smooth_q = 1;
+  reset();
+  expect_rejected(sqattn_forward_sparse(p, p, p, 1, 1, 300, 64, 0.1f, 0, (const uint8_t*)p, p, p, (size_t)1 << 40,
+                                        g_stream, &bad),
+                  SQATTN_ERR_UNSUPPORTED, "dense", "forward_sparse smoothing");
+  reset();
+  expect_rejected(sqattn_attend_packed((const int8_t*)p, (const float*)p, (const int8_t*)p, (const float*)p, p,
+                                       nullptr, 1, 1, 64, 64, 0.1f, 0, &bad, p, g_stream),
+                  SQATTN_ERR_UNSUPPORTED, "step of the forward", "attend_packed smoothing");
+  reset();
+  expect_rejected(sqattn_attend_quantized((const int8_t*)p, (const float*)p, (const int8_t*)p, (const float*)p, p,
+                                          nullptr, 1, 1, 64, 64, 0.1f, 0, &bad, p, g_stream),
+                  SQATTN_ERR_UNSUPPORTED, "step of the forward", "attend_quantized smoothing");
   bad = sqattn_opts{};
   bad.second_pass_count = (uint32_t*)((char*)p + 2);
   reset();
@@ -734,6 +815,12 @@ int main() {
           a.out_dtype = (N % 2) ? SQATTN_OUT_BF16 : SQATTN_OUT_FP32;
           a.counter = N == 300;
           forward_case(a, false);
+          if (qb == 128 || (qb != 1 && qb != 16 && N > 64)) {
+            Attn sm = a;
+            sm.smooth = 1;
+            sm.q_block = qb == 192 ? 256 : qb;
+            forward_case(sm, false);
+          }
           if (qb == 128) {
             forward_case(a, true);
             strided_case(a, false);

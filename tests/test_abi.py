@@ -80,7 +80,11 @@ def _err():
     (dict(opts=sq.Opts(24, 64, 64, 0)), INVALID, "q_block"),
     (dict(opts=sq.Opts(128, 64, 64, 2)), INVALID, "out_dtype"),
     (dict(opts=sq.Opts(128, 64, 64, -1)), INVALID, "out_dtype"),
-    (dict(opts=sq.Opts(128, 64, 64, 0, FAKE + 2)), INVALID, "second_pass_count"),
+    (dict(opts=sq.Opts(128, 64, 64, 0, 0, FAKE + 2)), INVALID, "second_pass_count"),
+    (dict(opts=sq.Opts(128, 64, 64, 0, 2)), INVALID, "smooth_q"),
+    (dict(opts=sq.Opts(16, 64, 64, 0, 1)), UNSUPPORTED, "Q smoothing"),
+    (dict(opts=sq.Opts(192, 64, 64, 0, 1)), UNSUPPORTED, "Q smoothing"),
+    (dict(opts=sq.Opts(1, 64, 64, 0, 1)), UNSUPPORTED, "Q smoothing"),
 ])
 def test_forward_validation(kw, code, needle):
     assert _fwd(**kw) == code

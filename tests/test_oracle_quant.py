@@ -174,26 +174,64 @@ def test_block_permutation_permutes_codes():
 
 # --------------------------------------------------------------------------- FP8 V
 
+def _check_pow2_scale(a, s, emin=-127):
+    """s = 2^e is the smallest power of two (>= 2^emin) with a <= 448 s,
+    checked in exact rationals."""
+    m, e = np.frexp(np.float64(s))
+    assert m == 0.5, s                                        # a power of two
+    e = int(e) - 1
+    a = Fraction(float(a))
+    assert a <= 448 * Fraction(2) ** e
+    assert e == emin or a > 448 * Fraction(2) ** (e - 1)
+
+
 def test_v_fp8_matches_ieee_and_torch():
     rng = np.random.default_rng(8)
-    vb = _bf16(rng.standard_normal((300, 64)))
+    # blocks of very different magnitude, including ones whose absmax sits
+    # on, just above and just below 448 times a power of two
+    x = rng.standard_normal((320, 64)) * np.exp2(rng.integers(-30, 30, size=5)).repeat(64)[:, None]
+    x[70, 3] = 448.0 * 2.0 ** 5
+    x[140, 9] = 448.0 * 2.0 ** -3 * (1 + 2.0 ** -7)
+    x[200, 1] = -448.0 * (1 - 2.0 ** -8)
+    vb = _bf16(x)
     vc, vs = quant.quantize_v_fp8(vb, 64)
     x = _f(vb)
     for i in range(vs.size):
-        _nearest(Fraction(float(np.abs(x[i * 64:(i + 1) * 64]).max())) / 448, vs[i])
-    srow = np.repeat(vs, 64)[:300][:, None]
-    y = x / srow                                              # host IEEE division
+        _check_pow2_scale(np.abs(x[i * 64:(i + 1) * 64]).max(), vs[i])
+    srow = np.repeat(vs, 64)[:320][:, None]
+    y = x / srow                                              # host IEEE division (exact: a power of two)
     ref = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(vc, ref)
-    # the absmax element of each block becomes +-448 exactly
+    # the absmax element of each block lands in the top binade of E4M3:
+    # (224, 448], codes 0x77 .. 0x7E by magnitude (0x76 = 224 itself when it
+    # rounds down)
     for i in range(vs.size):
         blk = np.abs(x[i * 64:(i + 1) * 64])
         j = np.unravel_index(blk.argmax(), blk.shape)
-        assert vc[i * 64 + j[0], j[1]] & 0x7F == 0x7E
+        assert 0x76 <= (vc[i * 64 + j[0], j[1]] & 0x7F) <= 0x7E
     # reconstruction within half an E4M3 step (relative 2^-4) or half the subnormal step
     deq = fp.e4m3_decode(vc) * srow
     tol = np.maximum(np.abs(x) * 2.0 ** -4, srow * 2.0 ** -10)
     assert np.all(np.abs(deq - x) <= tol * (1 + 1e-6))
+
+
+def test_v_fp8_scale_edges():
+    # absmax exactly 448 * 2^e gives 2^e (code 448), one bf16 step above gives
+    # 2^(e+1); blocks too small for 2^-127 clamp there
+    for e in (-20, 0, 7):
+        for bump, want in ((0, e), (1, e + 1)):
+            a = np.float32(448.0 * 2.0 ** e)
+            bits = (np.array([a], np.float32).view(np.uint32) >> 16).astype(np.uint16) + bump
+            vb = np.zeros((64, 8), np.uint16)
+            vb[5, 2] = bits[0]
+            vc, vs = quant.quantize_v_fp8(vb, 64)
+            assert vs[0] == np.float32(2.0 ** want), (e, bump, vs)
+            assert vc[5, 2] == (0x7E if bump == 0 else 0x76)   # 448, or 448.x / 2 rounded to 224
+    tiny = np.zeros((64, 8), np.uint16)
+    tiny[0, 0] = 0x0001                                         # smallest bf16 subnormal, 2^-133
+    vc, vs = quant.quantize_v_fp8(tiny, 64)
+    assert vs[0] == np.float32(2.0 ** -127)
+    _check_pow2_scale(2.0 ** -133, vs[0])
 
 
 def test_v_fp8_zero_block():

@@ -185,6 +185,18 @@ def gen_inputs(w: Workload, N: int | None = None, d: int | None = None, B: int |
     return q, k, v, rows
 
 
+def add_channel_offset(x_bits: np.ndarray, sigma: float, seed: int) -> np.ndarray:
+    """x + o for uint16 bf16 bits x [..., N, d]: one offset vector o ~ N(0,
+    sigma^2) per head (leading index), the same for every row, rounded back
+    to bf16 -- the per-channel outliers of Q that Q smoothing targets (K gets
+    such an offset in every workload already)."""
+    x_bits = np.asarray(x_bits, np.uint16)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    lead = x_bits.shape[:-2]
+    off = g.normal(0.0, sigma, lead + (1, x_bits.shape[-1]))
+    return f32_to_bf16_bits((bf16_bits_to_f32(x_bits).astype(np.float64) + off).astype(np.float32))
+
+
 def gen_block_mask(B: int, H: int, N: int, density: float, seed: int, band: int = 2) -> np.ndarray:
     """A block-sparse mask uint8 [B, H, ceil(N/128), ceil(N/64)] for 128-row
     query blocks x 64-key tiles: every query block keeps the key tiles within
