@@ -29,6 +29,8 @@ _PV = {"bf16": PV_BF16, "fp8": PV_FP8, PV_BF16: PV_BF16, PV_FP8: PV_FP8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsqattn.so")
+# the checking build (include/sqattn_debug.h): same C-ABI, for tests
+debug_lib_path = os.path.join(_HERE, "libsqattn_debug.so")
 
 _c = ctypes
 _vp, _i, _f, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
@@ -87,19 +89,24 @@ class SqattnError(RuntimeError):
 _lib = None
 
 
+def load_library(path: str):
+    """A ctypes.CDLL of a libsqattn build at `path` with the C-ABI's argument
+    and result types set (the binding's own library is lib())."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_quantized_attention_block_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     """The loaded libsqattn (ctypes.CDLL).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(lib_path):
-            raise RuntimeError(f"{lib_path} is missing: build it with "
-                               "`python -m bit_quantized_attention_block_amd.build`")
-        L = ctypes.CDLL(lib_path)
-        for name, (res, args) in EXPORTS.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load_library(lib_path)
     return _lib
 
 

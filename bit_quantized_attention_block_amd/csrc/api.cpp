@@ -1,6 +1,9 @@
 // C-ABI of the sqattn library: argument validation, workspace layout and the
 // launch sequence of each entry point.  See include/sqattn.h for the contract.
 #include "../../include/sqattn.h"
+#ifdef SQATTN_DEBUG
+#include "../../include/sqattn_debug.h"
+#endif
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -144,6 +147,12 @@ int hip_check(const char* what) {
 // (w % 8) * per_xcd + w / 8, so each XCD walks consecutive query blocks of the
 // same head, which share K/V tiles through that XCD's L2.
 int launch_attention(sqattn::AttnParams p, int d, int pv, hipStream_t st, const char* what) {
+#ifdef SQATTN_DEBUG
+  {
+    const hipError_t e = sqattn::debug_word(&p.debug);
+    if (e != hipSuccess) return fail(SQATTN_ERR_HIP, std::string(what) + ": violation word: " + hipGetErrorString(e));
+  }
+#endif
   p.qtiles = (p.N + sqattn::ATT_QWG - 1) / sqattn::ATT_QWG;
   const long long W = (long long)p.BH * p.qtiles;
   p.per_xcd = (int)((W + 7) / 8);
@@ -237,6 +246,18 @@ size_t w8a8_scale_bytes(long long rows, long long K) { return (size_t)(((rows + 
 extern "C" {
 
 int sqattn_version(void) { return SQATTN_VERSION; }
+
+#ifdef SQATTN_DEBUG
+uint32_t sqattn_debug_violations(void) {
+  uint32_t* w = nullptr;
+  uint32_t v = 0xFFFFFFFFu;
+  if (sqattn::debug_word(&w) != hipSuccess) return v;
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&v, w, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(w, 0, 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return 0xFFFFFFFFu;
+  return v;
+}
+#endif
 
 const char* sqattn_status_string(int s) {
   switch (s) {

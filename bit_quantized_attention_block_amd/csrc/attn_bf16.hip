@@ -128,6 +128,7 @@ struct Ctx {
   uint32_t qboff;         // SM: this lane's byte offset in them (block lane / 16, 4 keys)
   uint32_t qbw;           // SM: byte offset of this wave's block in an entry's bias area
   long long qbg;          // SM: byte offset of this wave's block row from qbh (global)
+  uint32_t* dbg;          // checking build: the violation word (else null)
   int N, nt, lane, wave, g, lr;
   uint32_t kad[G::NCH];   // per-lane LDS byte offsets of the K operands (k-step ch, half 0)
   uint32_t vad[4];        // ... of the V^T operands (16-key k-step ks, channel block 0)
@@ -194,6 +195,9 @@ struct Ctx {
   };
   __device__ __forceinline__ Refill refill(int j) const {
     const int tk = tile_at(j + 1), tv = tile_at(j);
+    SQ_CHECK(dbg, tk >= 0 && tk < nt, 0);
+    SQ_CHECK(dbg, tv >= 0 && tv < nt, 1);
+    SQ_CHECK(dbg, N - 1 - tk * KT >= 0, 2);  // the last K row read exists
     return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, skh + tk,
                   SM ? qbh + (long long)tk * KT * 4 : nullptr, (uint32_t)(min(N - 1 - tk * KT, KT) * D),
                   j % NSLOT};
@@ -228,10 +232,15 @@ struct Ctx {
   // touches before both wave groups have passed that phase.
   __device__ __forceinline__ void phase_bar() const {
     __builtin_amdgcn_sched_barrier(0);
+#ifdef SQATTN_DEBUG
+    // checking build: every load in flight lands before every barrier
+    __builtin_amdgcn_s_waitcnt(0);
+#else
     if (wave == 0 || (SM && wave == 1))
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (G::PER + 1)));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::PER));
+#endif
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -444,6 +453,7 @@ struct Ctx {
     float mx = -__builtin_inff();
     for (int j = 0; j < npos; ++j) {
       const int t = tile_at(j);
+      SQ_CHECK(dbg, t >= 0 && t < nt, 4);
       __syncthreads();
       const int kmax = N - 1 - t * KT;
       for (int u = wave; u < G::KCH; u += WAVES) {
@@ -508,6 +518,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
   C.kh = (const uint8_t*)p.k + hoff;
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
+  C.dbg = p.debug;
   if constexpr (SM) {
     // blocks of q_block (64, 128 or 256) rows: the work-group's first block
     // and this wave's (a wave whose rows all lie past N takes the last
@@ -540,6 +551,7 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
     const uint8_t* m0 = p.mask + ((long long)bh * p.mq + 2 * qt) * p.nt;
     const uint8_t* m1 = (2 * qt + 1 < p.mq) ? m0 + p.nt : nullptr;
     npos = build_tile_list(m0, m1, p.nt, list, list + SP_MAXT, NTHR);
+    SQ_CHECK(p.debug, npos >= 0 && npos <= SP_MAXT, 3);
     C.list = list;
     C.cnt = npos;
     C.has_m = false;

@@ -128,6 +128,7 @@ struct Ctx {
   uint32_t qboff;         // SM: this lane's byte offset in them (block lane / 16, 4 keys)
   uint32_t qbw;           // SM: byte offset of this wave's block in a slot's bias area
   long long qbg;          // SM: byte offset of this wave's block row from qbh (global)
+  uint32_t* dbg;          // checking build: the violation word (else null)
   int N, nt, lane, wave, g, lr;
   uint32_t kbase, vbase;  // per-lane LDS operand offsets (slot 0)
   float cq;               // sQ(row) * scale * log2(e)
@@ -167,6 +168,9 @@ struct Ctx {
     uint32_t klim;
   };
   __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) const {
+    SQ_CHECK(dbg, tk >= 0 && tk < nt, 0);
+    SQ_CHECK(dbg, tv >= 0 && tv < nt, 1);
+    SQ_CHECK(dbg, N - 1 - tk * KT >= 0, 2);  // the last K row read exists
     return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, tv, ks, vs,
                   (uint32_t)(min(N - 1 - tk * KT, KT) * D)};
   }
@@ -393,6 +397,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   C.vth = (const uint8_t*)p.vt + (long long)bh * p.nt * G::VBYTES;
   C.skh = p.sk + (long long)bh * p.nt;
   C.svh = p.sv + (long long)bh * p.nt;
+  C.dbg = p.debug;
   if constexpr (SM) {
     // blocks of q_block (64, 128 or 256) rows: the work-group's first block
     // and this wave's; lane l of the bias load reads block b0 + l / 16 (the
@@ -433,6 +438,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     const uint8_t* m0 = p.mask + ((long long)bh * p.mq + 2 * qt) * nt;
     const uint8_t* m1 = (2 * qt + 1 < p.mq) ? m0 + nt : nullptr;
     npos = build_tile_list(m0, m1, nt, list, list + SP_MAXT, NTHR);
+    SQ_CHECK(p.debug, npos >= 0 && npos <= SP_MAXT, 3);
   }
   auto tile_at = [&](int j) { return SP ? (list[min(j, npos - 1)] & 0xFFFFFF) : min(j, nt - 1); };
   auto kept = [&](int j) { return SP ? ((list[j] >> (24 + (C.wave >> 2))) & 1) != 0 : true; };
@@ -473,7 +479,11 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     // a plain barrier (the "memory" clobber keeps every memory access on its
     // side).  __syncthreads() would add a fence that waits for every
     // direct-to-LDS load in flight, which defeats the ring.
+#ifdef SQATTN_DEBUG
+    __builtin_amdgcn_s_waitcnt(0);  // checking build: every load in flight lands first
+#else
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB) & ~0x0F00);  // and lgkmcnt(0)
+#endif
     asm volatile("s_barrier" ::: "memory");
     rf = C.refill(tile_at(t + 5), (t + 1) & (NSLOT - 1), tile_at(t + 3), (t - 1) & (NSLOT - 1));
     c = c_next;

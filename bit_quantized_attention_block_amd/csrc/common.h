@@ -8,6 +8,20 @@
 
 namespace sqattn {
 
+// Index checks of the checking build (SQATTN_DEBUG): a failed condition sets
+// bit `bit` of the violation word (a vector atomic); nothing in the release
+// build.
+#ifdef SQATTN_DEBUG
+#define SQ_CHECK(word, cond, bit)                                  \
+  do {                                                             \
+    if ((word) != nullptr && !(cond)) atomicOr((word), 1u << (bit)); \
+  } while (0)
+#else
+#define SQ_CHECK(word, cond, bit) \
+  do {                            \
+  } while (0)
+#endif
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));

@@ -62,6 +62,11 @@ inline int kmean_chunks(int BH, int N) {
 // device (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch(void** ptr);
+#ifdef SQATTN_DEBUG
+// checking build: the device address of the kernels' violation word (one
+// 32-bit word per device, bits set by failed index checks)
+hipError_t debug_word(uint32_t** ptr);
+#endif
 void launch_kmean(const uint16_t* k, const Lay& lk, int BH, int N, int d, uint64_t* partial, float* mean,
                   hipStream_t st, const RowNorm& nm = RowNorm{});
 // mean: null (plain), one row per head (K smoothing), or with mean_blocks one
@@ -99,6 +104,9 @@ struct AttnParams {
   // Q smoothing: null, or the logit bias [BH][nq][nt * 64] of every (Q block,
   // key) in units of sQ sK, binary32 (q_block 64, 128 or 256; dense only)
   const float* qbias;
+  // checking build (SQATTN_DEBUG): the device word the kernels set bits of on
+  // an index check that fails; null otherwise
+  uint32_t* debug;
 };
 
 // 16-bit P.V kernel; p.qtiles and p.per_xcd must be set.  Returns the status

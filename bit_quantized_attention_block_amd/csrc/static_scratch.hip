@@ -37,4 +37,27 @@ hipError_t static_scratch(void** ptr) {
   return hipSuccess;
 }
 
+#ifdef SQATTN_DEBUG
+static __device__ __align__(256) uint32_t violations[64];
+
+hipError_t debug_word(uint32_t** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(violations));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = (uint32_t*)addr[dev];
+  return hipSuccess;
+}
+#endif
+
 }  // namespace sqattn

@@ -39,6 +39,23 @@ def test_library_loads_and_exports_every_declared_function():
     assert sq.version() == 10100
 
 
+def test_checking_build_exports_the_same_calls_and_its_own():
+    # libsqattn_debug.so: every call of include/sqattn.h plus the one of
+    # include/sqattn_debug.h
+    dbg = os.path.join(ROOT, "include", "sqattn_debug.h")
+    txt = re.sub(r"/\*.*?\*/", "", open(dbg).read(), flags=re.S)
+    extra = sorted(set(re.findall(r"\b(sqattn_[a-z0-9_]+)\s*\(", txt)))
+    assert extra == ["sqattn_debug_violations"]
+    nm = subprocess.run(["nm", "-D", "--defined-only", sq.debug_lib_path], capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    for n in declared() + extra:
+        assert n in syms, n
+    rel = subprocess.run(["nm", "-D", "--defined-only", sq.lib_path], capture_output=True, text=True).stdout
+    assert "sqattn_debug_violations" not in rel
+    L = sq.load_library(sq.debug_lib_path)
+    assert L.sqattn_version() == sq.version()
+
+
 def test_status_strings():
     L = sq.lib()
     for s in range(6):
