@@ -349,7 +349,9 @@ struct Ctx {
     const int j = i - NK;
     return *(const v4i*)(e + vad[j / G::NCB] + (j % G::NCB) * 32 * 128);
   }
-  static constexpr int RD = 4;  // operand reads in flight ahead of their MFMA
+  // operand reads in flight ahead of their MFMA (3 measured 2-3% faster than
+  // 2 or 4 on wan14b-480p; 5 spills)
+  static constexpr int RD = 3;
   v4i pre[RD];                  // M(t)'s first operands, read at the end of V(t)
   template <bool QK>
   __device__ __forceinline__ void prefetch(int t) {

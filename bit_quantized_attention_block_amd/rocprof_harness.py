@@ -149,7 +149,7 @@ def collect(workload: str, outdir: str, reps: int) -> int:
     os.makedirs(outdir, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
     passes = [("trace", ["--kernel-trace", "--stats"], 300)]
-    passes += [(n, ["--pmc", *c], 120) for n, c in COUNTER_PASSES.items()]
+    passes += [(n, ["--pmc", *c], 240) for n, c in COUNTER_PASSES.items()]
     commands = {}
     for name, args, limit in passes:
         cmd = _rocprof(args, outdir, name, workload, reps, limit)
