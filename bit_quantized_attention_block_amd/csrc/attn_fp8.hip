@@ -295,35 +295,50 @@ struct Ctx {
     const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
     const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
 
-    // running max of tile t (SM: of the biased binary32 scores; the bias of
-    // tile t > 0 sits in V slot t - 1, landed at boundary t - 1)
+    // Plain scores: the next tile's score MFMAs, then P.V of the previous
+    // tile (relative to m(t-1) = m) into O and the rest of the refill, and
+    // only then the running max of tile t, so that its vector work runs under
+    // the matrix instructions (measured about 2.5% faster than max, P.V,
+    // scores).  SM (biased binary32 scores; the bias of tile t > 0 sits in V
+    // slot t - 1, landed at boundary t - 1, while this iteration's refill
+    // writes V slot t - 2): max, P.V, scores, since the other order needs
+    // more registers than the wave has there.
     float mn;
-    if constexpr (SM) {
-      if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NSLOT - 1)) * G::VS + G::VQB + qbw);
-      mn = __builtin_fmaxf(m, tile_max_f(sc) * c);
-    } else {
-      mn = __builtin_fmaxf(m, (float)(tile_max(sc) - SQ_MAGIC) * c);  // c >= 0
-    }
-    if constexpr (SP) mn = act ? mn : m;
-
-    // P.V of the previous tile (relative to m(t-1) = m) into O
-    pv(va, pprev, sve, &rf);
-    // scores of the next tile
-    if constexpr (QK) {
+    auto running_max = [&]() {
+      if constexpr (SM) {
+        if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NSLOT - 1)) * G::VS + G::VQB + qbw);
+        mn = __builtin_fmaxf(m, tile_max_f(sc) * c);
+      } else {
+        mn = __builtin_fmaxf(m, (float)(tile_max(sc) - SQ_MAGIC) * c);  // c >= 0
+      }
+      if constexpr (SP) mn = act ? mn : m;
+    };
+    auto scores = [&]() {
+      if constexpr (QK) {
 #pragma unroll
-      for (int ch = 0; ch < G::NCH; ++ch)
+        for (int ch = 0; ch < G::NCH; ++ch)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const v4i a = *(const v4i*)(lds + ka + kb * 32 * G::KROW + ch * 32);
-          if (ch == 0) {
-            sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], magic, 0, 0, 0);
-          } else {
-            sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], sn[kb], 0, 0, 0);
+          for (int kb = 0; kb < 2; ++kb) {
+            const v4i a = *(const v4i*)(lds + ka + kb * 32 * G::KROW + ch * 32);
+            if (ch == 0) {
+              sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], magic, 0, 0, 0);
+            } else {
+              sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[ch], sn[kb], 0, 0, 0);
+            }
           }
-        }
+      }
+    };
+    if constexpr (SM) {
+      running_max();
+      pv(va, pprev, sve, &rf);
+      scores();
+    } else {
+      scores();
+      pv(va, pprev, sve, &rf);
     }
 #pragma unroll
     for (int i = G::NCB; i < G::LPB; ++i) load_part(rf, i);
+    if constexpr (!SM) running_max();
 
     // O and l follow the max: rescale when it moved for some row of the
     // wave (always on the first tile, where m = -inf and O = l = 0)
