@@ -59,10 +59,10 @@ W8A8_SRC = os.path.join(CSRC, "w8a8.hip")
 W8A8_KERNEL = "w8a8_gemm_kernel"
 
 
-def _traffic(name, src):
-    """Per-launch HBM bytes of the workload's profiled kernel from the
-    committed counter summary, or None if absent or taken on another version
-    of the kernel source or of a header it includes."""
+def _profiled(name, src):
+    """The committed counter summary of the workload's profiled kernel, or
+    None if absent or taken on another version of the kernel source or of a
+    header it includes."""
     from bit_quantized_attention_block_amd.rocprof_harness import source_key
     try:
         with open(TRAFFIC_FILE) as f:
@@ -71,7 +71,25 @@ def _traffic(name, src):
         return None
     if not t or t.get("src_key") != source_key(src):
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def _traffic(name, src):
+    """Per-launch HBM bytes of the workload's profiled kernel (see _profiled)."""
+    t = _profiled(name, src)
+    return t.get("bytes_per_launch") if t else None
+
+
+def _at_profiled_clock(roof, name, src):
+    """Adds the sustained shader clock of the profiled run (GRBM cycles per
+    XCD over the kernel time) and the roofline fractions against the peaks
+    scaled to that clock (the quoted peaks assume 2.4 GHz)."""
+    t = _profiled(name, src)
+    clk = t.get("sustained_clock_ghz") if t else None
+    roof["profiled_clock_ghz"] = round(clk, 4) if clk else None
+    roof["frac_at_profiled_clock"] = round(roof["frac"] * 2.4 / clk, 4) if clk else None
+    roof["frac_mixed_at_profiled_clock"] = round(roof["frac_mixed"] * 2.4 / clk, 4) if clk else None
+    return roof
 
 
 def mixed_peak(pv):
@@ -335,11 +353,12 @@ def bench_w8a8(a):
                                  "gemm_kernel_min": round(k_min, 4), "quantize_x": round(q_ms, 4),
                                  "rmsnorm_quantize_x": round(n_ms, 4), "layernorm_quantize_x": round(l_ms, 4)},
                    "rmsnorm": bool(a.rmsnorm), "layernorm": bool(a.layernorm)},
-        "roofline": {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
-                     "peak_mixed": INT8_PEAK_TOPS, "frac_mixed": round(k_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
-                     "ops_per_launch": w.ops},
+        "roofline": _at_profiled_clock(
+            {"kernel": W8A8_KERNEL, "bound": "mfma", "achieved": round(k_tops, 2),
+             "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+             "peak_mixed": INT8_PEAK_TOPS, "frac_mixed": round(k_tops / INT8_PEAK_TOPS, 4),
+             "traffic": _traffic(w.name, W8A8_SRC), "avg_launch_ms": round(k_ms, 4),
+             "ops_per_launch": w.ops}, w.name, W8A8_SRC),
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -698,12 +717,14 @@ def main(argv=None):
                    "stages_ms": {"forward_median": round(ms_med, 4), "forward_min": round(ms_min, 4),
                                  "attention_kernel": round(k_ms, 4), "attention_kernel_median": round(k_med, 4),
                                  "attention_kernel_min": round(k_min, 4), "quantize_and_pack": round(p_ms, 4)}},
-        "roofline": {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
-                     "peak_mixed": round(mixed_peak(w.pv), 2),
-                     "frac_mixed": round(k_tops / mixed_peak(w.pv), 4),
-                     "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
-                     "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
+        "roofline": _at_profiled_clock(
+            {"kernel": ATTN_KERNEL[w.pv], "bound": "mfma", "achieved": round(k_tops, 2),
+             "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(k_tops / INT8_PEAK_TOPS, 4),
+             "peak_mixed": round(mixed_peak(w.pv), 2),
+             "frac_mixed": round(k_tops / mixed_peak(w.pv), 4),
+             "traffic": _traffic(w.name, ATTN_SRC[w.pv]) if M is None else None,
+             "avg_launch_ms": round(k_ms, 4), "ops_per_launch": ops},
+            w.name if M is None else "", ATTN_SRC[w.pv]),
     }
     if a.smooth_q:
         res["config"]["smooth_q"] = {

@@ -142,6 +142,13 @@ int hip_check(const char* what) {
   return SQATTN_OK;
 }
 
+// Status of a W8A8 GEMM launch: the one-time attribute setup, then the launch.
+int gemm_status(hipError_t attr, const char* what) {
+  if (attr != hipSuccess)
+    return fail(SQATTN_ERR_HIP, std::string(what) + ": setting the GEMM kernel's LDS size: " + hipGetErrorString(attr));
+  return hip_check(what);
+}
+
 // The attention kernel of the P.V type.  A work item is (head, 256-row query
 // block); work-group w runs on XCD w % 8 (round-robin dispatch) and takes item
 // (w % 8) * per_xcd + w / 8, so each XCD walks consecutive query blocks of the
@@ -705,9 +712,9 @@ int sqattn_w8a8_gemm(const int8_t* x_codes, const float* x_scales, const int8_t*
       (s = check_ptr(out, "out", 16)))
     return s;
   if (bias && (s = check_ptr(bias, "bias", 4))) return s;
-  sqattn::launch_w8a8_gemm(x_codes, x_scales, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16,
-                           (hipStream_t)stream);
-  return hip_check("sqattn_w8a8_gemm launch");
+  return gemm_status(sqattn::launch_w8a8_gemm(x_codes, x_scales, w_codes, w_scales, bias, M, N, K, out,
+                                              out_dtype == SQATTN_OUT_BF16, (hipStream_t)stream),
+                     "sqattn_w8a8_gemm launch");
 }
 
 size_t sqattn_w8a8_workspace_bytes(int M, int K) {
@@ -738,8 +745,9 @@ int sqattn_w8a8_linear(const void* x, const int8_t* w_codes, const float* w_scal
   int8_t* xc = ws.at<int8_t>(0);
   float* xs = ws.at<float>(codes_bytes);
   sqattn::launch_w8a8_quant((const uint16_t*)x, M, K, xc, xs, st);
-  sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st);
-  return hip_check("sqattn_w8a8_linear launch");
+  return gemm_status(
+      sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st),
+      "sqattn_w8a8_linear launch");
 }
 
 int sqattn_w8a8_rmsnorm_quantize(const void* x, const float* gamma, float eps, int rows, int cols, int8_t* codes,
@@ -790,8 +798,9 @@ int sqattn_w8a8_linear_rmsnorm(const void* x, const float* gamma, float eps, con
   float* xs = ws.at<float>(cb);
   float* r = ws.at<float>(cb + sb);
   sqattn::launch_w8a8_rmsnorm_quant((const uint16_t*)x, gamma, eps, M, K, xc, xs, r, st);
-  sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st);
-  return hip_check("sqattn_w8a8_linear_rmsnorm launch");
+  return gemm_status(
+      sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st),
+      "sqattn_w8a8_linear_rmsnorm launch");
 }
 
 int sqattn_w8a8_layernorm_quantize(const void* x, const float* gamma, const float* beta, float eps, int rows,
@@ -845,8 +854,9 @@ int sqattn_w8a8_linear_layernorm(const void* x, const float* gamma, const float*
   float* mu = ws.at<float>(cb + sb);
   float* r = ws.at<float>(cb + sb + rb);
   sqattn::launch_w8a8_layernorm_quant((const uint16_t*)x, gamma, beta, eps, M, K, xc, xs, mu, r, st);
-  sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st);
-  return hip_check("sqattn_w8a8_linear_layernorm launch");
+  return gemm_status(
+      sqattn::launch_w8a8_gemm(xc, xs, w_codes, w_scales, bias, M, N, K, out, out_dtype == SQATTN_OUT_BF16, st),
+      "sqattn_w8a8_linear_layernorm launch");
 }
 
 }  // extern "C"

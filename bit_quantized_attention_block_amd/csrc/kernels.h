@@ -136,7 +136,9 @@ void launch_w8a8_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps,
 // LayerNorm (mean, rstd per row) fused with the block quantization
 void launch_w8a8_layernorm_quant(const uint16_t* x, const float* gamma, const float* beta, float eps, int R, int C,
                                  int8_t* codes, float* scales, float* mean, float* rstd, hipStream_t st);
-void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
-                      int M, int N, int K, void* out, int out_bf16, hipStream_t st);
+// Returns the status of the one-time kernel attribute setup (launch errors
+// surface through hipGetLastError as usual).
+hipError_t launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
+                            int M, int N, int K, void* out, int out_bf16, hipStream_t st);
 
 }  // namespace sqattn

@@ -24,6 +24,8 @@
 //       padded rows) with direct-to-LDS loads one slice ahead.  Work-groups
 //       are numbered so that each XCD walks a compact 8 x 4 patch of output
 //       tiles that shares x and W slices in its L2.
+#include <mutex>
+
 #include "common.h"
 #include "exact.h"
 #include "kernels.h"
@@ -342,8 +344,8 @@ void launch_w8a8_layernorm_quant(const uint16_t* x, const float* gamma, const fl
                      scales, rstd, gamma, mean, beta);
 }
 
-void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
-                      int M, int N, int K, void* out, int out_bf16, hipStream_t st) {
+hipError_t launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
+                            int M, int N, int K, void* out, int out_bf16, hipStream_t st) {
   GemmParams p;
   p.x = x;
   p.sx = sx;
@@ -360,12 +362,15 @@ void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const f
   const long long tiles = (long long)p.mt * p.nt;
   p.per_xcd = (int)((tiles + 7) / 8);
   p.out_bf16 = out_bf16;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)w8a8_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    attr = true;
-  }
+  // the attribute is per kernel: set once per process (the first status is kept)
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)w8a8_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  });
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(w8a8_gemm_kernel, dim3(8 * p.per_xcd), dim3(NTHR), LDS_BYTES, st, p);
+  return hipSuccess;
 }
 
 }  // namespace sqattn

@@ -70,6 +70,9 @@ def spec(workload: str) -> dict:
     return {"w": w, "kind": "attn", "kernel": ATTN_KERNEL[w.pv], "src": ATTN_SRC[w.pv], "ops": w.ops,
             "ops_text": "4 B H N^2 d", "title": f"{w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})"}
 COPY_BYTES = 1 << 30
+N_XCD = 8                   # accelerator complex dies of the MI355X (one GRBM each)
+INT8_PEAK_OPS = 5.0e15      # dense INT8 matrix peak quoted for the MI355X ...
+PEAK_CLOCK_GHZ = 2.4        # ... at this shader clock
 COPY_REPS = 3
 
 COUNTER_PASSES = {
@@ -238,6 +241,18 @@ def source_key(path):
     return h.hexdigest()
 
 
+def _steady_ns(outdir: str, match):
+    """(mean duration in ns, count) of the matching dispatches of the kernel
+    trace without the first one, or None when there are fewer than two."""
+    rows = [r for r in _rows(outdir, "trace", "kernel_trace.csv") if match(r.get("Kernel_Name", ""))]
+    try:
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[1:]]
+    except (KeyError, ValueError):
+        return None
+    return (sum(d) / len(d), len(d)) if d else None
+
+
 def summarize(workload: str, outdir: str, profiles: str) -> int:
     sp = spec(workload)
     w = sp["w"]
@@ -303,6 +318,11 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     if attn_avg_ns:
         lines += ["", f"`{kname}` average: {attn_avg_ns / 1e6:.3f} ms -> "
                       f"{ops / (attn_avg_ns * 1e-9) / 1e12:.1f} TOPS ({sp['ops_text']} / t)."]
+    steady = _steady_ns(outdir, is_attn)
+    if steady:
+        lines += [f"Without the first launch of the process (code loading and cold caches), over the other "
+                  f"{steady[1]} launches of the kernel trace: {steady[0] / 1e6:.3f} ms -> "
+                  f"{ops / (steady[0] * 1e-9) / 1e12:.1f} TOPS."]
     lines += ["", f"## HBM traffic per `{kname}` launch (TCC FETCH_SIZE / WRITE_SIZE)", "",
               f"- calibration: device copy of {COPY_BYTES} bytes, {n_copy} dispatches; FETCH_SIZE reads "
               f"{f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per copy -> scale {f_scale:.4f} (read), "
@@ -316,6 +336,17 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     lines += ["", f"## Shader counters per `{kname}` launch (sums over the device)", ""]
     for c, v in sq_vals.items():
         lines += [f"- {c}: {v:.4g}" if v is not None else f"- {c}: n/a"]
+    dur_ns = steady[0] if steady else attn_avg_ns
+    clock_ghz = None
+    if sq_vals.get("GRBM_GUI_ACTIVE") and dur_ns:
+        # GRBM counts shader-clock cycles in each of the 8 XCDs (summed over them)
+        clock_ghz = sq_vals["GRBM_GUI_ACTIVE"] / N_XCD / (dur_ns * 1e-9) / 1e9
+        frac = ops / (dur_ns * 1e-9) / (INT8_PEAK_OPS * clock_ghz / PEAK_CLOCK_GHZ)
+        lines += ["", f"Sustained shader clock: GRBM_GUI_ACTIVE / {N_XCD} XCDs / kernel time "
+                      f"({'steady' if steady else 'traced'} average) = {clock_ghz:.3f} GHz; at that clock the "
+                      f"INT8 matrix peak is {INT8_PEAK_OPS * clock_ghz / PEAK_CLOCK_GHZ / 1e12:.0f} TOPS and the "
+                      f"kernel reaches {frac:.3f} of it ({frac * PEAK_CLOCK_GHZ / clock_ghz:.3f} of the "
+                      f"{INT8_PEAK_OPS / 1e12:.0f} TOPS quoted at {PEAK_CLOCK_GHZ} GHz)."]
     if sq_vals.get("SQ_VALU_MFMA_BUSY_CYCLES") and sq_vals.get("SQ_BUSY_CYCLES"):
         lines += ["", "SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD; SQ_BUSY_CYCLES per shader engine "
                       "(32 engines, 32 SIMDs each): MFMA busy fraction = "
@@ -335,7 +366,9 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
                     "bytes_per_launch": round(traffic),
                     "read_bytes": round(read_b), "write_bytes": round(write_b),
                     "fetch_kib": f_attn, "write_kib": w_attn, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
-                    "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns}
+                    "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns,
+                    "steady_avg_duration_ns": steady[0] if steady else None,
+                    "sustained_clock_ghz": clock_ghz}
     with open(tf, "w") as f:
         json.dump(allt, f, indent=1, sort_keys=True)
     print("\n".join(lines))

@@ -395,8 +395,8 @@ void launch_w8a8_layernorm_quant(const uint16_t* x, const float* gamma, const fl
   record("w8a8 ln: rstd", rstd, (long double)R * 4, true);
   launched(st);
 }
-void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias, int M,
-                      int N, int K, void* out, int out_bf16, hipStream_t st) {
+hipError_t launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const float* sw, const float* bias,
+                            int M, int N, int K, void* out, int out_bf16, hipStream_t st) {
   record("gemm: x", x, (long double)M * K, false);
   record("gemm: x scales", sx, (long double)((M + 127) / 128) * (K / 128) * 4, false);
   record("gemm: w", w, (long double)N * K, false);
@@ -404,6 +404,7 @@ void launch_w8a8_gemm(const int8_t* x, const float* sx, const int8_t* w, const f
   if (bias) record("gemm: bias", bias, (long double)N * 4, false);
   record("gemm: out", out, (long double)M * N * (out_bf16 ? 2 : 4), true);
   launched(st);
+  return hipSuccess;
 }
 
 }  // namespace sqattn
