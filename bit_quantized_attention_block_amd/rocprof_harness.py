@@ -12,11 +12,11 @@ Sub-commands:
 writes profiles/<kernel>_<workload>_bench_trace.md: the per-kernel durations of
 that run next to the HIP-event figures of its bench line.
 
-`target` is the profiled program: seeded inputs of the workload in HBM, then
-R x (quantize Q/K, pack V, attention kernel) -- or, for a W8A8 workload, R x
-(quantize x, block-scaled GEMM) on pre-quantized weights -- and, for
-calibration, three device copies of a 1 GiB buffer (a plain read + write of
-known size).
+`target` is the profiled program: seeded inputs of the workload in HBM,
+quantize Q/K and pack V once, then R attention kernels back to back -- or, for
+a W8A8 workload, quantize x once and R block-scaled GEMMs back to back on
+pre-quantized weights -- and, for calibration, three device copies of a 1 GiB
+buffer (a plain read + write of known size).
 
 `collect` runs `target` under rocprofv3 in separate passes: kernel trace with
 statistics, FETCH_SIZE, WRITE_SIZE, and the shader counters of MFMA
@@ -25,8 +25,10 @@ that asks for more counters than the hardware has hangs, so each pass holds
 only counters that fit one run).
 
 `summarize` turns the CSV output into
-  profiles/<kernel>_<workload>_profile.md  kernel durations (rocprofv3 --stats),
-                                           HBM bytes and MFMA busy per launch
+  profiles/<kernel>_<workload>_profile.md  kernel durations (rocprofv3 --stats,
+                                           and without the first launch), HBM
+                                           bytes, MFMA busy and the sustained
+                                           shader clock per launch
   profiles/kernel_traffic.json             per-launch HBM bytes of the profiled
                                            kernel, keyed by workload, with a
                                            sha256 over the kernel source and
@@ -70,6 +72,7 @@ def spec(workload: str) -> dict:
     return {"w": w, "kind": "attn", "kernel": ATTN_KERNEL[w.pv], "src": ATTN_SRC[w.pv], "ops": w.ops,
             "ops_text": "4 B H N^2 d", "title": f"{w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})"}
 COPY_BYTES = 1 << 30
+WARM_SECONDS = 0.25
 N_XCD = 8                   # accelerator complex dies of the MI355X (one GRBM each)
 INT8_PEAK_OPS = 5.0e15      # dense INT8 matrix peak quoted for the MI355X ...
 PEAK_CLOCK_GHZ = 2.4        # ... at this shader clock
@@ -106,25 +109,37 @@ def run_target(workload: str, reps: int) -> None:
         wc, ws = sq.w8a8_quantize(Wt)
         del Wt
         y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-        for _ in range(reps):
-            xc, xs = sq.w8a8_quantize(X)
-            sq.w8a8_gemm(xc, xs, wc, ws, bias=bias, out=y)
-            torch.cuda.synchronize()
-            print(f"[target] {w.name}: rep done", flush=True)
+        xc, xs = sq.w8a8_quantize(X)
+        launch = lambda: sq.w8a8_gemm(xc, xs, wc, ws, bias=bias, out=y)
     else:
         q, k, v, _ = W.gen_inputs(w)
         Q, K, V = to(q), to(k), to(v)
         out = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
-        for _ in range(reps):
-            qi, qs, ki, ks, _mu = sq.quantize_qk(Q, K, w.q_block, w.k_block)
-            if w.pv == "fp8":
-                vc, vs = sq.quantize_v_fp8(V)
-                vp = sq.pack_v(vc, "fp8")
-            else:
-                vs, vp = None, sq.pack_v(V, "bf16")
-            sq.attend_packed(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block, out=out)
+        qi, qs, ki, ks, _mu = sq.quantize_qk(Q, K, w.q_block, w.k_block)
+        if w.pv == "fp8":
+            vc, vs = sq.quantize_v_fp8(V)
+            vp = sq.pack_v(vc, "fp8")
+        else:
+            vs, vp = None, sq.pack_v(V, "bf16")
+        launch = lambda: sq.attend_packed(qi, qs, ki, ks, vp, vs, scale=w.scale, pv=w.pv, q_block=w.q_block,
+                                          out=out)
+    torch.cuda.synchronize()
+    # Warm-up: the profiled kernel itself for about WARM_SECONDS, so that the
+    # shader clock has left its idle level (the summary leaves these launches
+    # out of the steady figures), then the profiled launches back to back, as
+    # the bench times them.
+    n_warm, t0 = 0, time.time()
+    while time.time() - t0 < WARM_SECONDS:
+        launch()
+        n_warm += 1
+        if n_warm % 4 == 0:
             torch.cuda.synchronize()
-            print(f"[target] {w.name}: rep done", flush=True)
+    torch.cuda.synchronize()
+    print(f"[target] warm-up launches: {n_warm}", flush=True)
+    for _ in range(reps):
+        launch()
+    torch.cuda.synchronize()
+    print(f"[target] {w.name}: {reps} launches done", flush=True)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(COPY_REPS):
@@ -194,8 +209,13 @@ def _per_dispatch(rows, counter):
     return d
 
 
-def _mean_for(d, match):
-    vals = [v for (n, v) in d.values() if match(n)]
+def _mean_for(d, match, skip: int = 0):
+    """Mean over the matching dispatches in dispatch order, without the first
+    `skip` of them (all of them if fewer are left)."""
+    keys = sorted(d, key=lambda k: int(k) if str(k).isdigit() else str(k))
+    vals = [d[k][1] for k in keys if match(d[k][0])]
+    if len(vals) > skip:
+        vals = vals[skip:]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
@@ -241,13 +261,26 @@ def source_key(path):
     return h.hexdigest()
 
 
-def _steady_ns(outdir: str, match):
+def _warm_launches(outdir: str, name: str) -> int:
+    """Warm-up launches the target reported in a pass's log (1 if absent: the
+    first launch of the process is left out in any case)."""
+    try:
+        with open(os.path.join(outdir, name + ".log")) as f:
+            for line in f:
+                if line.startswith("[target] warm-up launches:"):
+                    return max(1, int(line.split(":")[1]))
+    except (OSError, ValueError):
+        pass
+    return 1
+
+
+def _steady_ns(outdir: str, match, skip: int = 1):
     """(mean duration in ns, count) of the matching dispatches of the kernel
-    trace without the first one, or None when there are fewer than two."""
+    trace without the first `skip`, or None when none are left."""
     rows = [r for r in _rows(outdir, "trace", "kernel_trace.csv") if match(r.get("Kernel_Name", ""))]
     try:
         rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[1:]]
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[skip:]]
     except (KeyError, ValueError):
         return None
     return (sum(d) / len(d), len(d)) if d else None
@@ -280,8 +313,9 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     write = _per_dispatch(_rows(outdir, "write", "counter_collection.csv"), "WRITE_SIZE")
     sqr = _rows(outdir, "sq", "counter_collection.csv")
     grbm = _rows(outdir, "grbm", "counter_collection.csv")
-    f_attn, n_attn = _mean_for(fetch, is_attn)
-    w_attn, _ = _mean_for(write, is_attn)
+    # the kernel's counters over its launches after the target's warm-up
+    f_attn, n_attn = _mean_for(fetch, is_attn, _warm_launches(outdir, "fetch"))
+    w_attn, _ = _mean_for(write, is_attn, _warm_launches(outdir, "write"))
     f_copy, n_copy = _mean_for(fetch, is_copy)
     w_copy, _ = _mean_for(write, is_copy)
     if None in (f_attn, w_attn, f_copy, w_copy) or not f_copy or not w_copy:
@@ -295,10 +329,10 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
 
     sq_vals = {}
     for c in COUNTER_PASSES["sq"]:
-        v, _ = _mean_for(_per_dispatch(sqr, c), is_attn)
+        v, _ = _mean_for(_per_dispatch(sqr, c), is_attn, _warm_launches(outdir, "sq"))
         sq_vals[c] = v
     for c in COUNTER_PASSES["grbm"]:
-        v, _ = _mean_for(_per_dispatch(grbm, c), is_attn)
+        v, _ = _mean_for(_per_dispatch(grbm, c), is_attn, _warm_launches(outdir, "grbm"))
         sq_vals[c] = v
 
     ops = sp["ops"]
@@ -318,11 +352,13 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     if attn_avg_ns:
         lines += ["", f"`{kname}` average: {attn_avg_ns / 1e6:.3f} ms -> "
                       f"{ops / (attn_avg_ns * 1e-9) / 1e12:.1f} TOPS ({sp['ops_text']} / t)."]
-    steady = _steady_ns(outdir, is_attn)
+    n_warm = _warm_launches(outdir, "trace")
+    steady = _steady_ns(outdir, is_attn, n_warm)
     if steady:
-        lines += [f"Without the first launch of the process (code loading and cold caches), over the other "
-                  f"{steady[1]} launches of the kernel trace: {steady[0] / 1e6:.3f} ms -> "
-                  f"{ops / (steady[0] * 1e-9) / 1e12:.1f} TOPS."]
+        lines += [f"Steady: without the {n_warm} warm-up launch(es) of the process (code loading, cold caches, "
+                  f"the shader clock leaving its idle level), over the other {steady[1]} launches of the kernel "
+                  f"trace: {steady[0] / 1e6:.3f} ms -> {ops / (steady[0] * 1e-9) / 1e12:.1f} TOPS.  The counters "
+                  f"below are averaged over the launches after each pass's own warm-up."]
     lines += ["", f"## HBM traffic per `{kname}` launch (TCC FETCH_SIZE / WRITE_SIZE)", "",
               f"- calibration: device copy of {COPY_BYTES} bytes, {n_copy} dispatches; FETCH_SIZE reads "
               f"{f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per copy -> scale {f_scale:.4f} (read), "
@@ -345,7 +381,7 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
         lines += ["", f"Sustained shader clock: GRBM_GUI_ACTIVE / {N_XCD} XCDs / kernel time "
                       f"({'steady' if steady else 'traced'} average) = {clock_ghz:.3f} GHz; at that clock the "
                       f"INT8 matrix peak is {INT8_PEAK_OPS * clock_ghz / PEAK_CLOCK_GHZ / 1e12:.0f} TOPS and the "
-                      f"kernel reaches {frac:.3f} of it ({frac * PEAK_CLOCK_GHZ / clock_ghz:.3f} of the "
+                      f"kernel reaches {frac:.3f} of it ({frac * clock_ghz / PEAK_CLOCK_GHZ:.3f} of the "
                       f"{INT8_PEAK_OPS / 1e12:.0f} TOPS quoted at {PEAK_CLOCK_GHZ} GHz)."]
     if sq_vals.get("SQ_VALU_MFMA_BUSY_CYCLES") and sq_vals.get("SQ_BUSY_CYCLES"):
         lines += ["", "SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD; SQ_BUSY_CYCLES per shader engine "

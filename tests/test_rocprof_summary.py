@@ -26,6 +26,22 @@ def test_steady_average_drops_the_first_launch(tmp_path):
     assert n == 2 and mean == 12.0
 
 
+def test_warm_up_launches_are_skipped(tmp_path):
+    _trace(tmp_path, [("k(p)", 0, 50), ("k(p)", 100, 140), ("k(p)", 200, 210), ("k(p)", 300, 314)])
+    (tmp_path / "trace.log").write_text("[target] warm-up launches: 2\n[target] w: 2 launches done\n")
+    n = rh._warm_launches(str(tmp_path), "trace")
+    assert n == 2
+    assert rh._steady_ns(str(tmp_path), lambda n: True, n) == (12.0, 2)
+    assert rh._warm_launches(str(tmp_path), "fetch") == 1  # no log: the first launch only
+
+
+def test_counter_means_skip_the_warm_up_in_dispatch_order():
+    d = {"10": ("k", 5.0), "2": ("k", 100.0), "3": ("copy", 7.0), "11": ("k", 7.0)}
+    assert rh._mean_for(d, lambda n: n == "k", 1) == (6.0, 2)
+    assert rh._mean_for(d, lambda n: n == "k", 5) == (112.0 / 3, 3)  # fewer left: all of them
+    assert rh._mean_for(d, lambda n: n == "copy") == (7.0, 1)
+
+
 def test_steady_average_needs_two_launches(tmp_path):
     _trace(tmp_path, [("sqattn::w8a8_gemm_kernel(p)", 0, 5)])
     assert rh._steady_ns(str(tmp_path), lambda n: "w8a8_gemm_kernel" in n) is None
