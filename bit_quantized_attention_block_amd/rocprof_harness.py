@@ -19,8 +19,9 @@ pre-quantized weights -- and, for calibration, three device copies of a 1 GiB
 buffer (a plain read + write of known size).
 
 `collect` runs `target` under rocprofv3 in separate passes: kernel trace with
-statistics, FETCH_SIZE, WRITE_SIZE, and the shader counters of MFMA
-utilisation.  Every pass is its own process under a hard time limit (a pass
+statistics, FETCH_SIZE, WRITE_SIZE, the shader counters of MFMA utilisation,
+the GRBM cycle counters, and the matrix ops per operand type
+(SQ_INSTS_VALU_MFMA_MOPS_I8 / _BF16 / _F8).  Every pass is its own process under a hard time limit (a pass
 that asks for more counters than the hardware has hangs, so each pass holds
 only counters that fit one run).
 
@@ -66,11 +67,13 @@ def spec(workload: str) -> dict:
         from workloads import linear as WL
         w = WL.get_linear(workload)
         return {"w": w, "kind": "w8a8", "kernel": W8A8_KERNEL, "src": W8A8_SRC, "ops": w.ops,
-                "ops_text": "2 M N K", "title": f"{w.name} (M={w.M}, N={w.N}, K={w.K}, bf16 output, bias)"}
+                "ops_text": "2 M N K", "type_ops": {"I8": w.ops},
+                "title": f"{w.name} (M={w.M}, N={w.N}, K={w.K}, bf16 output, bias)"}
     import workloads as W
     w = W.get(workload)
     return {"w": w, "kind": "attn", "kernel": ATTN_KERNEL[w.pv], "src": ATTN_SRC[w.pv], "ops": w.ops,
-            "ops_text": "4 B H N^2 d", "title": f"{w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})"}
+            "ops_text": "4 B H N^2 d", "type_ops": {"I8": w.ops / 2, ("BF16" if w.pv == "bf16" else "F8"): w.ops / 2},
+            "title": f"{w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, P.V {w.pv})"}
 COPY_BYTES = 1 << 30
 WARM_SECONDS = 0.25
 N_XCD = 8                   # accelerator complex dies of the MI355X (one GRBM each)
@@ -84,7 +87,12 @@ COUNTER_PASSES = {
     "sq": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
            "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"],
     "grbm": ["GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+    "mops": ["SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+             "SQ_INSTS_VALU_MFMA_I8", "SQ_INSTS_VALU_MFMA_BF16", "SQ_INSTS_VALU_MFMA_F8"],
 }
+# dense matrix peaks quoted for the MI355X at 2.4 GHz, ops/s, per operand type
+# of the MOPS counters (F8 counts the E4M3 scaled MFMA)
+TYPE_PEAK_OPS = {"I8": 5.0e15, "BF16": 2.5e15, "F8": 5.0e15}
 
 
 # ---------------------------------------------------------------------------
@@ -334,6 +342,11 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
     for c in COUNTER_PASSES["grbm"]:
         v, _ = _mean_for(_per_dispatch(grbm, c), is_attn, _warm_launches(outdir, "grbm"))
         sq_vals[c] = v
+    mops_rows = _rows(outdir, "mops", "counter_collection.csv")
+    mops = {}
+    for c in COUNTER_PASSES["mops"]:
+        v, _ = _mean_for(_per_dispatch(mops_rows, c), is_attn, _warm_launches(outdir, "mops"))
+        mops[c] = v
 
     ops = sp["ops"]
     lines = [f"# `{kname}` on {sp['title']}", "",
@@ -383,6 +396,26 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
                       f"INT8 matrix peak is {INT8_PEAK_OPS * clock_ghz / PEAK_CLOCK_GHZ / 1e12:.0f} TOPS and the "
                       f"kernel reaches {frac:.3f} of it ({frac * clock_ghz / PEAK_CLOCK_GHZ:.3f} of the "
                       f"{INT8_PEAK_OPS / 1e12:.0f} TOPS quoted at {PEAK_CLOCK_GHZ} GHz)."]
+    mfma_util = None
+    if any(v is not None for v in mops.values()):
+        lines += ["", f"## Matrix-core work per `{kname}` launch (SQ_INSTS_VALU_MFMA_MOPS_*: ops / 512)", "",
+                  "| operand type | instructions | ops counted | ops of the operation | counted / operation |",
+                  "|---|---|---|---|---|"]
+        need_cycles = 0.0  # CU-cycles the counted ops need at the quoted per-clock peaks
+        for t in ("I8", "BF16", "F8"):
+            m, n = mops.get(f"SQ_INSTS_VALU_MFMA_MOPS_{t}"), mops.get(f"SQ_INSTS_VALU_MFMA_{t}")
+            if m is None:
+                continue
+            got, want = m * 512.0, sp["type_ops"].get(t, 0.0)
+            lines += [f"| {t} | {n:.4g} | {got:.4g} | {want:.4g} | " + (f"{got / want:.4f} |" if want else "— |")]
+            need_cycles += got / (TYPE_PEAK_OPS[t] / PEAK_CLOCK_GHZ / 1e9 / 256)
+        if sq_vals.get("GRBM_GUI_ACTIVE"):
+            cycles = sq_vals["GRBM_GUI_ACTIVE"] / N_XCD  # per XCD, i.e. per CU
+            mfma_util = need_cycles / 256 / cycles
+            lines += ["", f"At the quoted per-clock peaks (I8 and F8 {TYPE_PEAK_OPS['I8'] / 2.4e9 / 256:.0f}, "
+                          f"BF16 {TYPE_PEAK_OPS['BF16'] / 2.4e9 / 256:.0f} ops per clock per CU) the counted ops "
+                          f"keep the matrix cores of the 256 CUs busy {need_cycles / 256:.4g} cycles of the "
+                          f"kernel's {cycles:.4g}: matrix-core utilisation {mfma_util:.3f}."]
     if sq_vals.get("SQ_VALU_MFMA_BUSY_CYCLES") and sq_vals.get("SQ_BUSY_CYCLES"):
         lines += ["", "SQ_VALU_MFMA_BUSY_CYCLES is counted per SIMD; SQ_BUSY_CYCLES per shader engine "
                       "(32 engines, 32 SIMDs each): MFMA busy fraction = "
@@ -404,7 +437,7 @@ def summarize(workload: str, outdir: str, profiles: str) -> int:
                     "fetch_kib": f_attn, "write_kib": w_attn, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
                     "copy_bytes": COPY_BYTES, "avg_duration_ns": attn_avg_ns,
                     "steady_avg_duration_ns": steady[0] if steady else None,
-                    "sustained_clock_ghz": clock_ghz}
+                    "sustained_clock_ghz": clock_ghz, "mfma_utilisation": mfma_util}
     with open(tf, "w") as f:
         json.dump(allt, f, indent=1, sort_keys=True)
     print("\n".join(lines))
