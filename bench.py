@@ -89,6 +89,10 @@ def _at_profiled_clock(roof, name, src):
     roof["profiled_clock_ghz"] = round(clk, 4) if clk else None
     roof["frac_at_profiled_clock"] = round(roof["frac"] * 2.4 / clk, 4) if clk else None
     roof["frac_mixed_at_profiled_clock"] = round(roof["frac_mixed"] * 2.4 / clk, 4) if clk else None
+    # matrix-core utilisation of the profiled run: its counted MFMA ops per
+    # operand type over what the matrix cores do in its cycles
+    mu = t.get("mfma_utilisation") if t else None
+    roof["mfma_utilisation_profiled"] = round(mu, 4) if mu else None
     return roof
 
 
