@@ -275,6 +275,38 @@ def cpu_baseline_w8a8(w, x, wt, b, row_blocks=64, w_rows=8192):
             "sample_seconds": round(t2 - t0, 2)}
 
 
+def numerics_w8a8(w, x, wt, b, y_dev, rows=1024, cols=1024):
+    """Error of the GPU layer output (bf16) on the first rows x cols outputs:
+    against the oracle, also as a ratio to the rounding bound of the kernel's
+    fp32 evaluation ((n + 2) 2^-24 sum_j |sx sw D_j|, n slices) plus a bf16
+    step of the result, and against the unquantized float64 product of the
+    same bf16 inputs (the method's own error).  Whole 128-row blocks, so the
+    sample's scales are the layer's."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    r, c = min(w.M, rows), min(w.N, cols)
+    xf, wf = W.bf16_bits_to_f32(x[:r]), W.bf16_bits_to_f32(wt[:c])
+    cx, sx = oracle.w8a8.quantize_blocks(xf)
+    cw, sw = oracle.w8a8.quantize_blocks(wf)
+    bb = None if b is None else np.asarray(b[:c], np.float32)
+    ref = oracle.w8a8.linear(cx, sx, cw, sw, bb)
+    tol = (w.K // 128 + 2) * 2.0 ** -24 * oracle.w8a8.linear_bound(cx, sx, cw, sw, bb) + 2.0 ** -8 * np.abs(ref)
+    g = y_dev[:r, :c].float().cpu().numpy().astype(np.float64)
+    e = np.abs(g - ref)
+    exact = xf.astype(np.float64) @ wf.astype(np.float64).T
+    if bb is not None:
+        exact += bb.astype(np.float64)[None, :]
+    dq = np.abs(g - exact)
+    return {"outputs": f"rows 0..{r - 1} x columns 0..{c - 1}",
+            "vs_oracle_max_abs": float(e.max()),
+            "vs_oracle_max_over_bound": float((e / np.maximum(tol, 1e-300)).max()),
+            "vs_fp64_unquantized_max_abs": float(dq.max()),
+            "vs_fp64_unquantized_mean_abs": float(dq.mean()),
+            "vs_fp64_unquantized_rel_rms": float(np.sqrt((dq ** 2).mean() / (exact ** 2).mean()))}
+
+
 def bench_w8a8(a):
     """One step = the W8A8 layer on bf16 activations in HBM: INT8 quantization
     of x (128x128 blocks) and the block-scaled INT8 GEMM with bias, bf16
@@ -367,8 +399,11 @@ def bench_w8a8(a):
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline_w8a8(w, x, wt, b)
+        # Y holds the plain layer's output of the last kernel launches
+        res["numerics"] = numerics_w8a8(w, x, wt, b, Y)
     else:
         res["cpu_baseline"] = None
+        res["numerics"] = None
     res["system"] = system_info(torch)
     res["system"]["clocks"] = clocks.summary()
     print(json.dumps(res), flush=True)
