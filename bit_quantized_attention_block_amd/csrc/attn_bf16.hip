@@ -63,6 +63,9 @@ namespace sqattn {
 
 namespace {
 
+// (1, 1) as a bf16 pair: the row sums' second operand
+constexpr v2bf ONE_BF16X2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 __device__ __forceinline__ int perm_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 constexpr float HEADROOM = 64.0f;  // log2 units
@@ -300,7 +303,7 @@ struct Ctx {
   }
 
   // ---- V(t): P = 2^(S c - k) with k = 1.5 * 2^23 c + ref, packed to bf16 as
-  // the P^T operands, and the row sum.  Register i of half kb holds key
+  // the P^T operands, and the row sum of those rounded P.  Register i of half kb holds key
   // 32 kb + 16 (i / 8) + 8 g + i % 8 (perm_key order), which is element
   // i % 8 of lane-half g of 16-key k-step 2 kb + i / 8.  MASK: keys >= kvalid
   // get P = 0.  SM: bias_e is the entry holding the tile's bias (< 0: the
@@ -325,7 +328,11 @@ struct Ctx {
           u1 = key + 1 < kvalid ? u1 : 0.0f;
         }
         w[j] = pack_bf16x2(u0, u1);
-        part[j] = ks == 0 ? u0 + u1 : part[j] + (u0 + u1);
+        // the row sum adds the rounded P the matrix cores multiply, a pair
+        // per v_dot2_f32_bf16 (fewer vector instructions and registers than
+        // adding the fp32 values)
+        part[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[j]), ONE_BF16X2,
+                                                  ks == 0 ? 0.0f : part[j], false);
       }
       pb[ks] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       // the refill, spread over the phase
