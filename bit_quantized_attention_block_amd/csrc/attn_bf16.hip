@@ -142,6 +142,7 @@ struct Ctx {
   v4i pb[4];              // P^T operands of the current tile, four 16-key k-steps
   v16f o[G::NCB];         // O^T accumulators
   float m, l;             // reference max (log2 units), row sum
+  float lp[4];            // the row sum's four partials (one per packed pair), kept across tiles
   // block-sparse: the work-group's tile list (LDS), its length, and whether
   // this wave's reference is set (taken from its first kept tile)
   const int* list;
@@ -313,7 +314,6 @@ struct Ctx {
     if constexpr (SM) {
       if (bias_e >= 0) add_bias(lds + bias_e * G::ES + G::BOFF + qbw);
     }
-    float part[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint32_t w[4];
@@ -329,10 +329,10 @@ struct Ctx {
         }
         w[j] = pack_bf16x2(u0, u1);
         // the row sum adds the rounded P the matrix cores multiply, a pair
-        // per v_dot2_f32_bf16 (fewer vector instructions and registers than
-        // adding the fp32 values)
-        part[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[j]), ONE_BF16X2,
-                                                  ks == 0 ? 0.0f : part[j], false);
+        // per v_dot2_f32_bf16 into one of four partials that are combined
+        // only after the last tile (fewer vector instructions and registers
+        // than adding the fp32 values per tile)
+        lp[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[j]), ONE_BF16X2, lp[j], false);
       }
       pb[ks] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       // the refill, spread over the phase
@@ -342,7 +342,6 @@ struct Ctx {
         if (i * 4 / (G::PER + 1) == ks) load_part(rf, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l += (part[0] + part[1]) + (part[2] + part[3]);
   }
 
   // ---- M(t): refill, then S(t+1) from entry t's K tile (QK), then
@@ -574,13 +573,14 @@ __global__ __launch_bounds__(NTHR) void attn_bf16_kernel(AttnParams p) {
       C.m = C.exact_max(npos);
       if constexpr (SP) C.has_m = true;
     }
-    C.l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) C.lp[j] = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < G::NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) C.o[cb][i] = 0.0f;
     C.pipeline(npos, pass == 0);
-    C.l = pair_sum_f(C.l);
+    C.l = pair_sum_f((C.lp[0] + C.lp[1]) + (C.lp[2] + C.lp[3]));
     // the sum bounds every P: l < 2^HEADROOM keeps P and O far from overflow
     const bool over = !(C.l < __builtin_exp2f(HEADROOM));
     if (pass == 1 || !__syncthreads_or(over)) break;
