@@ -37,14 +37,13 @@
 // * 448 is folded into the exponent: y = 2^(x c - (m - log2 448)) = 448 P~,
 //   the E4M3 operand is the rounded y and the row sum adds the unrounded y, so
 //   O = sum(sV y^ code) / sum(y).
-// * LDS ring of NS slots (eight in the dense kernel, four in the block-sparse
-//   and Q-smoothing ones, whose tile list or bias leave no room for more),
-//   filled by direct-to-LDS loads one interval of NS / 2 tiles ahead, with
-//   one barrier per interval; V^T rows hold 64 one-byte keys padded to 80
+// * LDS ring, direct-to-LDS refills three tiles ahead and one barrier per
+//   tile as in the 16-bit kernel; V^T rows hold 64 one-byte keys padded to 80
 //   bytes (five 16-byte units, odd, so 16 lanes reading 16 bytes of
 //   consecutive rows hit distinct banks).  Each slot also carries its tile's
 //   scale (64 copies, one per lane).  The first K tile is read straight from
-//   global memory; K(x) and V(x) sit in slot x mod NS.
+//   global memory, so K slot j holds tiles with index = j mod 4 from tile 1 on
+//   and every refill has two tile boundaries to land.
 // * Keys past N: the K tile reads row N-1 there (a real score of the same
 //   tile, so the tile max is unchanged), y is zeroed for them in the last
 //   tile, and the packed V tile is zero past N.
@@ -69,13 +68,7 @@ __device__ __forceinline__ int perm_key(int r) { return (r & ~12) | ((r & 4) << 
 
 constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
-// LDS ring depth in tiles: eight slots in the dense kernel, four where the
-// block-sparse tile list or the Q-smoothing bias leave no room for more.  A
-// ring of NS slots takes one barrier every NS / 2 tiles.
-template <bool SP, bool SM>
-constexpr int ring_slots() {
-  return (SP || SM) ? 4 : 8;
-}
+constexpr int NSLOT = 4;                          // LDS ring depth (tiles)
 constexpr float LOG2_448 = 8.80735492205760410f;  // log2(448)
 constexpr int E8M0_ONE = 127;                     // E8M0 scale 2^0
 constexpr int SQ_MAGIC = 0x4B400000;              // bits of 1.5 * 2^23
@@ -100,7 +93,7 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
   return *(const __attribute__((address_space(4))) float*)p;
 }
 
-template <int D, bool SM, int NS>
+template <int D, bool SM = false>
 struct Geo {
   static constexpr int NCH = D / 32;            // QK k-steps per 32-key half
   static constexpr int NCB = D / 32;            // 32-channel blocks of O^T
@@ -114,8 +107,8 @@ struct Geo {
   static constexpr int VSC = D * VROW;          // offset of the V scale in a V slot
   static constexpr int VQB = VSC + 256;         // offset of the Q-smoothing bias (SM)
   static constexpr int VS = VQB + (SM ? 1024 : 0);  // V slot bytes
-  static constexpr int VBASE = NS * KS;         // V ring offset in LDS
-  static constexpr int LDS_BYTES = NS * (KS + VS);
+  static constexpr int VBASE = NSLOT * KS;      // V ring offset in LDS
+  static constexpr int LDS_BYTES = NSLOT * (KS + VS);
   static constexpr int KINST = (KT * KROWC + 63) / 64;   // 1 KB direct loads per K tile
   static constexpr int VINST = (D * VROWC + 63) / 64;     // ... per V tile
   static constexpr int PER = (KINST + VINST + WAVES - 1) / WAVES;  // K+V loads per wave
@@ -125,8 +118,7 @@ struct Geo {
 
 template <int D, bool SP = false, bool SM = false>
 struct Ctx {
-  static constexpr int NS = ring_slots<SP, SM>();
-  using G = Geo<D, SM, NS>;
+  using G = Geo<D, SM>;
   uint8_t* lds;
   const uint8_t* kh;
   const uint8_t* vth;
@@ -300,8 +292,8 @@ struct Ctx {
   template <bool QK, bool MASK>
   __device__ __forceinline__ void iter(v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t,
                                        float c, int sve, const Refill& rf, int tile = 0, bool act = true) {
-    const uint32_t ka = kbase + ((t + 1) & (NS - 1)) * G::KS;
-    const uint32_t va = vbase + ((t - 1) & (NS - 1)) * G::VS;
+    const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
+    const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
 
     // Plain scores: the next tile's score MFMAs, then P.V of the previous
     // tile (relative to m(t-1) = m) into O and the rest of the refill, and
@@ -314,7 +306,7 @@ struct Ctx {
     float mn;
     auto running_max = [&]() {
       if constexpr (SM) {
-        if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NS - 1)) * G::VS + G::VQB + qbw);
+        if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NSLOT - 1)) * G::VS + G::VQB + qbw);
         mn = __builtin_fmaxf(m, tile_max_f(sc) * c);
       } else {
         mn = __builtin_fmaxf(m, (float)(tile_max(sc) - SQ_MAGIC) * c);  // c >= 0
@@ -396,8 +388,7 @@ struct Ctx {
 template <int D, bool SP, bool SM>
 __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   using Cx = Ctx<D, SP, SM>;
-  using G = typename Cx::G;
-  constexpr int NS = Cx::NS;
+  using G = Geo<D, SM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int w = blockIdx.x;
@@ -470,25 +461,12 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, 0.0f, C.g);
     return;
   }
-  // The ring: K(x) sits in K slot x mod NS, V(x) in V slot x mod NS, and
-  // BE = NS / 2 iterations run between two barriers.  Iteration i reads K(i+1)
-  // and V(i-1) and refills with K(i+BE+1) and V(i+BE-1), whose slots last
-  // held K(i+1-BE) and V(i-1-BE), both read in iteration i-BE, before the
-  // last barrier.  Every tile read in an interval was loaded in the one
-  // before it, and the barrier at an interval's end waits for all of that
-  // interval's loads.  Fewer barriers are what the depth buys: measured on
-  // wan14b-480p-fp8 (interleaved A/B, bit-identical outputs), a barrier every
-  // tile with four slots 14.58 ms, every second tile 14.01 ms, every fourth
-  // tile with eight slots 13.81 ms.
-  // Prologue: K(1..NS) and V(0..NS-1) (past the end: the last tile, never
-  // read), all landed before the loop; S(0) from global memory meanwhile.
-  // The first interval's refills rewrite prologue slots with the same bytes
-  // (read only after the interval's barrier), so every iteration issues the
-  // same loads.  The first iteration multiplies V slot NS-1 by P(-1) = 0 (a
-  // finite tile, so nothing).
-  constexpr int BE = NS / 2;
+  // Prologue: K(1..4) into K slots 1,2,3,0 and V(0..3) into V slots 0..3 (past
+  // the end: the last tile, never read), all landed before the loop; S(0)
+  // from global memory meanwhile.  The first iteration multiplies V slot 3 by
+  // P(-1) = 0 (a finite tile, so T = 0).
 #pragma unroll
-  for (int j = 0; j < NS; ++j) C.load_kv(tile_at(j + 1), (j + 1) & (NS - 1), tile_at(j), j);
+  for (int j = 0; j < NSLOT; ++j) C.load_kv(tile_at(j + 1), (j + 1) & (NSLOT - 1), tile_at(j), j);
   v16i S0[2], S1[2];
   v8i P0, P1;
   C.qk_first(S0, tile_at(0));
@@ -499,44 +477,49 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) P1[r] = 0;
 
-  auto refill_for = [&](int i) {
-    return C.refill(tile_at(i + BE + 1), (i + BE + 1) & (NS - 1), tile_at(i + BE - 1), (i + BE - 1) & (NS - 1));
-  };
-  typename Cx::Refill rf = refill_for(0);
-  // bar: iteration t ends an interval (t mod BE = BE - 1)
-  auto step = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t, bool bar) {
-    const float c_next = C.cq * C.k_scale((t + 1) & (NS - 1));
-    const int sve = C.v_scale_e8((t - 1) & (NS - 1));
+  // Boundary after iteration t: K(t+2) and V(t) (issued three boundaries ago
+  // or in the prologue) must have landed; refill K slot (t+1)%4 with K(t+5)
+  // and V slot (t-1)%4 with V(t+3), spread over the next iteration.  The
+  // first iteration's refill rewrites K slot 0 and V slot 2 with the bytes
+  // the prologue put there (read no earlier than iterations 3 and 2, after
+  // boundaries that wait for it), so every iteration issues the same loads.
+  typename Cx::Refill rf = C.refill(tile_at(4), 0, tile_at(2), 2);
+  auto step = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
+    // K(t+1) and V(t-1) have landed (boundary t-1); their slots are refilled
+    // only after this iteration
+    const float c_next = C.cq * C.k_scale((t + 1) & (NSLOT - 1));
+    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
     C.template iter<true, false>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
-    if (bar) {
-      // Wait for our own loads and LDS reads, then a plain barrier (the
-      // "memory" clobber keeps every memory access on its side).
-      // __syncthreads() would add a fence of its own around the direct-to-LDS
-      // loads.
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~0x0F00);  // and lgkmcnt(0)
-      asm volatile("s_barrier" ::: "memory");
-    }
-    rf = refill_for(t + 1);
+    // Wait for our own loads of three boundaries ago and all LDS reads, then
+    // a plain barrier (the "memory" clobber keeps every memory access on its
+    // side).  __syncthreads() would add a fence that waits for every
+    // direct-to-LDS load in flight, which defeats the ring.
+#ifdef SQATTN_DEBUG
+    __builtin_amdgcn_s_waitcnt(0);  // checking build: every load in flight lands first
+#else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB) & ~0x0F00);  // and lgkmcnt(0)
+#endif
+    asm volatile("s_barrier" ::: "memory");
+    rf = C.refill(tile_at(t + 5), (t + 1) & (NSLOT - 1), tile_at(t + 3), (t - 1) & (NSLOT - 1));
     c = c_next;
   };
   auto last = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
-    const int sve = C.v_scale_e8((t - 1) & (NS - 1));
+    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
     C.template iter<false, true>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
-    // V(t) may have been loaded in this interval, by any wave: wait for every
-    // load, then a barrier
+    // V(t) may still be in flight (issued up to two boundaries ago, by any
+    // wave): wait for every load, then a barrier
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    C.pv(C.vbase + (t & (NS - 1)) * G::VS, pcur, C.v_scale_e8(t & (NS - 1)), nullptr);
+    C.pv(C.vbase + (t & (NSLOT - 1)) * G::VS, pcur, C.v_scale_e8(t & (NSLOT - 1)), nullptr);
   };
-  // tiles in pairs, so that the score and P registers alternate without
-  // copies; BE is even, so only the second of a pair can end an interval
+  // tiles in pairs, so that the score and P registers alternate without copies
   int t = 0;
   for (; t + 2 < npos; t += 2) {
-    step(S0, S1, P1, P0, t, false);
-    step(S1, S0, P0, P1, t + 1, BE == 2 || ((t + 1) & (BE - 1)) == BE - 1);
+    step(S0, S1, P1, P0, t);
+    step(S1, S0, P0, P1, t + 1);
   }
   if (t + 1 < npos) {
-    step(S0, S1, P1, P0, t, false);
+    step(S0, S1, P1, P0, t);
     last(S1, S0, P0, P1, t + 1);
   } else {
     last(S0, S1, P1, P0, t);
@@ -551,7 +534,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
 
 template <int D, bool SP, bool SM>
 static hipError_t launch_d(const AttnParams& q, hipStream_t st) {
-  constexpr int lds = Geo<D, SM, ring_slots<SP, SM>()>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
+  constexpr int lds = Geo<D, SM>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   // the attribute is per kernel: set once per process (the first status is kept)
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
