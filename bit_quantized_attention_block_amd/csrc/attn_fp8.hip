@@ -37,13 +37,14 @@
 // * 448 is folded into the exponent: y = 2^(x c - (m - log2 448)) = 448 P~,
 //   the E4M3 operand is the rounded y and the row sum adds the unrounded y, so
 //   O = sum(sV y^ code) / sum(y).
-// * LDS ring, direct-to-LDS refills three tiles ahead and one barrier per
-//   tile as in the 16-bit kernel; V^T rows hold 64 one-byte keys padded to 80
-//   bytes (five 16-byte units, odd, so 16 lanes reading 16 bytes of
-//   consecutive rows hit distinct banks).  Each slot also carries its tile's
-//   scale (64 copies, one per lane).  The first K tile is read straight from
-//   global memory, so K slot j holds tiles with index = j mod 4 from tile 1 on
-//   and every refill has two tile boundaries to land.
+// * LDS ring filled by direct-to-LDS loads: eight slots and one barrier
+//   every four tiles in the dense kernel, four slots and a barrier every tile
+//   in the block-sparse and Q-smoothing ones (whose tile list or bias leave
+//   no room for eight); V^T rows hold 64 one-byte keys padded to 80 bytes
+//   (five 16-byte units, odd, so 16 lanes reading 16 bytes of consecutive
+//   rows hit distinct banks).  Each slot also carries its tile's scale (64
+//   copies, one per lane).  The first K tile is read straight from global
+//   memory; K(x) and V(x) sit in slot x mod the ring depth.
 // * Keys past N: the K tile reads row N-1 there (a real score of the same
 //   tile, so the tile max is unchanged), y is zeroed for them in the last
 //   tile, and the packed V tile is zero past N.
@@ -68,7 +69,18 @@ __device__ __forceinline__ int perm_key(int r) { return (r & ~12) | ((r & 4) << 
 
 constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
-constexpr int NSLOT = 4;                          // LDS ring depth (tiles)
+// LDS ring: NS slots, one barrier every BE tiles.  The dense kernel takes
+// eight slots and a barrier every fourth tile; the block-sparse and
+// Q-smoothing kernels, whose tile list or bias leave no room for eight, four
+// slots and a barrier every tile (measured faster there than every second).
+template <bool SP, bool SM>
+constexpr int ring_slots() {
+  return (SP || SM) ? 4 : 8;
+}
+template <bool SP, bool SM>
+constexpr int ring_every() {
+  return (SP || SM) ? 1 : 4;
+}
 constexpr float LOG2_448 = 8.80735492205760410f;  // log2(448)
 constexpr int E8M0_ONE = 127;                     // E8M0 scale 2^0
 constexpr int SQ_MAGIC = 0x4B400000;              // bits of 1.5 * 2^23
@@ -93,7 +105,7 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
   return *(const __attribute__((address_space(4))) float*)p;
 }
 
-template <int D, bool SM = false>
+template <int D, bool SM, int NS>
 struct Geo {
   static constexpr int NCH = D / 32;            // QK k-steps per 32-key half
   static constexpr int NCB = D / 32;            // 32-channel blocks of O^T
@@ -107,8 +119,8 @@ struct Geo {
   static constexpr int VSC = D * VROW;          // offset of the V scale in a V slot
   static constexpr int VQB = VSC + 256;         // offset of the Q-smoothing bias (SM)
   static constexpr int VS = VQB + (SM ? 1024 : 0);  // V slot bytes
-  static constexpr int VBASE = NSLOT * KS;      // V ring offset in LDS
-  static constexpr int LDS_BYTES = NSLOT * (KS + VS);
+  static constexpr int VBASE = NS * KS;         // V ring offset in LDS
+  static constexpr int LDS_BYTES = NS * (KS + VS);
   static constexpr int KINST = (KT * KROWC + 63) / 64;   // 1 KB direct loads per K tile
   static constexpr int VINST = (D * VROWC + 63) / 64;     // ... per V tile
   static constexpr int PER = (KINST + VINST + WAVES - 1) / WAVES;  // K+V loads per wave
@@ -118,7 +130,8 @@ struct Geo {
 
 template <int D, bool SP = false, bool SM = false>
 struct Ctx {
-  using G = Geo<D, SM>;
+  static constexpr int NS = ring_slots<SP, SM>();
+  using G = Geo<D, SM, NS>;
   uint8_t* lds;
   const uint8_t* kh;
   const uint8_t* vth;
@@ -141,15 +154,17 @@ struct Ctx {
   // ---- global -> LDS (direct); see the 16-bit kernel for the scheme.  Chunk
   // slot i < PER of a wave is one 1 KB chunk of the K or V slot; PER and
   // PER + 1 copy the K and V scales.
-  uint32_t off[G::PER];  // lane's byte offset of chunk slot i within its tile
-  int chunk[G::PER];     // wave-uniform chunk of slot i: < KINST K, else V
+  uint32_t off[G::PER];    // lane's byte offset of chunk slot i within its tile
+  uint32_t kmask[G::PER];  // wave-uniform: all ones for a K chunk, 0 for a V chunk
+  uint32_t cofs[G::PER];   // wave-uniform: the chunk's LDS offset in its ring slot (V: past VBASE)
 
   __device__ __forceinline__ void init_loads() {
 #pragma unroll
     for (int i = 0; i < G::PER; ++i) {
       int u = wave + WAVES * i;
       if (u >= G::KINST + G::VINST) u -= G::KINST + G::VINST;
-      chunk[i] = u;
+      kmask[i] = u < G::KINST ? ~0u : 0u;
+      cofs[i] = u < G::KINST ? (uint32_t)(u * 1024) : (uint32_t)(G::VBASE + (u - G::KINST) * 1024);
       if (u < G::KINST) {
         const int q = u * 64 + lane;
         off[i] = (uint32_t)(min(q / G::KROWC, KT - 1) * D + min(q % G::KROWC, G::KCPR - 1) * 16);
@@ -166,13 +181,14 @@ struct Ctx {
     const uint8_t* vt;
     int tk, tv, ks, vs;
     uint32_t klim;
+    uint32_t kso, vso;  // LDS offsets of the K slot and of the V slot (from VBASE)
   };
   __device__ __forceinline__ Refill refill(int tk, int ks, int tv, int vs) const {
     SQ_CHECK(dbg, tk >= 0 && tk < nt, 0);
     SQ_CHECK(dbg, tv >= 0 && tv < nt, 1);
     SQ_CHECK(dbg, N - 1 - tk * KT >= 0, 2);  // the last K row read exists
     return Refill{kh + (long long)tk * KT * D, vth + (long long)tv * G::VBYTES, tk, tv, ks, vs,
-                  (uint32_t)(min(N - 1 - tk * KT, KT) * D)};
+                  (uint32_t)(min(N - 1 - tk * KT, KT) * D), (uint32_t)(ks * G::KS), (uint32_t)(vs * G::VS)};
   }
   __device__ __forceinline__ void load_part(const Refill& r, int i) {
     if (SM && i == G::PER + 2) {
@@ -189,12 +205,14 @@ struct Ctx {
       lds_dma4(svh + r.tv, 0u, lds_addr(lds + G::VBASE + r.vs * G::VS + G::VSC));
       return;
     }
-    const int u = chunk[i];
-    const bool isk = u < G::KINST;  // wave-uniform
+    const uint32_t km = kmask[i];
+    const bool isk = km != 0;  // wave-uniform
     const uint8_t* base = isk ? r.kt : r.vt;
     const uint32_t o = isk ? min(off[i], r.klim + (off[i] & (D - 1))) : off[i];
-    const int dst = isk ? r.ks * G::KS + u * 1024 : G::VBASE + r.vs * G::VS + (u - G::KINST) * 1024;
-    lds_dma16(base, o, lds_addr(lds + dst));
+    // the slot offset through the masks: written as a select, it compiles to
+    // a branch around every load (measured 1-1.5% slower)
+    const uint32_t dst = cofs[i] + (r.kso & km) + (r.vso & ~km);
+    lds_dma16(base, o, lds_addr(lds) + dst);
   }
   __device__ __forceinline__ void load_kv(int tk, int ks, int tv, int vs) {
     const Refill r = refill(tk, ks, tv, vs);
@@ -292,8 +310,8 @@ struct Ctx {
   template <bool QK, bool MASK>
   __device__ __forceinline__ void iter(v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t,
                                        float c, int sve, const Refill& rf, int tile = 0, bool act = true) {
-    const uint32_t ka = kbase + ((t + 1) & (NSLOT - 1)) * G::KS;
-    const uint32_t va = vbase + ((t - 1) & (NSLOT - 1)) * G::VS;
+    const uint32_t ka = kbase + ((t + 1) & (NS - 1)) * G::KS;
+    const uint32_t va = vbase + ((t - 1) & (NS - 1)) * G::VS;
 
     // Plain scores: the next tile's score MFMAs, then P.V of the previous
     // tile (relative to m(t-1) = m) into O and the rest of the refill, and
@@ -306,7 +324,7 @@ struct Ctx {
     float mn;
     auto running_max = [&]() {
       if constexpr (SM) {
-        if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NSLOT - 1)) * G::VS + G::VQB + qbw);
+        if (t > 0) add_bias(sc, lds + G::VBASE + ((t - 1) & (NS - 1)) * G::VS + G::VQB + qbw);
         mn = __builtin_fmaxf(m, tile_max_f(sc) * c);
       } else {
         mn = __builtin_fmaxf(m, (float)(tile_max(sc) - SQ_MAGIC) * c);  // c >= 0
@@ -388,7 +406,8 @@ struct Ctx {
 template <int D, bool SP, bool SM>
 __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
   using Cx = Ctx<D, SP, SM>;
-  using G = Geo<D, SM>;
+  using G = typename Cx::G;
+  constexpr int NS = Cx::NS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int w = blockIdx.x;
@@ -461,12 +480,26 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
     if (rok) store_out_row(p.out, p.out_bf16 != 0, lay_row(p.lo, bh, row), C.o, 0.0f, C.g);
     return;
   }
-  // Prologue: K(1..4) into K slots 1,2,3,0 and V(0..3) into V slots 0..3 (past
-  // the end: the last tile, never read), all landed before the loop; S(0)
-  // from global memory meanwhile.  The first iteration multiplies V slot 3 by
-  // P(-1) = 0 (a finite tile, so T = 0).
+  // The ring: K(x) sits in K slot x mod NS, V(x) in V slot x mod NS, and BE
+  // iterations run between two barriers.  Iteration i reads K(i+1) and
+  // V(i-1) and refills with K(i+KA) and V(i+VA), KA = NS-BE+1, VA = NS-BE-1,
+  // whose slots last held K(i+1-BE) and V(i-1-BE), both read in iteration
+  // i-BE, before the last barrier.  The barrier after iteration j needs the
+  // tiles of the next BE iterations, loaded in iterations up to j+2BE-NS, so
+  // each wave lets its loads of the NS-2BE latest iterations stay in flight.
+  // Measured on wan14b-480p-fp8 (interleaved A/B, bit-identical outputs):
+  // eight slots with a barrier every fourth tile 12.87 ms against 13.16 ms
+  // for four slots with a barrier every tile.
+  // Prologue: K(1..NS) and V(0..NS-1) (past the end: the last tile, never
+  // read), all landed before the loop; S(0) from global memory meanwhile.
+  // The refills of the first iterations rewrite prologue slots with the same
+  // bytes, read only after a barrier that waits for them, so every iteration
+  // issues the same loads.  The first iteration multiplies V slot NS-1 by
+  // P(-1) = 0 (a finite tile, so nothing).
+  constexpr int BE = ring_every<SP, SM>(), KA = NS - BE + 1, VA = NS - BE - 1;
+  static_assert(NS >= 2 * BE && (BE == 1 || BE % 2 == 0), "ring schedule");
 #pragma unroll
-  for (int j = 0; j < NSLOT; ++j) C.load_kv(tile_at(j + 1), (j + 1) & (NSLOT - 1), tile_at(j), j);
+  for (int j = 0; j < NS; ++j) C.load_kv(tile_at(j + 1), (j + 1) & (NS - 1), tile_at(j), j);
   v16i S0[2], S1[2];
   v8i P0, P1;
   C.qk_first(S0, tile_at(0));
@@ -477,49 +510,50 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) P1[r] = 0;
 
-  // Boundary after iteration t: K(t+2) and V(t) (issued three boundaries ago
-  // or in the prologue) must have landed; refill K slot (t+1)%4 with K(t+5)
-  // and V slot (t-1)%4 with V(t+3), spread over the next iteration.  The
-  // first iteration's refill rewrites K slot 0 and V slot 2 with the bytes
-  // the prologue put there (read no earlier than iterations 3 and 2, after
-  // boundaries that wait for it), so every iteration issues the same loads.
-  typename Cx::Refill rf = C.refill(tile_at(4), 0, tile_at(2), 2);
-  auto step = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
-    // K(t+1) and V(t-1) have landed (boundary t-1); their slots are refilled
-    // only after this iteration
-    const float c_next = C.cq * C.k_scale((t + 1) & (NSLOT - 1));
-    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
+  auto refill_for = [&](int i) {
+    return C.refill(tile_at(i + KA), (i + KA) & (NS - 1), tile_at(i + VA), (i + VA) & (NS - 1));
+  };
+  typename Cx::Refill rf = refill_for(0);
+  // bar: iteration t ends an interval (t mod BE = BE - 1)
+  auto step = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t, bool bar) {
+    const float c_next = C.cq * C.k_scale((t + 1) & (NS - 1));
+    const int sve = C.v_scale_e8((t - 1) & (NS - 1));
     C.template iter<true, false>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
-    // Wait for our own loads of three boundaries ago and all LDS reads, then
-    // a plain barrier (the "memory" clobber keeps every memory access on its
-    // side).  __syncthreads() would add a fence that waits for every
-    // direct-to-LDS load in flight, which defeats the ring.
+    if (bar) {
+      // Wait for our own loads but those of the NS-2BE latest iterations, and
+      // for all LDS reads, then a plain barrier (the "memory" clobber keeps
+      // every memory access on its side).  __syncthreads() would add a fence
+      // that waits for every direct-to-LDS load in flight, which defeats the
+      // ring.
 #ifdef SQATTN_DEBUG
-    __builtin_amdgcn_s_waitcnt(0);  // checking build: every load in flight lands first
+      __builtin_amdgcn_s_waitcnt(0);  // checking build: every load in flight lands first
 #else
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * G::LPB) & ~0x0F00);  // and lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2 * BE) * G::LPB) & ~0x0F00);  // and lgkmcnt(0)
 #endif
-    asm volatile("s_barrier" ::: "memory");
-    rf = C.refill(tile_at(t + 5), (t + 1) & (NSLOT - 1), tile_at(t + 3), (t - 1) & (NSLOT - 1));
+      asm volatile("s_barrier" ::: "memory");
+    }
+    rf = refill_for(t + 1);
     c = c_next;
   };
   auto last = [&](v16i (&sc)[2], v16i (&sn)[2], const v8i& pprev, v8i& pcur, int t) {
-    const int sve = C.v_scale_e8((t - 1) & (NSLOT - 1));
+    const int sve = C.v_scale_e8((t - 1) & (NS - 1));
     C.template iter<false, true>(sc, sn, pprev, pcur, t, c, sve, rf, tile_at(t), kept(t));
-    // V(t) may still be in flight (issued up to two boundaries ago, by any
-    // wave): wait for every load, then a barrier
+    // V(t) may still be in flight (loaded by any wave): wait for every load,
+    // then a barrier
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    C.pv(C.vbase + (t & (NSLOT - 1)) * G::VS, pcur, C.v_scale_e8(t & (NSLOT - 1)), nullptr);
+    C.pv(C.vbase + (t & (NS - 1)) * G::VS, pcur, C.v_scale_e8(t & (NS - 1)), nullptr);
   };
-  // tiles in pairs, so that the score and P registers alternate without copies
+  // tiles in pairs, so that the score and P registers alternate without
+  // copies (BE is 1 or even: the first of a pair ends an interval only when
+  // BE is 1)
   int t = 0;
   for (; t + 2 < npos; t += 2) {
-    step(S0, S1, P1, P0, t);
-    step(S1, S0, P0, P1, t + 1);
+    step(S0, S1, P1, P0, t, BE == 1);
+    step(S1, S0, P0, P1, t + 1, BE <= 2 || ((t + 1) & (BE - 1)) == BE - 1);
   }
   if (t + 1 < npos) {
-    step(S0, S1, P1, P0, t);
+    step(S0, S1, P1, P0, t, BE == 1);
     last(S1, S0, P0, P1, t + 1);
   } else {
     last(S0, S1, P1, P0, t);
@@ -534,7 +568,7 @@ __global__ __launch_bounds__(NTHR) void attn_fp8_kernel(AttnParams p) {
 
 template <int D, bool SP, bool SM>
 static hipError_t launch_d(const AttnParams& q, hipStream_t st) {
-  constexpr int lds = Geo<D, SM>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
+  constexpr int lds = Geo<D, SM, ring_slots<SP, SM>()>::LDS_BYTES + (SP ? SP_LIST_BYTES : 0);
   // the attribute is per kernel: set once per process (the first status is kept)
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
